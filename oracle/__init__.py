@@ -1,0 +1,38 @@
+"""Plain fp64 CPU oracle for one Orthrus dual-view decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  The
+product path (``dual_view_block_amd``) never imports it and shares no code,
+header, table or helper with it; the oracle in turn imports nothing from the
+product path.
+
+What is computed follows the Orthrus pages:
+
+* block attention of the diffusion view and of the AR verify pass over one
+  shared KV cache -- ``oracle.attention``;
+* greedy and T>0 (rejection-sampling) consensus -- ``oracle.consensus``.
+
+Every function is the plain definition written out in float64 (or exact
+integers), one sequence / head at a time, with explicit masks.  Library
+primitives used as single steps: ``numpy.matmul``, ``numpy.exp``,
+``numpy.cumsum``, ``numpy.searchsorted``.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+against closed forms, library routines (``torch`` SDPA in float64), brute
+force on tiny inputs, invariants the pages fix, and exact enumeration of the
+sampler's uniforms.  No function is "parity unpinned".
+"""
+from .attention import (MASK_DIFF_BIDIR, MASK_VERIFY_CAUSAL, block_attention,
+                        block_attention_rows, transient_kv_bytes)
+from .consensus import (greedy_consensus, row_argmax, sample_consensus,
+                        accept_prefix, accepts, residual_weights, inverse_cdf_pick,
+                        fixed_point_weight, uniform_to_grid_int,
+                        tokens_committed)
+
+__all__ = [
+    "MASK_DIFF_BIDIR", "MASK_VERIFY_CAUSAL", "block_attention",
+    "block_attention_rows", "transient_kv_bytes", "greedy_consensus",
+    "row_argmax", "sample_consensus", "accept_prefix", "accepts", "residual_weights",
+    "inverse_cdf_pick", "fixed_point_weight", "uniform_to_grid_int",
+    "tokens_committed",
+]

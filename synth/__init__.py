@@ -1,0 +1,180 @@
+"""Seeded synthetic inputs for the dual-view decode step.
+
+This module only draws and lays out inputs; it holds none of the method's
+arithmetic (no attention, no argmax, no accept test).  Both the HIP path and
+the CPU oracle are fed from the tensors it returns, so the two sides always see
+bit-identical inputs.
+
+Workloads (shapes and value laws) stand in for the pages' settings: Qwen3
+1.7B / 8B attention shapes, block size K = 32 (the pages' default), a frozen
+model's KV cache modelled as N(0, 1) values rounded to bf16, and vocab-sized
+logits.  The public evaluation suites the pages measure on are not needed:
+only context length and acceptance pattern reach this path, and both are
+swept synthetically (L from 256 to 131072, first-mismatch index over 0..K).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+VOCAB_QWEN3 = 151936
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    layers: int
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    cache_len: int            # L (for ragged: the largest allowed L)
+    block_k: int
+    vocab: int
+    logit_sigma: float
+    seed: int
+    max_len: Optional[int] = None     # cache capacity; defaults to cache_len
+    ragged_min: Optional[int] = None  # ragged: L_b ~ U{ragged_min..cache_len}
+
+    @property
+    def capacity(self) -> int:
+        return self.max_len if self.max_len is not None else self.cache_len
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    # 1 layer, 2 q heads, 1 KV head, D=64, L=256, K=4; vocab 1000, logits sigma 4
+    "tiny": Workload("tiny", 1, 1, 2, 1, 64, 256, 4, 1000, 4.0, 1),
+    # Qwen3-1.7B-shaped single layer: 16 q heads / 8 KV heads, D=128, L=2048
+    "qwen3_1p7b_layer": Workload("qwen3_1p7b_layer", 1, 1, 16, 8, 128, 2048, 32,
+                                 VOCAB_QWEN3, 3.0, 2),
+    # Qwen3-8B-shaped: 36 layers, 32 q heads / 8 KV heads, D=128, L=8192
+    "qwen3_8b_8k": Workload("qwen3_8b_8k", 36, 1, 32, 8, 128, 8192, 32,
+                            VOCAB_QWEN3, 3.0, 3),
+    # Qwen3-8B-shaped long context, L=32768, K=32 (K and L are swept around it)
+    "qwen3_8b_32k": Workload("qwen3_8b_32k", 36, 1, 32, 8, 128, 32768, 32,
+                             VOCAB_QWEN3, 3.0, 4),
+    "qwen3_8b_128k": Workload("qwen3_8b_128k", 36, 1, 32, 8, 128, 131072, 32,
+                              VOCAB_QWEN3, 3.0, 4),
+    # batched ragged: 16 sequences, L_b ~ U{1024..16384}, capacity 16384
+    "ragged_b16": Workload("ragged_b16", 36, 16, 32, 8, 128, 16384, 32,
+                           VOCAB_QWEN3, 3.0, 5, max_len=16384, ragged_min=1024),
+}
+
+K_SWEEP = (1, 4, 8, 16, 32)
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def _randn_bf16(shape, g, device) -> torch.Tensor:
+    """N(0, 1) float32 draws rounded once to bf16 (round-to-nearest-even)."""
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def cache_lengths(w: Workload, device="cpu") -> torch.Tensor:
+    """int32 [B]: L for every sequence, or seeded U{ragged_min..cache_len}."""
+    if w.ragged_min is None:
+        return torch.full((w.batch,), w.cache_len, dtype=torch.int32, device=device)
+    g = _gen(w.seed * 1000 + 7, "cpu")
+    lens = torch.randint(w.ragged_min, w.cache_len + 1, (w.batch,), generator=g, dtype=torch.int64)
+    return lens.to(torch.int32).to(device)
+
+
+def attention_inputs(w: Workload, layer: int = 0, device="cpu", seed_offset: int = 0):
+    """One layer's attention inputs (identical tensors go to both views).
+
+    Returns a dict: q [B,Hq,K,D], k_blk / v_blk [B,Hkv,K,D] (the block's
+    keys/values: K_diff/V_diff for the diffusion view, the AR K/V of the block
+    tokens for the verify view), k_cache / v_cache [B,Hkv,max_len,D], all
+    bf16, and cache_len int32 [B].  Cache rows at and beyond L_b hold ordinary
+    N(0,1) draws (tests that need poison there write it themselves).
+    """
+    g = _gen(w.seed * 7919 + 104729 * layer + seed_offset, device)
+    B, Hq, Hkv, D, K, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_k, w.capacity
+    return {
+        "q": _randn_bf16((B, Hq, K, D), g, device),
+        "k_blk": _randn_bf16((B, Hkv, K, D), g, device),
+        "v_blk": _randn_bf16((B, Hkv, K, D), g, device),
+        "k_cache": _randn_bf16((B, Hkv, S, D), g, device),
+        "v_cache": _randn_bf16((B, Hkv, S, D), g, device),
+        "cache_len": cache_lengths(w, device),
+    }
+
+
+def greedy_inputs(w: Workload, device="cpu", first_mismatch=None, ties: bool = False,
+                  seed_offset: int = 0):
+    """Verify logits [B,K,V] float32 and candidates [B,K] int32.
+
+    Logits are N(0, sigma) clamped to +-6 sigma; in each row one seeded token t
+    is set to 6 sigma + 1, so the row's top token is known by construction.
+    With ``ties`` a second seeded token t2 gets the same top value (the lower
+    of t, t2 is then the lowest-index top).  Candidates copy the top token up
+    to the seeded first-mismatch index j* (0..K; K = all match), differ from it
+    at j*, and are random after j*.
+    Returns (logits, cand, j_star [B] int64).
+    """
+    g = _gen(w.seed * 31 + 17 + seed_offset, "cpu")
+    B, K, V, s = w.batch, w.block_k, w.vocab, float(w.logit_sigma)
+    logits = torch.randn((B, K, V), generator=g, dtype=torch.float32) * s
+    logits.clamp_(-6.0 * s, 6.0 * s)
+    top = torch.randint(0, V, (B, K), generator=g)
+    top_val = 6.0 * s + 1.0
+    b_idx = torch.arange(B).unsqueeze(1).expand(B, K)
+    k_idx = torch.arange(K).unsqueeze(0).expand(B, K)
+    logits[b_idx, k_idx, top] = top_val
+    first_top = top.clone()
+    if ties:
+        t2 = torch.randint(0, V, (B, K), generator=g)
+        logits[b_idx, k_idx, t2] = top_val
+        first_top = torch.minimum(top, t2)
+    if first_mismatch is None:
+        j_star = torch.randint(0, K + 1, (B,), generator=g)
+    else:
+        j_star = torch.as_tensor(first_mismatch, dtype=torch.int64).expand(B).clone()
+    rand_tok = torch.randint(0, V, (B, K), generator=g)
+    shift = torch.randint(1, V, (B, K), generator=g)
+    cand = torch.where(k_idx < j_star.unsqueeze(1), first_top, rand_tok)
+    at_j = k_idx == j_star.unsqueeze(1)
+    cand = torch.where(at_j, (first_top + shift) % V, cand)
+    return logits.to(device), cand.to(torch.int32).to(device), j_star
+
+
+def quantise_uniforms(u: torch.Tensor) -> torch.Tensor:
+    """Put float uniforms on the 2**-24 grid in [0, 1) (exact in float32)."""
+    return (torch.floor(u.double() * 16777216.0).clamp(0, 16777215) / 16777216.0).float()
+
+
+def sample_inputs(w: Workload, device="cpu", draft_noise: Optional[float] = None,
+                  seed_offset: int = 0):
+    """Target/draft probabilities, candidates and uniforms for T>0 consensus.
+
+    z_p ~ N(0, sigma); z_q ~ N(0, sigma) independent, or z_q = z_p + N(0,
+    draft_noise) when ``draft_noise`` is set (a draft close to the target, so
+    acceptance runs long).  p, q = softmax in float64 rounded to float32.
+    cand[b, i] ~ q[b, i] (seeded multinomial); uniforms [B, K+1] on the 2**-24
+    grid.  Returns (p, q, cand int32, uniforms float32).
+    """
+    g = _gen(w.seed * 131 + 5 + seed_offset, "cpu")
+    B, K, V, s = w.batch, w.block_k, w.vocab, float(w.logit_sigma)
+    zp = torch.randn((B, K, V), generator=g, dtype=torch.float64) * s
+    if draft_noise is None:
+        zq = torch.randn((B, K, V), generator=g, dtype=torch.float64) * s
+    else:
+        zq = zp + torch.randn((B, K, V), generator=g, dtype=torch.float64) * float(draft_noise)
+    p64 = torch.softmax(zp, dim=-1)
+    q64 = torch.softmax(zq, dim=-1)
+    del zp, zq
+    gc = _gen(w.seed * 131 + 6 + seed_offset, "cpu")
+    cand = torch.multinomial(q64.reshape(B * K, V), 1, generator=gc).reshape(B, K)
+    gu = _gen(w.seed * 131 + 7 + seed_offset, "cpu")
+    u = quantise_uniforms(torch.rand((B, K + 1), generator=gu, dtype=torch.float64))
+    return (p64.float().to(device), q64.float().to(device),
+            cand.to(torch.int32).to(device), u.to(device))
