@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark one Orthrus dual-view decode step on one MI355X.
+
+A step is the whole hot path for one batch: for every one of 36 layers the
+diffusion-view block attention, then for every layer the AR verify block
+attention (each layer streams its own shared KV cache; the diffusion pass of
+all layers runs before the verify pass, as in the decode cycle of the Orthrus
+paper notes §4.1), then one greedy consensus over the [K, 151936] verify
+logits.  Default workload: Qwen3-8B attention shapes (32 q heads, 8 KV heads,
+head_dim 128), cached prefix L = 32768, block K = 32, batch 1, synthetic
+N(0, 1) bf16 inputs resident in HBM.
+
+Prints ONE JSON line (rank 0, N = 1).  `value` is the achieved HBM throughput
+of the whole step in TB/s: the algorithmic bytes of the step (each layer-view
+reads its cache, q and block K/V and writes its output; the consensus reads
+the logits) divided by the step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+METRIC = "dual-view step µs and achieved HBM TB/s at Qwen3-8B shape, L=32K, K=32"
+HBM_PEAK_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b_32k")
+    ap.add_argument("--cache-len", type=int, default=None)
+    ap.add_argument("--block-k", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--k-sweep", default="1,4,8,16,32",
+                    help="block sizes timed for the latency-vs-K line ('' to skip)")
+    ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with rocprofv3-derived HBM bytes per partial-kernel launch")
+    return ap.parse_args()
+
+
+def attn_bytes(w) -> int:
+    """Algorithmic bytes of one layer-view: cache K+V rows [0, L), q, k/v block, out."""
+    bf = 2
+    cache = 2 * w.batch * w.n_kv_heads * w.cache_len * w.head_dim * bf
+    q = w.batch * w.n_q_heads * w.block_k * w.head_dim * bf
+    blk = 2 * w.batch * w.n_kv_heads * w.block_k * w.head_dim * bf
+    return cache + q + blk + q  # out has q's shape
+
+
+def partial_bytes(w) -> int:
+    """Algorithmic bytes the streaming (partial) kernel must read per launch."""
+    return attn_bytes(w) - w.batch * w.n_q_heads * w.block_k * w.head_dim * 2
+
+
+def greedy_bytes(w) -> int:
+    return w.batch * w.block_k * (w.vocab * 4 + 4) + w.batch * (4 + 4) + w.batch * w.block_k * 4
+
+
+def attn_flops(w, causal: bool) -> int:
+    """2 matmuls (QK^T, PV) over the visible keys of every query row."""
+    L, K = w.cache_len, w.block_k
+    vis = K * (L + (K + 1) / 2.0) if causal else K * (L + K)
+    return int(4 * w.batch * w.n_q_heads * w.head_dim * vis)
+
+
+class Step:
+    """Every call of one decode step, prepared once (pointers resolved)."""
+
+    def __init__(self, w, caches, device):
+        import torch
+
+        import dual_view_block_amd as dvb
+        from synth import cache_lengths, greedy_inputs, view_inputs
+
+        self.w = w
+        self.cache_len = cache_lengths(w, device)
+        self.calls = {"diff": [], "verify": []}
+        self.keep = []
+        desc_q = torch.empty((w.batch, w.n_q_heads, w.block_k, w.head_dim), dtype=torch.bfloat16,
+                             device=device)
+        ws_bytes = dvb.orthrus_attn_workspace_size(dvb.attn_desc(desc_q, caches[0][0]))
+        self.splits = dvb.orthrus_attn_num_splits(dvb.attn_desc(desc_q, caches[0][0]))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        for view, mode in (("diff", dvb.ORTHRUS_MASK_DIFF_BIDIR), ("verify", dvb.ORTHRUS_MASK_VERIFY_CAUSAL)):
+            for layer, (kc, vc) in enumerate(caches):
+                q, kb, vb = view_inputs(w, layer, view, device)
+                out = torch.empty_like(q)
+                lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device)
+                self.calls[view].append(dvb.PreparedAttention(mode, q, kb, vb, kc, vc, self.cache_len, out,
+                                                              lse, ws))
+        logits, cand, _ = greedy_inputs(w, device=device)
+        B, K = w.batch, w.block_k
+        self.acc = torch.empty(B, dtype=torch.int32, device=device)
+        self.am = torch.empty((B, K), dtype=torch.int32, device=device)
+        self.corr = torch.empty(B, dtype=torch.int32, device=device)
+        cws = torch.empty(dvb.orthrus_consensus_workspace_size(B, K, w.vocab), dtype=torch.uint8, device=device)
+        self.greedy = dvb.PreparedGreedy(logits, cand, self.acc, self.am, self.corr, cws)
+        self.keep += [logits, cand, ws, cws]
+
+    def run(self, stream_ptr: int) -> None:
+        for c in self.calls["diff"]:
+            c(stream_ptr)
+        for c in self.calls["verify"]:
+            c(stream_ptr)
+        self.greedy(stream_ptr)
+
+
+def time_steps(step, steps: int, warmup: int, graph: bool):
+    import torch
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    g = None
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step.run(side.cuda_stream)  # warm the side stream before capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step.run(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    run = (lambda: g.replay()) if g is not None else (lambda: step.run(sp))
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        run()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return t0.elapsed_time(t1) / steps, wall / steps * 1e3
+
+
+def time_kernels(step, reps: int = 2):
+    """Average device duration of the partial (cache-streaming) kernel and of
+    the merge kernel, from HIP events recorded around each launch on the
+    launch stream."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    pairs_p, pairs_m = [], []
+    for _ in range(reps):
+        for view in ("diff", "verify"):
+            for c in step.calls[view]:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+                c.partial(sp)
+                e[1].record(stream)
+                c.merge(sp)
+                e[2].record(stream)
+                pairs_p.append((e[0], e[1], view))
+                pairs_m.append((e[1], e[2], view))
+    torch.cuda.synchronize()
+    part = {"diff": [], "verify": []}
+    for a, b, v in pairs_p:
+        part[v].append(a.elapsed_time(b) * 1e3)
+    merge = [a.elapsed_time(b) * 1e3 for a, b, _ in pairs_m]
+    allp = part["diff"] + part["verify"]
+    return {"partial_us": statistics.mean(allp), "partial_diff_us": statistics.mean(part["diff"]),
+            "partial_verify_us": statistics.mean(part["verify"]), "merge_us": statistics.mean(merge)}
+
+
+def cpu_baseline(w, caches, device):
+    """The oracle, untuned, on the host cores: one layer of the step (diffusion
+    and verify view) plus the greedy consensus, scaled to TB/s of the same
+    algorithmic bytes."""
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from synth import cache_lengths, greedy_inputs, view_inputs
+
+    kc, vc = caches[0]
+    kc_h, vc_h = kc.cpu(), vc.cpu()
+    lens = cache_lengths(w, "cpu")
+    t0 = time.perf_counter()
+    for view, mode in (("diff", oracle.MASK_DIFF_BIDIR), ("verify", oracle.MASK_VERIFY_CAUSAL)):
+        q, kb, vb = (t.cpu() for t in view_inputs(w, 0, view, device))
+        oracle.block_attention(q, kb, vb, kc_h, vc_h, lens, mode)
+    logits, cand, _ = greedy_inputs(w)
+    oracle.greedy_consensus(logits, cand)
+    dt = time.perf_counter() - t0
+    nbytes = 2 * attn_bytes(w) + greedy_bytes(w)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layer 0 of {w.layers} (diffusion + verify view, all heads) + greedy consensus, "
+                      f"L={w.cache_len}, K={w.block_k}: {dt:.2f} s on {os.cpu_count()} visible host CPUs",
+            "seconds": dt}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this decode step is "
+              "not sharded across GPUs -- run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from synth import WORKLOADS, layer_cache
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU (no HIP device visible)", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    if args.cache_len:
+        w = w.replace(cache_len=args.cache_len, max_len=None)
+    if args.block_k:
+        w = w.replace(block_k=args.block_k)
+    if args.layers:
+        w = w.replace(layers=args.layers)
+    print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+    caches = [layer_cache(w, layer, device) for layer in range(w.layers)]
+    torch.cuda.synchronize()
+    print(f"[bench] caches ready: {w.layers} layers x {2 * caches[0][0].numel() * 2 / 2**20:.0f} MiB",
+          file=sys.stderr, flush=True)
+
+    step = Step(w, caches, device)
+    ms, wall_ms = time_steps(step, args.steps, args.warmup, args.graph)
+    kern = time_kernels(step)
+    print(f"[bench] step {ms * 1e3:.1f} us (host wall {wall_ms * 1e3:.1f} us), partial kernel "
+          f"{kern['partial_us']:.2f} us, merge {kern['merge_us']:.2f} us", file=sys.stderr, flush=True)
+    acc = step.acc.cpu().tolist()
+
+    sweep = {}
+    ks = [int(k) for k in args.k_sweep.split(",") if k.strip()] if args.k_sweep else []
+    for K in ks:
+        if K == w.block_k:
+            sweep[K] = ms * 1e3
+            continue
+        wk = w.replace(block_k=K)
+        sk = Step(wk, caches, device)
+        mk, _ = time_steps(sk, args.steps, args.warmup, args.graph)
+        sweep[K] = mk * 1e3
+        del sk
+        print(f"[bench] K={K}: step {mk * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    step_bytes = 2 * w.layers * attn_bytes(w) + greedy_bytes(w)
+    value = step_bytes / (ms * 1e-3) / 1e12
+    pbytes = partial_bytes(w)
+    achieved = pbytes / (kern["partial_us"] * 1e-6) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    flops = w.layers * (attn_flops(w, False) + attn_flops(w, True))
+    line = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "cache_len": w.cache_len,
+                   "block_k": w.block_k, "vocab": w.vocab, "consensus": "greedy",
+                   "launch": "hip_graph" if args.graph else "eager", "splits": step.splits},
+        "step_us": round(ms * 1e3, 2),
+        "tokens_verified_per_s": round(w.batch * w.block_k / (ms * 1e-3), 1),
+        "algorithmic_bytes_per_step": step_bytes,
+        "frac_hbm_peak_step": round(value * 1e3 / HBM_PEAK_GBS, 4),
+        "mfma_tflops_step": round(flops / (ms * 1e-3) / 1e12, 2),
+        "step_us_vs_block_k": {str(k): round(v, 2) for k, v in sweep.items()},
+        "k32_over_k1": round(sweep[32] / sweep[1], 4) if 32 in sweep and 1 in sweep else None,
+        "kernel_us": {k: round(v, 3) for k, v in kern.items()},
+        "accept_len": acc,
+        "roofline": {"bound": "hbm", "kernel": "attn_split_kernel (orthrus_block_attn_partial)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": pbytes},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, caches, device)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,256 @@
+"""MI355X-native Orthrus dual-view decode step (C ABI + thin torch binding).
+
+The functions carry the C ABI's names (include/orthrus.h) and only marshal
+arguments: they check dtypes, shapes, devices and contiguity, allocate missing
+outputs / workspace with torch on the tensors' device, and call the library on
+torch's current HIP stream.  All computation happens in the gfx950 kernels.
+
+Sources for what each call computes: Orthrus paper notes (zhangshuibai.github.io
+paper-notes), §2.1, §3.2 and §4.1 (block attention of both views over the
+shared KV cache), §4.2 (greedy consensus), §4.3 and §7.2 (rejection-sampling
+consensus).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (ORTHRUS_MASK_DIFF_BIDIR, ORTHRUS_MASK_VERIFY_CAUSAL, AttnDesc, OrthrusError,
+                   status_string)
+
+__all__ = [
+    "AttnDesc", "OrthrusError", "ORTHRUS_MASK_DIFF_BIDIR", "ORTHRUS_MASK_VERIFY_CAUSAL",
+    "attn_desc", "orthrus_attn_workspace_size", "orthrus_attn_num_splits", "orthrus_block_attn",
+    "orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_consensus_workspace_size",
+    "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_status_string",
+    "PreparedAttention", "PreparedGreedy", "library_path",
+]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def orthrus_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device (the library has no CPU path)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def attn_desc(q: torch.Tensor, k_cache: torch.Tensor, softmax_scale: float = 0.0) -> AttnDesc:
+    B, Hq, K, D = q.shape
+    _, Hkv, max_len, _ = k_cache.shape
+    return AttnDesc(B, Hq, Hkv, D, K, max_len, float(softmax_scale))
+
+
+def orthrus_attn_workspace_size(desc: AttnDesc) -> int:
+    return int(_lib.load().orthrus_attn_workspace_size(ctypes.byref(desc)))
+
+
+def orthrus_attn_num_splits(desc: AttnDesc) -> int:
+    return int(_lib.load().orthrus_attn_num_splits(ctypes.byref(desc)))
+
+
+def orthrus_consensus_workspace_size(batch: int, block_k: int, vocab: int) -> int:
+    return int(_lib.load().orthrus_consensus_workspace_size(batch, block_k, vocab))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    _need(workspace, "workspace", torch.uint8, device=device)
+    return workspace
+
+
+def _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len):
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q and k_cache must be 4-D")
+    B, Hq, K, D = q.shape
+    _, Hkv, max_len, _ = k_cache.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, (B, Hq, K, D))
+    _need(k_blk, "k_blk", torch.bfloat16, (B, Hkv, K, D), dev)
+    _need(v_blk, "v_blk", torch.bfloat16, (B, Hkv, K, D), dev)
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, max_len, D), dev)
+    _need(v_cache, "v_cache", torch.bfloat16, (B, Hkv, max_len, D), dev)
+    _need(cache_len, "cache_len", torch.int32, (B,), dev)
+
+
+def orthrus_block_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len, mode: int, out=None, lse=None,
+                       workspace=None, softmax_scale: float = 0.0, want_lse: bool = True,
+                       stream=None):
+    """Block attention of one layer; returns (out bf16 [B,Hq,K,D], lse fp32 [B,Hq,K] or None)."""
+    _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len)
+    desc = attn_desc(q, k_cache, softmax_scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, tuple(q.shape), dev)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, tuple(q.shape[:3]), dev)
+    nbytes = orthrus_attn_workspace_size(desc)
+    ws = _workspace(nbytes, dev, workspace)
+    st = _lib.load().orthrus_block_attn(
+        ctypes.byref(desc), int(mode), q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
+        k_cache.data_ptr(), v_cache.data_ptr(), cache_len.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_block_attn", st)
+    return out, lse
+
+
+def orthrus_block_attn_diff(q, k_blk, v_blk, k_cache, v_cache, cache_len, **kw):
+    """Diffusion-view block attention (bidirectional within the block)."""
+    return orthrus_block_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len, ORTHRUS_MASK_DIFF_BIDIR, **kw)
+
+
+def orthrus_block_attn_verify(q, k_blk, v_blk, k_cache, v_cache, cache_len, **kw):
+    """AR verify block attention (causal within the block)."""
+    return orthrus_block_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len, ORTHRUS_MASK_VERIFY_CAUSAL,
+                              **kw)
+
+
+class PreparedAttention:
+    """A block-attention call with every pointer resolved once.
+
+    For launch loops (one call per layer per view): calling the object issues
+    exactly one C call on the given stream.  The tensors are held so that
+    their memory stays alive as long as the object.
+    """
+
+    def __init__(self, mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
+                 softmax_scale: float = 0.0):
+        _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len)
+        self.desc = attn_desc(q, k_cache, softmax_scale)
+        self._keep = (q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace)
+        nbytes = orthrus_attn_workspace_size(self.desc)
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")
+        lib = _lib.load()
+        self._fn = lib.orthrus_block_attn
+        self._args = (ctypes.byref(self.desc), int(mode), q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
+                      k_cache.data_ptr(), v_cache.data_ptr(), cache_len.data_ptr(), out.data_ptr(),
+                      lse.data_ptr() if lse is not None else None, workspace.data_ptr(),
+                      workspace.numel())
+
+        self._partial = lib.orthrus_block_attn_partial
+        self._partial_args = self._args[:8] + self._args[10:]
+        self._merge = lib.orthrus_block_attn_merge
+        self._merge_args = (self._args[0],) + self._args[8:]
+
+    def __call__(self, stream_ptr: int) -> None:
+        st = self._fn(*self._args, stream_ptr)
+        if st:
+            _lib.check("orthrus_block_attn", st)
+
+    def partial(self, stream_ptr: int) -> None:
+        """First half only: stream the cache into the split partials."""
+        st = self._partial(*self._partial_args, stream_ptr)
+        if st:
+            _lib.check("orthrus_block_attn_partial", st)
+
+    def merge(self, stream_ptr: int) -> None:
+        """Second half only: merge the split partials into out / lse."""
+        st = self._merge(*self._merge_args, stream_ptr)
+        if st:
+            _lib.check("orthrus_block_attn_merge", st)
+
+
+class PreparedGreedy:
+    """A greedy-consensus call with every pointer resolved once."""
+
+    def __init__(self, logits, cand, accept_len, row_argmax, correction, workspace):
+        B, K, V = logits.shape
+        dev = logits.device
+        _need(logits, "logits", torch.float32, (B, K, V))
+        _need(cand, "cand", torch.int32, (B, K), dev)
+        nbytes = orthrus_consensus_workspace_size(B, K, V)
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")
+        self._keep = (logits, cand, accept_len, row_argmax, correction, workspace)
+        self._fn = _lib.load().orthrus_consensus_greedy
+        self._args = (B, K, V, logits.data_ptr(), cand.data_ptr(), accept_len.data_ptr(),
+                      row_argmax.data_ptr() if row_argmax is not None else None, correction.data_ptr(),
+                      workspace.data_ptr(), workspace.numel())
+
+    def __call__(self, stream_ptr: int) -> None:
+        st = self._fn(*self._args, stream_ptr)
+        if st:
+            _lib.check("orthrus_consensus_greedy", st)
+
+
+def orthrus_consensus_greedy(logits, cand, accept_len=None, row_argmax=None, correction=None,
+                             workspace=None, want_row_argmax: bool = True, stream=None):
+    """Greedy consensus; returns (accept_len [B], row_argmax [B,K] or None, correction [B])."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, K, V]")
+    B, K, V = logits.shape
+    dev = logits.device
+    _need(logits, "logits", torch.float32, (B, K, V))
+    _need(cand, "cand", torch.int32, (B, K), dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if correction is None:
+        correction = torch.empty(B, dtype=torch.int32, device=dev)
+    if row_argmax is None and want_row_argmax:
+        row_argmax = torch.empty((B, K), dtype=torch.int32, device=dev)
+    _need(accept_len, "accept_len", torch.int32, (B,), dev)
+    _need(correction, "correction", torch.int32, (B,), dev)
+    if row_argmax is not None:
+        _need(row_argmax, "row_argmax", torch.int32, (B, K), dev)
+    ws = _workspace(orthrus_consensus_workspace_size(B, K, V), dev, workspace)
+    st = _lib.load().orthrus_consensus_greedy(
+        B, K, V, logits.data_ptr(), cand.data_ptr(), accept_len.data_ptr(),
+        row_argmax.data_ptr() if row_argmax is not None else None, correction.data_ptr(),
+        ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_consensus_greedy", st)
+    return accept_len, row_argmax, correction
+
+
+def orthrus_consensus_sample(p_target, q_draft, cand, uniforms, accept_len=None, correction=None,
+                             workspace=None, stream=None):
+    """T>0 rejection-sampling consensus; returns (accept_len [B], correction [B])."""
+    if p_target.dim() != 3:
+        raise ValueError("p_target must be [B, K, V]")
+    B, K, V = p_target.shape
+    dev = p_target.device
+    _need(p_target, "p_target", torch.float32, (B, K, V))
+    _need(q_draft, "q_draft", torch.float32, (B, K, V), dev)
+    _need(cand, "cand", torch.int32, (B, K), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if correction is None:
+        correction = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(accept_len, "accept_len", torch.int32, (B,), dev)
+    _need(correction, "correction", torch.int32, (B,), dev)
+    ws = _workspace(orthrus_consensus_workspace_size(B, K, V), dev, workspace)
+    st = _lib.load().orthrus_consensus_sample(
+        B, K, V, p_target.data_ptr(), q_draft.data_ptr(), cand.data_ptr(), uniforms.data_ptr(),
+        accept_len.data_ptr(), correction.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_consensus_sample", st)
+    return accept_len, correction

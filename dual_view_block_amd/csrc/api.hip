@@ -1,0 +1,254 @@
+// Host side of the C ABI declared in include/orthrus.h: argument validation
+// (before any HIP call), launch planning from the descriptor alone, and
+// stream-ordered launches.  No allocation, no synchronisation, no state.
+#include "../../include/orthrus.h"
+#include "common.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+namespace orthrus {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int env_int(const char* name, int fallback) {
+  const char* s = getenv(name);
+  if (s == nullptr || *s == '\0') return fallback;
+  const int v = atoi(s);
+  return v > 0 ? v : fallback;
+}
+
+orthrus_status check_desc(const orthrus_attn_desc* d) {
+  if (d == nullptr) return ORTHRUS_ERR_NULL_PTR;
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->block_k < 1 ||
+      d->max_len < 0 || d->head_dim < 1)
+    return ORTHRUS_ERR_BAD_SHAPE;
+  if (d->n_q_heads % d->n_kv_heads != 0) return ORTHRUS_ERR_BAD_SHAPE;
+  if (!(isfinite(d->softmax_scale) && d->softmax_scale >= 0.0f)) return ORTHRUS_ERR_BAD_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return ORTHRUS_ERR_UNSUPPORTED;
+  if (d->block_k > 32) return ORTHRUS_ERR_UNSUPPORTED;
+  // every element offset must fit comfortably in 63 bits and every grid dimension in range
+  const long long rows = (long long)(d->n_q_heads / d->n_kv_heads) * d->block_k;
+  if ((long long)d->batch * d->n_kv_heads > 65535LL || rows > (1LL << 20)) return ORTHRUS_ERR_BAD_SHAPE;
+  return ORTHRUS_OK;
+}
+
+AttnPlan make_plan(const orthrus_attn_desc* d) {
+  AttnPlan p{};
+  const int G = d->n_q_heads / d->n_kv_heads;
+  p.rows = G * d->block_k;
+  p.qblocks = p.rows <= 32 ? 1 : (p.rows <= 64 ? 2 : 4);
+  p.rows_per_wg = 32 * p.qblocks;
+  p.row_groups = (p.rows + p.rows_per_wg - 1) / p.rows_per_wg;
+  const long long groups = (long long)d->batch * d->n_kv_heads * p.row_groups;
+  long long s = (kTargetAttnGroups + groups - 1) / groups;
+  const long long max_tiles = (d->max_len + kTileKeys - 1) / kTileKeys;
+  if (s > max_tiles) s = max_tiles;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 1) s = 1;
+  p.splits = env_int("ORTHRUS_SPLITS", (int)s);
+  if (p.splits > kMaxSplits) p.splits = kMaxSplits;
+  const size_t slots = (size_t)groups * p.splits * p.rows_per_wg;
+  p.acc_bytes = round_up(slots * d->head_dim * sizeof(float), kAlign);
+  p.ml_bytes = round_up(slots * 2 * sizeof(float), kAlign);
+  p.ws_bytes = p.acc_bytes + p.ml_bytes;
+  return p;
+}
+
+// phases: 1 = partial (stream cache + block), 2 = merge, 3 = both
+orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q, const uint16_t* k_blk,
+                        const uint16_t* v_blk, const uint16_t* k_cache, const uint16_t* v_cache,
+                        const int32_t* cache_len, uint16_t* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream, int phases) {
+  const orthrus_status st = check_desc(d);
+  if (st != ORTHRUS_OK) return st;
+  if (mode != ORTHRUS_MASK_DIFF_BIDIR && mode != ORTHRUS_MASK_VERIFY_CAUSAL) return ORTHRUS_ERR_BAD_SHAPE;
+  if (!workspace) return ORTHRUS_ERR_NULL_PTR;
+  if ((phases & 1) && (!q || !k_blk || !v_blk || !k_cache || !v_cache || !cache_len))
+    return ORTHRUS_ERR_NULL_PTR;
+  if ((phases & 2) && !out) return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(workspace)) return ORTHRUS_ERR_MISALIGNED;
+  if ((phases & 1) && (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
+                       !aligned16(v_cache) || !aligned4(cache_len)))
+    return ORTHRUS_ERR_MISALIGNED;
+  if ((phases & 2) && (!aligned16(out) || (lse && !aligned4(lse)))) return ORTHRUS_ERR_MISALIGNED;
+  const AttnPlan plan = make_plan(d);
+  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+
+  AttnArgs a{};
+  a.q = q;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_len = cache_len;
+  a.out = out;
+  a.lse = lse;
+  a.ws_acc = reinterpret_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + plan.acc_bytes);
+  a.batch = d->batch;
+  a.n_q_heads = d->n_q_heads;
+  a.n_kv_heads = d->n_kv_heads;
+  a.group = d->n_q_heads / d->n_kv_heads;
+  a.block_k = d->block_k;
+  a.head_dim = d->head_dim;
+  a.max_len = d->max_len;
+  a.causal = mode == ORTHRUS_MASK_VERIFY_CAUSAL ? 1 : 0;
+  const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if ((phases & 1) && getenv("ORTHRUS_DEBUG") != nullptr)
+    fprintf(stderr, "[orthrus] attn mode=%d B=%d Hq=%d Hkv=%d D=%d K=%d max_len=%d rows=%d qblocks=%d "
+            "row_groups=%d splits=%d ws=%zu\n", mode, d->batch, d->n_q_heads, d->n_kv_heads,
+            d->head_dim, d->block_k, d->max_len, plan.rows, plan.qblocks, plan.row_groups,
+            plan.splits, plan.ws_bytes);
+  const hipError_t e = launch_block_attention(a, plan, phases, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status check_consensus_sizes(int32_t B, int32_t K, int32_t V) {
+  if (B < 1 || K < 1 || V < 1) return ORTHRUS_ERR_BAD_SHAPE;
+  if (K > 32) return ORTHRUS_ERR_UNSUPPORTED;
+  if ((long long)B * K > 65535LL) return ORTHRUS_ERR_BAD_SHAPE;
+  return ORTHRUS_OK;
+}
+
+ConsensusPlan make_consensus_plan(int32_t B, int32_t K, int32_t V) {
+  ConsensusPlan p{};
+  const long long rows = (long long)B * K;
+  long long gc = (1024 + rows - 1) / rows;
+  long long gmax = V / 1024;
+  if (gmax < 1) gmax = 1;
+  if (gc > gmax) gc = gmax;
+  if (gc < 1) gc = 1;
+  p.greedy_chunks = (int)gc;
+  long long sc = (V + 4095) / 4096;
+  if (sc > 256) sc = 256;
+  if (sc < 1) sc = 1;
+  p.sample_chunks = (int)sc;
+  p.greedy_bytes = round_up((size_t)rows * p.greedy_chunks * 8, kAlign);
+  p.sample_bytes = round_up((size_t)B * p.sample_chunks * 2 * 8 + (size_t)B * 4, kAlign);
+  p.ws_bytes = p.greedy_bytes > p.sample_bytes ? p.greedy_bytes : p.sample_bytes;
+  return p;
+}
+
+}  // namespace
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" {
+
+size_t orthrus_attn_workspace_size(const orthrus_attn_desc* d) {
+  if (check_desc(d) != ORTHRUS_OK) return 0;
+  return make_plan(d).ws_bytes;
+}
+
+int32_t orthrus_attn_num_splits(const orthrus_attn_desc* d) {
+  if (check_desc(d) != ORTHRUS_OK) return -1;
+  return make_plan(d).splits;
+}
+
+orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, orthrus_mask_mode mode, const uint16_t* q,
+                                  const uint16_t* k_blk, const uint16_t* v_blk, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int32_t* cache_len, uint16_t* out,
+                                  float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attn(d, (int)mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
+                  workspace_bytes, stream, 3);
+}
+
+orthrus_status orthrus_block_attn_partial(const orthrus_attn_desc* d, orthrus_mask_mode mode,
+                                          const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
+                                          const uint16_t* k_cache, const uint16_t* v_cache,
+                                          const int32_t* cache_len, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  return run_attn(d, (int)mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, nullptr, nullptr, workspace,
+                  workspace_bytes, stream, 1);
+}
+
+orthrus_status orthrus_block_attn_merge(const orthrus_attn_desc* d, uint16_t* out, float* lse,
+                                        const void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attn(d, ORTHRUS_MASK_DIFF_BIDIR, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, out, lse,
+                  const_cast<void*>(workspace), workspace_bytes, stream, 2);
+}
+
+orthrus_status orthrus_block_attn_diff(const orthrus_attn_desc* d, const uint16_t* q, const uint16_t* k_blk,
+                                       const uint16_t* v_blk, const uint16_t* k_cache,
+                                       const uint16_t* v_cache, const int32_t* cache_len, uint16_t* out,
+                                       float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attn(d, ORTHRUS_MASK_DIFF_BIDIR, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse,
+                  workspace, workspace_bytes, stream, 3);
+}
+
+orthrus_status orthrus_block_attn_verify(const orthrus_attn_desc* d, const uint16_t* q,
+                                         const uint16_t* k_blk, const uint16_t* v_blk,
+                                         const uint16_t* k_cache, const uint16_t* v_cache,
+                                         const int32_t* cache_len, uint16_t* out, float* lse,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attn(d, ORTHRUS_MASK_VERIFY_CAUSAL, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse,
+                  workspace, workspace_bytes, stream, 3);
+}
+
+size_t orthrus_consensus_workspace_size(int32_t batch, int32_t block_k, int32_t vocab) {
+  if (check_consensus_sizes(batch, block_k, vocab) != ORTHRUS_OK) return 0;
+  return make_consensus_plan(batch, block_k, vocab).ws_bytes;
+}
+
+orthrus_status orthrus_consensus_greedy(int32_t batch, int32_t block_k, int32_t vocab, const float* logits,
+                                        const int32_t* cand, int32_t* accept_len, int32_t* row_argmax,
+                                        int32_t* correction, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  const orthrus_status st = check_consensus_sizes(batch, block_k, vocab);
+  if (st != ORTHRUS_OK) return st;
+  if (!logits || !cand || !accept_len || !correction || !workspace) return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(logits) || !aligned4(cand) || !aligned4(accept_len) || !aligned4(correction) ||
+      (row_argmax && !aligned4(row_argmax)) || !aligned16(workspace))
+    return ORTHRUS_ERR_MISALIGNED;
+  const ConsensusPlan plan = make_consensus_plan(batch, block_k, vocab);
+  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+  const hipError_t e = launch_consensus_greedy(batch, block_k, vocab, logits, cand, accept_len, row_argmax,
+                                               correction, workspace, plan,
+                                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status orthrus_consensus_sample(int32_t batch, int32_t block_k, int32_t vocab, const float* p_target,
+                                        const float* q_draft, const int32_t* cand, const float* uniforms,
+                                        int32_t* accept_len, int32_t* correction, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  const orthrus_status st = check_consensus_sizes(batch, block_k, vocab);
+  if (st != ORTHRUS_OK) return st;
+  if (!p_target || !q_draft || !cand || !uniforms || !accept_len || !correction || !workspace)
+    return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(p_target) || !aligned16(q_draft) || !aligned4(cand) || !aligned4(uniforms) ||
+      !aligned4(accept_len) || !aligned4(correction) || !aligned16(workspace))
+    return ORTHRUS_ERR_MISALIGNED;
+  const ConsensusPlan plan = make_consensus_plan(batch, block_k, vocab);
+  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+  const hipError_t e = launch_consensus_sample(batch, block_k, vocab, p_target, q_draft, cand, uniforms,
+                                               accept_len, correction, workspace, plan,
+                                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+const char* orthrus_status_string(orthrus_status s) {
+  switch (s) {
+    case ORTHRUS_OK: return "ORTHRUS_OK";
+    case ORTHRUS_ERR_NULL_PTR: return "ORTHRUS_ERR_NULL_PTR: a required pointer is NULL";
+    case ORTHRUS_ERR_BAD_SHAPE: return "ORTHRUS_ERR_BAD_SHAPE: a size is out of range or inconsistent";
+    case ORTHRUS_ERR_UNSUPPORTED: return "ORTHRUS_ERR_UNSUPPORTED: valid size that this build does not support";
+    case ORTHRUS_ERR_MISALIGNED: return "ORTHRUS_ERR_MISALIGNED: a device pointer is not 16-byte aligned";
+    case ORTHRUS_ERR_WORKSPACE_TOO_SMALL: return "ORTHRUS_ERR_WORKSPACE_TOO_SMALL: workspace below the size query";
+    case ORTHRUS_ERR_HIP: return "ORTHRUS_ERR_HIP: the HIP runtime refused the launch";
+  }
+  return "ORTHRUS_ERR_UNKNOWN";
+}
+
+}  // extern "C"

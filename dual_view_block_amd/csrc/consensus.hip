@@ -1,0 +1,323 @@
+// In-model consensus for gfx950: greedy argmax matching and exact
+// rejection sampling (Orthrus paper notes, zhangshuibai.github.io, §4.1 step
+// 3, §4.2, §4.3 and §7.2).
+//
+// Greedy: the verify logits [B, K, V] are scanned once.  A row's argmax is the
+// maximum of a 64-bit key (order-preserving float bits << 32 | ~index), so the
+// lowest index wins ties, NaN (canonical key 0xFFFFFFFF) beats every number,
+// and -0 is folded onto +0.  Reduction order cannot change a max, so the
+// result is bit-exact.  Stage 1: one work-group per (row, vocab chunk) with
+// 128-bit loads and wave-shuffle reductions; stage 2: one wave per sequence
+// reduces the chunks, compares candidates with a ballot and takes the first
+// mismatch.
+//
+// Sampling: one wave per sequence evaluates the accept tests u*q < p exactly
+// in fp64 and takes the first rejection a.  If a < K, the residual of row a is
+// drawn by an integer inverse CDF: w_v = max(0, F(p) - F(q)) with
+// F(x) = floor(clamp(x,0,1) * 2^60) in uint64, chunk sums per work-group,
+// then one work-group scans the chunk sums, finds the chunk holding the
+// target T = floor(m*S/2^24) (128-bit product) and scans inside it.  Integer
+// sums make the pick independent of reduction order.
+#include "common.h"
+
+namespace orthrus {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (x != x) return 0xFFFFFFFFu;  // NaN ranks above every number
+  if (x == 0.0f) u = 0u;           // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ unsigned long long pack_key(float x, uint32_t idx) {
+  return ((unsigned long long)order_key(x) << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+  return a > b ? a : b;
+}
+
+__device__ __forceinline__ unsigned long long wave_max64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = umax64(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_sum64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ---------------------------------------------------------------- greedy --
+__global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* __restrict__ logits,
+                                                                  int vocab, int chunk_len,
+                                                                  unsigned long long* part) {
+  const int c = blockIdx.x;
+  const size_t row = blockIdx.y;
+  const int begin = c * chunk_len;
+  const int end = min(vocab, begin + chunk_len);
+  const float* rp = logits + row * (size_t)vocab;
+  unsigned long long best = 0;  // below every packed key of a real element
+  if ((vocab & 3) == 0) {
+    // chunk_len is a multiple of 4, so begin is 16-byte aligned within the row
+    for (int v = begin + 4 * threadIdx.x; v < end; v += 4 * kThreads) {
+      const float4 x = *reinterpret_cast<const float4*>(rp + v);
+      best = umax64(best, pack_key(x.x, v));
+      best = umax64(best, pack_key(x.y, v + 1));
+      best = umax64(best, pack_key(x.z, v + 2));
+      best = umax64(best, pack_key(x.w, v + 3));
+    }
+  } else {
+    for (int v = begin + threadIdx.x; v < end; v += kThreads) best = umax64(best, pack_key(rp[v], v));
+  }
+  __shared__ unsigned long long red[kThreads / 64];
+  best = wave_max64(best);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long m = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) m = umax64(m, red[w]);
+    part[row * gridDim.x + c] = m;
+  }
+}
+
+__global__ __launch_bounds__(64) void greedy_finalize_kernel(int block_k, int chunks,
+                                                             const unsigned long long* part,
+                                                             const int32_t* cand, int32_t* accept_len,
+                                                             int32_t* row_argmax, int32_t* correction) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  int am = -1;
+  bool mismatch = false;
+  if (i < block_k) {
+    const unsigned long long* pp = part + ((size_t)b * block_k + i) * chunks;
+    unsigned long long m = 0;
+    for (int c = 0; c < chunks; ++c) m = umax64(m, pp[c]);
+    am = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+    mismatch = cand[(size_t)b * block_k + i] != am;
+    if (row_argmax != nullptr) row_argmax[(size_t)b * block_k + i] = am;
+  }
+  const unsigned long long mm = __ballot(mismatch);
+  const int a = mm ? __builtin_ctzll(mm) : block_k;
+  const int am_a = __shfl(am, a < block_k ? a : 0);
+  if (i == 0) {
+    accept_len[b] = a;
+    correction[b] = a < block_k ? am_a : -1;
+  }
+}
+
+// -------------------------------------------------------------- sampling --
+__device__ __forceinline__ unsigned long long fixed_point(float x) {
+  const float c = (x > 0.0f) ? fminf(x, 1.0f) : 0.0f;  // NaN and negatives -> 0
+  return (unsigned long long)((double)c * 1152921504606846976.0);  // 2^60, exact
+}
+
+__global__ __launch_bounds__(64) void sample_accept_kernel(int block_k, int vocab,
+                                                           const float* __restrict__ p,
+                                                           const float* __restrict__ q,
+                                                           const int32_t* __restrict__ cand,
+                                                           const float* __restrict__ uniforms,
+                                                           int32_t* accept_len, int32_t* correction,
+                                                           int32_t* ws_a) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  bool reject = false;
+  if (i < block_k) {
+    const size_t row = (size_t)b * block_k + i;
+    const int c = cand[row];
+    const bool valid = c >= 0 && c < vocab;
+    const float pv = valid ? p[row * vocab + c] : 0.0f;
+    const float qv = valid ? q[row * vocab + c] : 0.0f;
+    const float u = uniforms[(size_t)b * (block_k + 1) + i];
+    const bool acc = valid && (__dmul_rn((double)u, (double)qv) < (double)pv);
+    reject = !acc;
+  }
+  const unsigned long long mm = __ballot(reject);
+  const int a = mm ? __builtin_ctzll(mm) : block_k;
+  if (i == 0) {
+    accept_len[b] = a;
+    ws_a[b] = a;
+    if (a >= block_k) correction[b] = -1;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void residual_chunks_kernel(int block_k, int vocab, int chunk_len,
+                                                                   const float* __restrict__ p,
+                                                                   const float* __restrict__ q,
+                                                                   const int32_t* ws_a,
+                                                                   unsigned long long* sums) {
+  const int c = blockIdx.x;
+  const int b = blockIdx.y;
+  const int a = ws_a[b];
+  if (a >= block_k) return;
+  const size_t row = ((size_t)b * block_k + a) * vocab;
+  const int begin = c * chunk_len;
+  const int end = min(vocab, begin + chunk_len);
+  unsigned long long sw = 0, sp = 0;
+  for (int v = begin + threadIdx.x; v < end; v += kThreads) {
+    const unsigned long long fp = fixed_point(p[row + v]);
+    const unsigned long long fq = fixed_point(q[row + v]);
+    sw += fp > fq ? fp - fq : 0ull;
+    sp += fp;
+  }
+  __shared__ unsigned long long red[2][kThreads / 64];
+  sw = wave_sum64(sw);
+  sp = wave_sum64(sp);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = sw;
+    red[1][threadIdx.x >> 6] = sp;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long tw = 0, tp = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      tw += red[0][w];
+      tp += red[1][w];
+    }
+    sums[((size_t)b * gridDim.x + c) * 2 + 0] = tw;
+    sums[((size_t)b * gridDim.x + c) * 2 + 1] = tp;
+  }
+}
+
+// Inclusive block-wide scan of one uint64 per thread; also returns the total.
+__device__ unsigned long long block_scan64(unsigned long long v, unsigned long long* total,
+                                           unsigned long long* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  if (lane == 63) scratch[w] = v;
+  __syncthreads();
+  unsigned long long off = 0, tot = 0;
+  for (int k = 0; k < kThreads / 64; ++k) {
+    if (k < w) off += scratch[k];
+    tot += scratch[k];
+  }
+  __syncthreads();
+  *total = tot;
+  return v + off;
+}
+
+__global__ __launch_bounds__(kThreads) void residual_select_kernel(int block_k, int vocab, int chunk_len,
+                                                                   int chunks,
+                                                                   const float* __restrict__ p,
+                                                                   const float* __restrict__ q,
+                                                                   const float* __restrict__ uniforms,
+                                                                   const int32_t* ws_a,
+                                                                   const unsigned long long* sums,
+                                                                   int32_t* correction) {
+  const int b = blockIdx.x;
+  const int a = ws_a[b];
+  if (a >= block_k) return;
+  __shared__ unsigned long long scratch[kThreads / 64];
+  __shared__ int found;
+  // ---- totals of both weight families (chunks <= kThreads by construction)
+  const int c = threadIdx.x;
+  const unsigned long long cw = c < chunks ? sums[((size_t)b * chunks + c) * 2 + 0] : 0ull;
+  const unsigned long long cp = c < chunks ? sums[((size_t)b * chunks + c) * 2 + 1] : 0ull;
+  unsigned long long Sw, Sp;
+  const unsigned long long incw = block_scan64(cw, &Sw, scratch);
+  const unsigned long long incp = block_scan64(cp, &Sp, scratch);
+  const bool use_p = (Sw == 0);
+  const unsigned long long S = use_p ? Sp : Sw;
+  if (S == 0) {  // no probability mass at all: token 0
+    if (threadIdx.x == 0) correction[b] = 0;
+    return;
+  }
+  // ---- target T = floor(m * S / 2^24), m = floor(u_K * 2^24) in [0, 2^24)
+  const float u = uniforms[(size_t)b * (block_k + 1) + block_k];
+  float mf = (u > 0.0f) ? u * 16777216.0f : 0.0f;
+  unsigned long long m = (unsigned long long)mf;
+  if (m > 16777215ull) m = 16777215ull;
+  const unsigned long long lo = m * S;
+  const unsigned long long hi = __umul64hi(m, S);
+  const unsigned long long T = (hi << 40) | (lo >> 24);
+  // ---- chunk holding T: exclusive prefix <= T < inclusive prefix
+  const unsigned long long inc = use_p ? incp : incw;
+  const unsigned long long mine = use_p ? cp : cw;
+  if (threadIdx.x == 0) found = chunks - 1;
+  __syncthreads();
+  if (c < chunks && mine > 0 && inc - mine <= T && T < inc) found = c;
+  __syncthreads();
+  const int cs = found;
+  unsigned long long run = 0;
+  for (int k = 0; k < cs; ++k) run += sums[((size_t)b * chunks + k) * 2 + (use_p ? 1 : 0)];
+  // ---- scan inside the chunk, kThreads elements at a time
+  const size_t row = ((size_t)b * block_k + a) * vocab;
+  const int begin = cs * chunk_len;
+  const int end = min(vocab, begin + chunk_len);
+  __shared__ int pick;
+  if (threadIdx.x == 0) pick = -1;
+  __syncthreads();
+  for (int base = begin; base < end; base += kThreads) {
+    const int v = base + threadIdx.x;
+    unsigned long long w = 0;
+    if (v < end) {
+      const unsigned long long fp = fixed_point(p[row + v]);
+      if (use_p) {
+        w = fp;
+      } else {
+        const unsigned long long fq = fixed_point(q[row + v]);
+        w = fp > fq ? fp - fq : 0ull;
+      }
+    }
+    unsigned long long tot;
+    const unsigned long long incl = block_scan64(w, &tot, scratch) + run;
+    const bool hit = v < end && incl > T && incl - w <= T;
+    if (hit) pick = v;  // exactly one element satisfies both bounds
+    __syncthreads();
+    if (pick >= 0) break;
+    run += tot;
+  }
+  if (threadIdx.x == 0) correction[b] = pick >= 0 ? pick : end - 1;
+}
+
+}  // namespace
+
+hipError_t launch_consensus_greedy(int batch, int block_k, int vocab, const float* logits,
+                                   const int32_t* cand, int32_t* accept_len, int32_t* row_argmax,
+                                   int32_t* correction, void* workspace, const ConsensusPlan& plan,
+                                   hipStream_t stream) {
+  auto* part = reinterpret_cast<unsigned long long*>(workspace);
+  const int chunks = plan.greedy_chunks;
+  int chunk_len = (vocab + chunks - 1) / chunks;
+  chunk_len = (chunk_len + 3) & ~3;
+  hipLaunchKernelGGL(argmax_partial_kernel, dim3(chunks, batch * block_k), dim3(kThreads), 0, stream,
+                     logits, vocab, chunk_len, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(greedy_finalize_kernel, dim3(batch), dim3(64), 0, stream, block_k, chunks, part,
+                     cand, accept_len, row_argmax, correction);
+  return hipGetLastError();
+}
+
+hipError_t launch_consensus_sample(int batch, int block_k, int vocab, const float* p_target,
+                                   const float* q_draft, const int32_t* cand, const float* uniforms,
+                                   int32_t* accept_len, int32_t* correction, void* workspace,
+                                   const ConsensusPlan& plan, hipStream_t stream) {
+  auto* ws = reinterpret_cast<uint8_t*>(workspace);
+  auto* sums = reinterpret_cast<unsigned long long*>(ws);
+  auto* ws_a = reinterpret_cast<int32_t*>(ws + (size_t)batch * plan.sample_chunks * 2 * 8);
+  const int chunks = plan.sample_chunks;
+  const int chunk_len = (vocab + chunks - 1) / chunks;
+  hipLaunchKernelGGL(sample_accept_kernel, dim3(batch), dim3(64), 0, stream, block_k, vocab, p_target,
+                     q_draft, cand, uniforms, accept_len, correction, ws_a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(residual_chunks_kernel, dim3(chunks, batch), dim3(kThreads), 0, stream, block_k,
+                     vocab, chunk_len, p_target, q_draft, ws_a, sums);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(residual_select_kernel, dim3(batch), dim3(kThreads), 0, stream, block_k, vocab,
+                     chunk_len, chunks, p_target, q_draft, uniforms, ws_a, sums, correction);
+  return hipGetLastError();
+}
+
+}  // namespace orthrus

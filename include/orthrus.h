@@ -1,0 +1,191 @@
+/*
+ * orthrus.h -- C ABI of the MI355X (gfx950) dual-view decode-step library.
+ *
+ * One Orthrus decode cycle over a frozen AR model's shared KV cache runs, per
+ * layer, a diffusion-view block attention and an AR verify attention, then one
+ * consensus over the verify distributions.  Sources for what each call
+ * computes (the Orthrus pages):
+ *   - Paper notes on Orthrus (zhangshuibai.github.io paper-notes,
+ *     "Orthrus: Memory-Efficient Parallel Token Generation via Dual-View
+ *     Diffusion"): §2.1-2.2 (two views share one KV cache; the diffusion K/V
+ *     of the block are transient), §3.2 (block mask), §4.1-4.3 (the cycle:
+ *     parallel projection, AR verification, consensus; greedy and T>0).
+ *   - hotdry.top blog post on Orthrus dual-view diffusion decoding, sections
+ *     on the dual-view attention architecture and on in-model consensus.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major arrays with
+ *     the shapes given below; bf16 values travel as uint16_t bit patterns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream).  No call synchronises, allocates or frees,
+ *     and the library keeps no pointer after it returns: buffers must stay
+ *     alive until the stream has passed the call.
+ *   - All argument checks run on the host before anything is enqueued; on a
+ *     non-OK status nothing was enqueued.  No exception crosses the ABI.
+ *   - Calls are reentrant and thread-safe (the library has no mutable state).
+ *   - Device buffers must be 16-byte aligned (128-bit loads and stores).
+ */
+#ifndef ORTHRUS_H
+#define ORTHRUS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ORTHRUS_OK = 0,
+  ORTHRUS_ERR_NULL_PTR = 1,            /* a required pointer is NULL */
+  ORTHRUS_ERR_BAD_SHAPE = 2,           /* a size is out of range or inconsistent */
+  ORTHRUS_ERR_UNSUPPORTED = 3,         /* valid but not built (e.g. head_dim 96) */
+  ORTHRUS_ERR_MISALIGNED = 4,          /* a device pointer is not 16-byte aligned */
+  ORTHRUS_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the size query */
+  ORTHRUS_ERR_HIP = 6                  /* the HIP runtime refused the launch */
+} orthrus_status;
+
+/* Which block keys a block row may see (paper notes §3.2 and §4.1):
+ * DIFF_BIDIR   -- diffusion view: every block row sees all K block keys
+ *                 (anchor + K-1 mask positions attend to each other);
+ * VERIFY_CAUSAL -- AR verify pass: block row i sees block keys j <= i.
+ * In both modes every row sees all cached positions [0, cache_len[b]). */
+typedef enum {
+  ORTHRUS_MASK_DIFF_BIDIR = 0,
+  ORTHRUS_MASK_VERIFY_CAUSAL = 1
+} orthrus_mask_mode;
+
+typedef struct {
+  int32_t batch;         /* B >= 1 sequences */
+  int32_t n_q_heads;     /* Hq >= 1, a multiple of n_kv_heads */
+  int32_t n_kv_heads;    /* Hkv >= 1; q head h reads KV head h / (Hq / Hkv) */
+  int32_t head_dim;      /* D, 64 or 128 (other values: ORTHRUS_ERR_UNSUPPORTED) */
+  int32_t block_k;       /* K, 1..32 block positions (anchor + K-1 masks) */
+  int32_t max_len;       /* cache capacity per sequence = row stride of the cache */
+  float softmax_scale;   /* 0 -> 1/sqrt(D) */
+} orthrus_attn_desc;
+
+/* Workspace bytes that orthrus_block_attn* needs for `d` (0 if `d` is invalid).
+ * Depends only on the descriptor's shapes -- never on the cached lengths --
+ * so one buffer serves every decode step of a sequence batch. */
+size_t orthrus_attn_workspace_size(const orthrus_attn_desc* d);
+
+/* Number of cache splits one (sequence, KV head) is streamed in (diagnostic;
+ * -1 if `d` is invalid).  Also fixed by the descriptor alone. */
+int32_t orthrus_attn_num_splits(const orthrus_attn_desc* d);
+
+/* Dual-view block attention of one layer (paper notes §2.1, §3.2, §4.1).
+ *
+ * For every sequence b, q head h (KV head g = h / (Hq/Hkv)) and block row i,
+ * with L = clamp(cache_len[b], 0, max_len):
+ *   keys   = k_cache[b, g, 0:L] ++ k_blk[b, g, 0:K]   (values likewise)
+ *   s_j    = softmax_scale * <q[b, h, i], key_j>, over the keys `mode` allows
+ *   out    = sum_j softmax(s)_j * value_j              (one joint softmax)
+ *   lse    = ln sum_j exp(s_j)
+ *
+ *   q        bf16 [B, Hq, K, D]
+ *   k_blk    bf16 [B, Hkv, K, D]  diffusion view: the transient K_diff of the
+ *                                 block; verify: the AR keys of the block tokens
+ *   v_blk    bf16 [B, Hkv, K, D]
+ *   k_cache  bf16 [B, Hkv, max_len, D]  shared AR cache; read-only, rows >= L
+ *                                        are never read
+ *   v_cache  bf16 [B, Hkv, max_len, D]
+ *   cache_len int32 [B] on the device (positions before the anchor)
+ *   out      bf16 [B, Hq, K, D]  (written)
+ *   lse      fp32 [B, Hq, K]     natural-log LSE (written; may be NULL)
+ *   workspace  device scratch of at least orthrus_attn_workspace_size(d)
+ *              bytes; contents need no initialisation and are clobbered.
+ * Neither k_blk/v_blk nor anything else is ever written into the cache. */
+orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, orthrus_mask_mode mode,
+                                  const uint16_t* q, const uint16_t* k_blk,
+                                  const uint16_t* v_blk, const uint16_t* k_cache,
+                                  const uint16_t* v_cache, const int32_t* cache_len,
+                                  uint16_t* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* orthrus_block_attn with mode = ORTHRUS_MASK_DIFF_BIDIR: the diffusion view's
+ * block attention (anchor + K-1 masks, bidirectional within the block). */
+orthrus_status orthrus_block_attn_diff(const orthrus_attn_desc* d, const uint16_t* q,
+                                       const uint16_t* k_blk, const uint16_t* v_blk,
+                                       const uint16_t* k_cache, const uint16_t* v_cache,
+                                       const int32_t* cache_len, uint16_t* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* orthrus_block_attn with mode = ORTHRUS_MASK_VERIFY_CAUSAL: the AR verify
+ * pass over the K candidate tokens (causal within the block, paper notes
+ * §4.1 step 2). */
+orthrus_status orthrus_block_attn_verify(const orthrus_attn_desc* d, const uint16_t* q,
+                                         const uint16_t* k_blk, const uint16_t* v_blk,
+                                         const uint16_t* k_cache, const uint16_t* v_cache,
+                                         const int32_t* cache_len, uint16_t* out, float* lse,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/* The two halves of orthrus_block_attn, for callers that schedule or time
+ * them separately (or, later, combine partials from several cache shards).
+ * orthrus_block_attn_partial streams the cache and the block and leaves one
+ * unnormalised partial softmax state (running max, running sum, weighted
+ * value sum) per query row and cache split in `workspace`;
+ * orthrus_block_attn_merge combines the splits into `out` and `lse` exactly as
+ * orthrus_block_attn does (the pair gives bit-identical results).  Both calls
+ * must get the same descriptor and workspace, in this order on one stream;
+ * arguments, layouts and errors are those of orthrus_block_attn. */
+orthrus_status orthrus_block_attn_partial(const orthrus_attn_desc* d, orthrus_mask_mode mode,
+                                          const uint16_t* q, const uint16_t* k_blk,
+                                          const uint16_t* v_blk, const uint16_t* k_cache,
+                                          const uint16_t* v_cache, const int32_t* cache_len,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+orthrus_status orthrus_block_attn_merge(const orthrus_attn_desc* d, uint16_t* out, float* lse,
+                                        const void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/* Workspace bytes for either consensus call (0 if the sizes are invalid). */
+size_t orthrus_consensus_workspace_size(int32_t batch, int32_t block_k, int32_t vocab);
+
+/* Greedy consensus (paper notes §4.1 step 3 and §4.2).
+ *   logits     fp32 [B, K, V]  AR verify logits; row i is checked against cand[i]
+ *   cand       int32 [B, K]    diffusion candidates
+ *   accept_len int32 [B]       a = leading rows with cand[i] == argmax(row i)
+ *   row_argmax int32 [B, K]    argmax of every row (may be NULL)
+ *   correction int32 [B]       argmax of row a if a < K, else -1 (no bonus)
+ * argmax: lowest index among equal maxima; NaN ranks above every number (first
+ * NaN wins); -0 equals +0.  Results are bit-exact (comparisons only).
+ * Sizes: 1 <= B, 1 <= K <= 32, 1 <= V < 2^31. */
+orthrus_status orthrus_consensus_greedy(int32_t batch, int32_t block_k, int32_t vocab,
+                                        const float* logits, const int32_t* cand,
+                                        int32_t* accept_len, int32_t* row_argmax,
+                                        int32_t* correction, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/* T>0 consensus by exact rejection sampling (paper notes §4.3 and §7.2,
+ * Leviathan/Chen rule).
+ *   p_target  fp32 [B, K, V]  AR probabilities at the sampling temperature
+ *   q_draft   fp32 [B, K, V]  diffusion probabilities; cand[b, i] ~ q_draft[b, i]
+ *   cand      int32 [B, K]    values in [0, V)
+ *   uniforms  fp32 [B, K+1]   on the 2^-24 grid in [0, 1): [0, K) accept tests,
+ *                             [K] the residual draw
+ *   accept_len int32 [B]      first i with NOT(u_i * q_i(cand_i) < p_i(cand_i)),
+ *                             evaluated exactly in fp64; K if none
+ *   correction int32 [B]      -1 if a == K; else the token picked from the residual
+ *                             w_v = max(0, F(p_a[v]) - F(q_a[v])),
+ *                             F(x) = floor(clamp(x, 0, 1) * 2^60) (w = F(p_a) if
+ *                             all w are 0; token 0 if that is 0 too):
+ *                             smallest v with prefix_sum(w)_v > floor(m * S / 2^24),
+ *                             S = sum w, m = floor(u_K * 2^24).
+ * Integer arithmetic makes the result bit-exact and independent of reduction
+ * order.  Rows must be probability vectors (each summing to at most 8);
+ * a cand outside [0, V) counts as a rejection. */
+orthrus_status orthrus_consensus_sample(int32_t batch, int32_t block_k, int32_t vocab,
+                                        const float* p_target, const float* q_draft,
+                                        const int32_t* cand, const float* uniforms,
+                                        int32_t* accept_len, int32_t* correction,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* orthrus_status_string(orthrus_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ORTHRUS_H */

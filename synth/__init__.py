@@ -109,6 +109,24 @@ def attention_inputs(w: Workload, layer: int = 0, device="cpu", seed_offset: int
     }
 
 
+def layer_cache(w: Workload, layer: int, device="cpu"):
+    """One layer's shared KV cache (k_cache, v_cache) bf16 [B,Hkv,max_len,D]."""
+    g = _gen(w.seed * 7919 + 104729 * layer + 1, device)
+    shape = (w.batch, w.n_kv_heads, w.capacity, w.head_dim)
+    return _randn_bf16(shape, g, device), _randn_bf16(shape, g, device)
+
+
+def view_inputs(w: Workload, layer: int, view: str, device="cpu"):
+    """The block inputs of one view at one layer: (q, k_blk, v_blk) bf16.
+
+    The diffusion view and the verify view get independent draws (different
+    projections of different block tokens in the real model)."""
+    g = _gen(w.seed * 7919 + 104729 * layer + (2 if view == "diff" else 3) + 17 * w.block_k, device)
+    B, Hq, Hkv, D, K = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_k
+    return (_randn_bf16((B, Hq, K, D), g, device), _randn_bf16((B, Hkv, K, D), g, device),
+            _randn_bf16((B, Hkv, K, D), g, device))
+
+
 def greedy_inputs(w: Workload, device="cpu", first_mismatch=None, ties: bool = False,
                   seed_offset: int = 0):
     """Verify logits [B,K,V] float32 and candidates [B,K] int32.

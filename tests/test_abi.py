@@ -1,0 +1,137 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented status before touching HIP.
+No compute call runs here (no GPU in this process)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import dual_view_block_amd as dvb
+from dual_view_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "orthrus.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(orthrus_[a-z0-9_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_named_entry_points():
+    names = _declared_functions()
+    for n in ("orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_consensus_greedy",
+              "orthrus_consensus_sample"):
+        assert n in names
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True)
+    if out.returncode == 0:
+        exported = set(re.findall(r"\bT (orthrus_\w+)", out.stdout))
+        assert exported == set(_declared_functions())
+
+
+def test_status_strings():
+    for code in range(7):
+        s = dvb.orthrus_status_string(code)
+        assert s.startswith("ORTHRUS_")
+    assert "UNKNOWN" in dvb.orthrus_status_string(99)
+
+
+def _desc(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, block_k=32, max_len=32768,
+                softmax_scale=0.0)
+    base.update(kw)
+    return _lib.AttnDesc(**base)
+
+
+def test_workspace_query_depends_on_shapes_only():
+    lib = _lib.load()
+    ws = lib.orthrus_attn_workspace_size(ctypes.byref(_desc()))
+    assert ws > 0
+    # the same descriptor always gives the same size: there is no length input at all
+    assert ws == lib.orthrus_attn_workspace_size(ctypes.byref(_desc()))
+    assert lib.orthrus_attn_num_splits(ctypes.byref(_desc())) >= 1
+    assert lib.orthrus_attn_workspace_size(ctypes.byref(_desc(head_dim=96))) == 0
+    assert lib.orthrus_attn_num_splits(ctypes.byref(_desc(n_q_heads=30))) == -1
+    assert lib.orthrus_consensus_workspace_size(1, 32, 151936) > 0
+    assert lib.orthrus_consensus_workspace_size(1, 33, 151936) == 0
+
+
+def _attn_call(desc, mode=0, ptrs=None, ws_bytes=1 << 30):
+    lib = _lib.load()
+    p = dict(q=4096, kb=4096, vb=4096, kc=4096, vc=4096, lens=4096, out=4096, lse=4096, ws=4096)
+    p.update(ptrs or {})
+    return lib.orthrus_block_attn(ctypes.byref(desc) if desc is not None else None, mode, p["q"], p["kb"],
+                                  p["vb"], p["kc"], p["vc"], p["lens"], p["out"], p["lse"], p["ws"],
+                                  ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expected", [
+    (dict(desc=None), _lib.ORTHRUS_ERR_NULL_PTR),
+    (dict(desc=_desc(batch=0)), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(n_q_heads=30)), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(block_k=0)), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(max_len=-1)), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(softmax_scale=float("nan"))), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(softmax_scale=-1.0)), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(head_dim=96)), _lib.ORTHRUS_ERR_UNSUPPORTED),
+    (dict(desc=_desc(block_k=33)), _lib.ORTHRUS_ERR_UNSUPPORTED),
+    (dict(desc=_desc(), mode=2), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(), ptrs=dict(kc=None)), _lib.ORTHRUS_ERR_NULL_PTR),
+    (dict(desc=_desc(), ptrs=dict(lens=None)), _lib.ORTHRUS_ERR_NULL_PTR),
+    (dict(desc=_desc(), ptrs=dict(q=4104)), _lib.ORTHRUS_ERR_MISALIGNED),
+    (dict(desc=_desc(), ptrs=dict(ws=4100)), _lib.ORTHRUS_ERR_MISALIGNED),
+    (dict(desc=_desc(), ws_bytes=16), _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_attention_argument_checks(case, expected):
+    assert _attn_call(case.get("desc"), case.get("mode", 0), case.get("ptrs"),
+                      case.get("ws_bytes", 1 << 30)) == expected
+
+
+def test_consensus_argument_checks():
+    lib = _lib.load()
+    P = 4096
+    assert lib.orthrus_consensus_greedy(0, 4, 10, P, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert lib.orthrus_consensus_greedy(1, 40, 10, P, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_consensus_greedy(1, 4, 10, None, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert lib.orthrus_consensus_greedy(1, 4, 10, P + 4, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_MISALIGNED
+    assert lib.orthrus_consensus_greedy(1, 4, 10, P, P, P, P, P, P, 1, None) == _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL
+    assert lib.orthrus_consensus_sample(1, 4, 10, P, P, P, None, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert lib.orthrus_consensus_sample(1, 4, 0, P, P, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+
+
+def test_valid_call_without_gpu_reports_hip_error():
+    """Run in a child process: a well-formed call on a host with no GPU must
+    come back as ORTHRUS_ERR_HIP (validation passed, the launch was refused)."""
+    code = (
+        "import ctypes, sys; sys.path.insert(0, %r)\n"
+        "from dual_view_block_amd import _lib\n"
+        "lib = _lib.load()\n"
+        "d = _lib.AttnDesc(1, 2, 1, 64, 4, 256, 0.0)\n"
+        "P = 4096\n"
+        "print(lib.orthrus_block_attn(ctypes.byref(d), 0, P, P, P, P, P, P, P, P, P, 1 << 30, None))\n"
+    ) % ROOT
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, env=env)
+    assert res.returncode == 0, res.stderr
+    assert int(res.stdout.strip().splitlines()[-1]) == _lib.ORTHRUS_ERR_HIP
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "dual_view_block_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in src.lower(), f

@@ -1,0 +1,125 @@
+"""GPU parity of greedy and rejection-sampling consensus: bit-exact against the
+oracle (accept_len, row_argmax, correction) on the same inputs."""
+import numpy as np
+import pytest
+import torch
+
+import dual_view_block_amd as dvb
+import oracle
+from synth import WORKLOADS, Workload, greedy_inputs, sample_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _greedy_gpu(logits, cand):
+    acc, am, corr = dvb.orthrus_consensus_greedy(logits.to(DEV), cand.to(DEV))
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), am.cpu().numpy(), corr.cpu().numpy()
+
+
+def _check_greedy(logits, cand, what):
+    acc, am, corr = _greedy_gpu(logits, cand)
+    racc, ram, rcorr = oracle.greedy_consensus(logits, cand)
+    assert np.array_equal(am, ram), f"{what}: row_argmax differs"
+    assert np.array_equal(acc, racc), f"{what}: accept_len {acc} vs {racc}"
+    assert np.array_equal(corr, rcorr), f"{what}: correction {corr} vs {rcorr}"
+    tokens = oracle.tokens_committed(acc, logits.shape[1])
+    assert tokens.min() >= 1 and tokens.max() <= logits.shape[1]
+    print(f"{what}: accept_len={acc.tolist()} correction={corr.tolist()}", flush=True)
+
+
+@pytest.mark.parametrize("j", [0, 1, 2, 3, 4])
+def test_greedy_tiny_every_first_mismatch(j):
+    """Vocab 1000, K = 4, logits sigma 4, planted first mismatch j (4 = all match)."""
+    logits, cand, _ = greedy_inputs(WORKLOADS["tiny"], first_mismatch=j)
+    _check_greedy(logits, cand, f"tiny j={j}")
+
+
+@pytest.mark.parametrize("j", [0, 1, 16, 31, 32])
+@pytest.mark.parametrize("ties", [False, True])
+def test_greedy_qwen_vocab(j, ties):
+    """[1, 32, 151936] logits, sigma 3, with and without planted ties."""
+    logits, cand, _ = greedy_inputs(WORKLOADS["qwen3_1p7b_layer"], first_mismatch=j, ties=ties)
+    _check_greedy(logits, cand, f"qwen j={j} ties={ties}")
+
+
+def test_greedy_batch_seeded_mismatch():
+    w = WORKLOADS["ragged_b16"]
+    logits, cand, _ = greedy_inputs(w)
+    _check_greedy(logits, cand, "batch16")
+
+
+@pytest.mark.parametrize("V", [3, 1001, 4099])
+def test_greedy_odd_vocab(V):
+    w = Workload("odd", 1, 3, 1, 1, 1, 1, 5, V, 2.0, 33)
+    logits, cand, _ = greedy_inputs(w)
+    _check_greedy(logits, cand, f"V={V}")
+
+
+def test_greedy_nan_signed_zero_and_infinities():
+    V, K = 5000, 4
+    logits = torch.randn(1, K, V) * 3
+    logits[0, 0, 17] = float("nan")
+    logits[0, 0, 4000] = float("nan")
+    logits[0, 1] = 0.0
+    logits[0, 1, :10] = -0.0
+    logits[0, 2, 99] = float("inf")
+    logits[0, 2, 3000] = float("inf")
+    logits[0, 3] = float("-inf")
+    cand = torch.tensor([[17, 0, 99, 0]], dtype=torch.int32)
+    _check_greedy(logits, cand, "special values")
+    acc, am, _ = _greedy_gpu(logits, cand)
+    assert am[0].tolist() == [17, 0, 99, 0] and acc[0] == 4
+
+
+def _check_sample(p, q, cand, u, what):
+    acc, corr = dvb.orthrus_consensus_sample(p.to(DEV), q.to(DEV), cand.to(DEV), u.to(DEV))
+    torch.cuda.synchronize()
+    acc, corr = acc.cpu().numpy(), corr.cpu().numpy()
+    racc, rcorr = oracle.sample_consensus(p, q, cand, u)
+    assert np.array_equal(acc, racc), f"{what}: accept_len {acc} vs {racc}"
+    assert np.array_equal(corr, rcorr), f"{what}: correction {corr} vs {rcorr}"
+    print(f"{what}: accept_len={acc.tolist()} correction={corr.tolist()}", flush=True)
+    return acc, corr
+
+
+@pytest.mark.parametrize("noise", [None, 0.5])
+def test_sample_ragged_b16_qwen_vocab(noise):
+    """B=16, K=32, V=151936; independent draft (rejects early) or a close one."""
+    p, q, cand, u = sample_inputs(WORKLOADS["ragged_b16"], draft_noise=noise)
+    _check_sample(p, q, cand, u, f"b16 noise={noise}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sample_small_vocab(seed):
+    w = Workload("s", 1, 8, 1, 1, 1, 1, 6, 37, 1.5, 40 + seed)
+    p, q, cand, u = sample_inputs(w, draft_noise=0.7 if seed % 2 else None)
+    _check_sample(p, q, cand, u, f"small seed={seed}")
+
+
+def test_sample_degenerate_cases():
+    B, K, V = 3, 4, 64
+    g = torch.Generator().manual_seed(3)
+    p = torch.softmax(torch.randn(B, K, V, generator=g, dtype=torch.float64), -1).float()
+    q = p.clone()
+    cand = torch.randint(0, V, (B, K), generator=g, dtype=torch.int32)
+    u = torch.tensor([[0.0, 0.5, 1 - 2 ** -24, 0.25, 0.75]] * B, dtype=torch.float32)
+    acc, corr = _check_sample(p, q, cand, u, "q == p")
+    assert (acc == K).all() and (corr == -1).all()
+    # target gives the candidate probability 0 at row 1 -> rejected there even for u = 0
+    p2 = p.clone()
+    p2[:, 1, :] = 0.0
+    p2[:, 1, 7] = 1.0
+    cand2 = cand.clone()
+    cand2[:, 1] = 8
+    u2 = torch.zeros(B, K + 1)
+    acc, corr = _check_sample(p2, q, cand2, u2, "p(cand)=0")
+    assert (acc == 1).all() and (corr == 7).all()
+    # residual identically zero (p == q) at the rejected row -> falls back to p
+    p3, q3 = p.clone(), p.clone()
+    cand3 = cand.clone()
+    cand3[:, 0] = 5
+    p3[:, 0, 5] = 0.0
+    q3[:, 0, 5] = 0.0
+    _check_sample(p3, q3, cand3, u2, "zero residual")
