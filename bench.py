@@ -55,11 +55,6 @@ def attn_bytes(w) -> int:
     return cache + q + blk + q  # out has q's shape
 
 
-def partial_bytes(w) -> int:
-    """Algorithmic bytes the streaming (partial) kernel must read per launch."""
-    return attn_bytes(w) - w.batch * w.n_q_heads * w.block_k * w.head_dim * 2
-
-
 def greedy_bytes(w) -> int:
     return w.batch * w.block_k * (w.vocab * 4 + 4) + w.batch * (4 + 4) + w.batch * w.block_k * 4
 
@@ -88,7 +83,7 @@ class Step:
                              device=device)
         ws_bytes = dvb.orthrus_attn_workspace_size(dvb.attn_desc(desc_q, caches[0][0]))
         self.splits = dvb.orthrus_attn_num_splits(dvb.attn_desc(desc_q, caches[0][0]))
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=device)  # counters start at zero
         for view, mode in (("diff", dvb.ORTHRUS_MASK_DIFF_BIDIR), ("verify", dvb.ORTHRUS_MASK_VERIFY_CAUSAL)):
             for layer, (kc, vc) in enumerate(caches):
                 q, kb, vb = view_inputs(w, layer, view, device)
@@ -147,60 +142,65 @@ def time_steps(step, steps: int, warmup: int, graph: bool):
 
 
 def time_kernels(step, reps: int = 2):
-    """Average device duration of the partial (cache-streaming) kernel and of
-    the merge kernel, from HIP events recorded around each launch on the
-    launch stream."""
+    """Average device duration of one block-attention launch (the fused
+    streaming + merge kernel), from HIP events recorded around each launch on
+    the launch stream, for the diffusion and the verify view."""
     import torch
 
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    pairs_p, pairs_m = [], []
+    pairs = []
     for _ in range(reps):
         for view in ("diff", "verify"):
             for c in step.calls[view]:
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                e[0].record(stream)
-                c.partial(sp)
-                e[1].record(stream)
-                c.merge(sp)
-                e[2].record(stream)
-                pairs_p.append((e[0], e[1], view))
-                pairs_m.append((e[1], e[2], view))
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                c(sp)
+                e1.record(stream)
+                pairs.append((e0, e1, view))
     torch.cuda.synchronize()
-    part = {"diff": [], "verify": []}
-    for a, b, v in pairs_p:
-        part[v].append(a.elapsed_time(b) * 1e3)
-    merge = [a.elapsed_time(b) * 1e3 for a, b, _ in pairs_m]
-    allp = part["diff"] + part["verify"]
-    return {"partial_us": statistics.mean(allp), "partial_diff_us": statistics.mean(part["diff"]),
-            "partial_verify_us": statistics.mean(part["verify"]), "merge_us": statistics.mean(merge)}
+    per = {"diff": [], "verify": []}
+    for a, b, v in pairs:
+        per[v].append(a.elapsed_time(b) * 1e3)
+    allk = per["diff"] + per["verify"]
+    return {"attn_us": statistics.mean(allk), "attn_diff_us": statistics.mean(per["diff"]),
+            "attn_verify_us": statistics.mean(per["verify"]), "attn_min_us": min(allk),
+            "attn_max_us": max(allk)}
 
 
-def cpu_baseline(w, caches, device):
-    """The oracle, untuned, on the host cores: one layer of the step (diffusion
-    and verify view) plus the greedy consensus, scaled to TB/s of the same
-    algorithmic bytes."""
+def cpu_baseline(w, caches, device, budget_s: float = 10.0):
+    """The oracle, untuned, on the host cores, over a bounded sample of the same
+    workload: whole layers of the step (diffusion + verify view, all heads) until
+    about `budget_s` seconds have passed, plus one greedy consensus; reported in
+    TB/s of the same algorithmic bytes."""
     from threadpoolctl import threadpool_info
 
     import oracle
     from synth import cache_lengths, greedy_inputs, view_inputs
 
-    kc, vc = caches[0]
-    kc_h, vc_h = kc.cpu(), vc.cpu()
     lens = cache_lengths(w, "cpu")
     t0 = time.perf_counter()
-    for view, mode in (("diff", oracle.MASK_DIFF_BIDIR), ("verify", oracle.MASK_VERIFY_CAUSAL)):
-        q, kb, vb = (t.cpu() for t in view_inputs(w, 0, view, device))
-        oracle.block_attention(q, kb, vb, kc_h, vc_h, lens, mode)
     logits, cand, _ = greedy_inputs(w)
     oracle.greedy_consensus(logits, cand)
+    nbytes = greedy_bytes(w)
+    layers = 0
+    for layer, (kc, vc) in enumerate(caches):
+        kc_h, vc_h = kc.cpu(), vc.cpu()
+        for view, mode in (("diff", oracle.MASK_DIFF_BIDIR), ("verify", oracle.MASK_VERIFY_CAUSAL)):
+            q, kb, vb = (t.cpu() for t in view_inputs(w, layer, view, device))
+            oracle.block_attention(q, kb, vb, kc_h, vc_h, lens, mode)
+            nbytes += attn_bytes(w)
+        layers += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
-    nbytes = 2 * attn_bytes(w) + greedy_bytes(w)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": nbytes / dt / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layer 0 of {w.layers} (diffusion + verify view, all heads) + greedy consensus, "
-                      f"L={w.cache_len}, K={w.block_k}: {dt:.2f} s on {os.cpu_count()} visible host CPUs",
-            "seconds": dt}
+            "sample": f"{layers} of {w.layers} layers (diffusion + verify view, all heads) + one greedy "
+                      f"consensus, L={w.cache_len}, K={w.block_k}: {dt:.2f} s on {os.cpu_count()} "
+                      "visible host CPUs",
+            "seconds": round(dt, 3), "step_seconds_extrapolated": round(dt / nbytes * (
+                2 * w.layers * attn_bytes(w) + greedy_bytes(w)), 2)}
 
 
 def main():
@@ -233,8 +233,8 @@ def main():
     step = Step(w, caches, device)
     ms, wall_ms = time_steps(step, args.steps, args.warmup, args.graph)
     kern = time_kernels(step)
-    print(f"[bench] step {ms * 1e3:.1f} us (host wall {wall_ms * 1e3:.1f} us), partial kernel "
-          f"{kern['partial_us']:.2f} us, merge {kern['merge_us']:.2f} us", file=sys.stderr, flush=True)
+    print(f"[bench] step {ms * 1e3:.1f} us (host wall {wall_ms * 1e3:.1f} us), attention kernel "
+          f"{kern['attn_us']:.2f} us", file=sys.stderr, flush=True)
     acc = step.acc.cpu().tolist()
 
     sweep = {}
@@ -252,8 +252,8 @@ def main():
 
     step_bytes = 2 * w.layers * attn_bytes(w) + greedy_bytes(w)
     value = step_bytes / (ms * 1e-3) / 1e12
-    pbytes = partial_bytes(w)
-    achieved = pbytes / (kern["partial_us"] * 1e-6) / 1e9
+    pbytes = attn_bytes(w)
+    achieved = pbytes / (kern["attn_us"] * 1e-6) / 1e9
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
         traffic = json.load(open(args.traffic)).get("bytes_per_launch")
@@ -284,7 +284,7 @@ def main():
         "k32_over_k1": round(sweep[32] / sweep[1], 4) if 32 in sweep and 1 in sweep else None,
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
         "accept_len": acc,
-        "roofline": {"bound": "hbm", "kernel": "attn_split_kernel (orthrus_block_attn_partial)",
+        "roofline": {"bound": "hbm", "kernel": "attn_stream_kernel (one launch per orthrus_block_attn_* call)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": pbytes},

@@ -5,6 +5,7 @@
 #include "common.h"
 
 #include <math.h>
+#include <atomic>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -49,18 +50,35 @@ AttnPlan make_plan(const orthrus_attn_desc* d) {
   p.rows_per_wg = 32 * p.qblocks;
   p.row_groups = (p.rows + p.rows_per_wg - 1) / p.rows_per_wg;
   const long long groups = (long long)d->batch * d->n_kv_heads * p.row_groups;
-  long long s = (kTargetAttnGroups + groups - 1) / groups;
+  long long s = kPlanCUs / groups;
   const long long max_tiles = (d->max_len + kTileKeys - 1) / kTileKeys;
   if (s > max_tiles) s = max_tiles;
   if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
-  p.splits = env_int("ORTHRUS_SPLITS", (int)s);
-  if (p.splits > kMaxSplits) p.splits = kMaxSplits;
+  p.splits = (int)s;
   const size_t slots = (size_t)groups * p.splits * p.rows_per_wg;
-  p.acc_bytes = round_up(slots * d->head_dim * sizeof(float), kAlign);
+  p.counter_bytes = round_up((size_t)groups * 32 * sizeof(uint32_t), kAlign);  // one 128-byte line per group
   p.ml_bytes = round_up(slots * 2 * sizeof(float), kAlign);
-  p.ws_bytes = p.acc_bytes + p.ml_bytes;
+  p.acc_bytes = round_up(slots * d->head_dim * sizeof(uint16_t), kAlign);
+  p.ws_bytes = p.counter_bytes + p.ml_bytes + p.acc_bytes;
   return p;
+}
+
+// Compute units of the current device, cached per device ordinal (a benign,
+// idempotent cache: every thread that fills a slot writes the same value).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return -1;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 // phases: 1 = partial (stream cache + block), 2 = merge, 3 = both
@@ -82,6 +100,8 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   if ((phases & 2) && (!aligned16(out) || (lse && !aligned4(lse)))) return ORTHRUS_ERR_MISALIGNED;
   const AttnPlan plan = make_plan(d);
   if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+  const int cus = device_cus();
+  if (cus < 1) return ORTHRUS_ERR_HIP;
 
   AttnArgs a{};
   a.q = q;
@@ -92,8 +112,10 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.cache_len = cache_len;
   a.out = out;
   a.lse = lse;
-  a.ws_acc = reinterpret_cast<float*>(workspace);
-  a.ws_ml = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + plan.acc_bytes);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  a.counters = reinterpret_cast<uint32_t*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + plan.counter_bytes);
+  a.ws_acc = reinterpret_cast<uint16_t*>(ws + plan.counter_bytes + plan.ml_bytes);
   a.batch = d->batch;
   a.n_q_heads = d->n_q_heads;
   a.n_kv_heads = d->n_kv_heads;
@@ -102,14 +124,19 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.head_dim = d->head_dim;
   a.max_len = d->max_len;
   a.causal = mode == ORTHRUS_MASK_VERIFY_CAUSAL ? 1 : 0;
+  a.splits = attn_launch_splits(plan, d->batch, d->n_kv_heads, d->max_len, cus);
+  const int cap = env_int("ORTHRUS_MAX_SPLITS", a.splits);  // tuning: may only lower the split count
+  if (cap < a.splits) a.splits = cap;
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   if ((phases & 1) && getenv("ORTHRUS_DEBUG") != nullptr)
     fprintf(stderr, "[orthrus] attn mode=%d B=%d Hq=%d Hkv=%d D=%d K=%d max_len=%d rows=%d qblocks=%d "
             "row_groups=%d splits=%d ws=%zu\n", mode, d->batch, d->n_q_heads, d->n_kv_heads,
             d->head_dim, d->block_k, d->max_len, plan.rows, plan.qblocks, plan.row_groups,
-            plan.splits, plan.ws_bytes);
-  const hipError_t e = launch_block_attention(a, plan, phases, reinterpret_cast<hipStream_t>(stream));
+            a.splits, plan.ws_bytes);
+  // tuning switch: merge the splits inside the streaming kernel (one launch)
+  const bool fused = env_int("ORTHRUS_FUSED_MERGE", 0) > 0;
+  const hipError_t e = launch_block_attention(a, plan, phases, fused, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 

@@ -10,19 +10,25 @@ namespace orthrus {
 // Keys per LDS tile.  Every (sequence, KV head) range of cache rows is cut
 // into `splits` contiguous chunks that are whole multiples of this.
 constexpr int kTileKeys = 64;
-// Work-groups one attention launch aims for: two per CU on a 256-CU MI355X.
-constexpr int kTargetAttnGroups = 512;
+// The streaming kernel runs one 512-thread work-group per CU; with more than
+// one split per (sequence, KV head) the launch never exceeds the device's CU
+// count, so every work-group of a split group is resident at once.
+constexpr int kAttnThreads = 512;
+// CU count the workspace is sized for (MI355X).  A device with fewer CUs runs
+// fewer splits inside the same workspace.
+constexpr int kPlanCUs = 256;
 constexpr int kMaxSplits = 64;
 
 struct AttnPlan {
-  int rows;         // R = G * K query rows per (sequence, KV head)
-  int qblocks;      // 32-row query blocks per work-group: 1, 2 or 4
-  int rows_per_wg;  // 32 * qblocks
-  int row_groups;   // ceil(R / rows_per_wg)
-  int splits;       // S cache chunks per (sequence, KV head, row group)
-  size_t acc_bytes; // fp32 partial outputs
-  size_t ml_bytes;  // fp32 (max, sum) pairs
-  size_t ws_bytes;  // total workspace
+  int rows;          // R = G * K query rows per (sequence, KV head)
+  int qblocks;       // 32-row query blocks per work-group: 1, 2 or 4
+  int rows_per_wg;   // 32 * qblocks
+  int row_groups;    // ceil(R / rows_per_wg)
+  int splits;        // most splits per (sequence, KV head, row group) the workspace holds
+  size_t counter_bytes;  // uint32 arrival/departure counters per split group
+  size_t ml_bytes;       // fp32 (max, sum) per row and split
+  size_t acc_bytes;      // bf16 normalised partial outputs per row and split
+  size_t ws_bytes;       // total workspace
 };
 
 struct AttnArgs {
@@ -34,15 +40,22 @@ struct AttnArgs {
   const int32_t* cache_len;
   uint16_t* out;
   float* lse;
-  float* ws_acc;
-  float* ws_ml;
+  uint32_t* counters;
+  float* ws_ml;       // fp32 (reference max, sum) per row and split
+  uint16_t* ws_acc;   // bf16 normalised partial output per row and split
   int batch, n_q_heads, n_kv_heads, group, block_k, head_dim, max_len;
   int causal;
+  int splits;        // splits of this launch (<= plan.splits)
   float scale_log2;  // softmax scale * log2(e)
 };
 
-// phases: 1 = stream the cache into split partials, 2 = merge the splits, 3 = both
-hipError_t launch_block_attention(const AttnArgs& a, const AttnPlan& plan, int phases,
+// Splits a launch uses on a device with `cus` compute units.
+int attn_launch_splits(const AttnPlan& plan, int batch, int n_kv_heads, int max_len, int cus);
+
+// phases: 1 = stream the cache into split partials, 2 = merge the splits,
+// 3 = the whole call (merge in a second kernel, or inside the streaming
+// kernel when `fused_merge`)
+hipError_t launch_block_attention(const AttnArgs& a, const AttnPlan& plan, int phases, bool fused_merge,
                                   hipStream_t stream);
 
 // ---------------------------------------------------------------- consensus

@@ -70,8 +70,9 @@ typedef struct {
  * so one buffer serves every decode step of a sequence batch. */
 size_t orthrus_attn_workspace_size(const orthrus_attn_desc* d);
 
-/* Number of cache splits one (sequence, KV head) is streamed in (diagnostic;
- * -1 if `d` is invalid).  Also fixed by the descriptor alone. */
+/* Largest number of cache splits one (sequence, KV head) is streamed in
+ * (diagnostic; -1 if `d` is invalid).  Fixed by the descriptor alone; a
+ * device with fewer than 256 compute units uses fewer. */
 int32_t orthrus_attn_num_splits(const orthrus_attn_desc* d);
 
 /* Dual-view block attention of one layer (paper notes §2.1, §3.2, §4.1).
@@ -94,7 +95,11 @@ int32_t orthrus_attn_num_splits(const orthrus_attn_desc* d);
  *   out      bf16 [B, Hq, K, D]  (written)
  *   lse      fp32 [B, Hq, K]     natural-log LSE (written; may be NULL)
  *   workspace  device scratch of at least orthrus_attn_workspace_size(d)
- *              bytes; contents need no initialisation and are clobbered.
+ *              bytes.  It must be zero-filled once before its first use
+ *              (e.g. hipMemsetAsync); every call leaves it ready for the next
+ *              one (its split-group counters back at zero), whatever the
+ *              descriptor.  Calls that share a workspace must not overlap in
+ *              time (use one workspace per stream).
  * Neither k_blk/v_blk nor anything else is ever written into the cache. */
 orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, orthrus_mask_mode mode,
                                   const uint16_t* q, const uint16_t* k_blk,

@@ -194,10 +194,40 @@ def test_workspace_is_independent_of_cached_length():
     w = Workload("ws", 1, 1, 32, 8, 128, 4096, 32, 10, 1.0, 12)
     x = _inputs(w)
     desc = dvb.attn_desc(x["q"], x["k_cache"])
-    ws = torch.empty(dvb.orthrus_attn_workspace_size(desc), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(dvb.orthrus_attn_workspace_size(desc), dtype=torch.uint8, device=DEV)
     for L in (4096, 100, 2500):
         x["cache_len"].fill_(L)
         shared, _ = _run(x, "diff", workspace=ws)
         shared = shared.clone()
         fresh, _ = _run(x, "diff")
         assert torch.equal(shared, fresh)
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_merge_variants_agree_bitwise(mode, monkeypatch):
+    """The split merge as a second kernel, inside the streaming kernel, and
+    through the partial/merge entry points gives identical bits."""
+    w = WORKLOADS["qwen3_8b_8k"]
+    x = _inputs(w)
+    monkeypatch.setenv("ORTHRUS_FUSED_MERGE", "0")
+    two, two_lse = (t.clone() for t in _run(x, mode))
+    monkeypatch.setenv("ORTHRUS_FUSED_MERGE", "1")
+    fused, fused_lse = (t.clone() for t in _run(x, mode))
+    monkeypatch.setenv("ORTHRUS_FUSED_MERGE", "0")
+    desc = dvb.attn_desc(x["q"], x["k_cache"])
+    ws = torch.zeros(dvb.orthrus_attn_workspace_size(desc), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=DEV)
+    m = dvb.ORTHRUS_MASK_DIFF_BIDIR if mode == "diff" else dvb.ORTHRUS_MASK_VERIFY_CAUSAL
+    call = dvb.PreparedAttention(m, x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"],
+                                 x["cache_len"], out, lse, ws)
+    s = torch.cuda.current_stream().cuda_stream
+    call.partial(s)
+    call.merge(s)
+    torch.cuda.synchronize()
+    assert torch.equal(two, fused) and torch.equal(two_lse, fused_lse)
+    assert torch.equal(two, out) and torch.equal(two_lse, lse)
+    # the fused path leaves its counters at zero: a second fused call agrees too
+    monkeypatch.setenv("ORTHRUS_FUSED_MERGE", "1")
+    again, _ = _run(x, mode)
+    assert torch.equal(again, fused)
