@@ -83,7 +83,7 @@ class Step:
                              device=device)
         ws_bytes = dvb.orthrus_attn_workspace_size(dvb.attn_desc(desc_q, caches[0][0]))
         self.splits = dvb.orthrus_attn_num_splits(dvb.attn_desc(desc_q, caches[0][0]))
-        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=device)  # counters start at zero
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
         for view, mode in (("diff", dvb.ORTHRUS_MASK_DIFF_BIDIR), ("verify", dvb.ORTHRUS_MASK_VERIFY_CAUSAL)):
             for layer, (kc, vc) in enumerate(caches):
                 q, kb, vb = view_inputs(w, layer, view, device)
@@ -142,9 +142,9 @@ def time_steps(step, steps: int, warmup: int, graph: bool):
 
 
 def time_kernels(step, reps: int = 2):
-    """Average device duration of one block-attention launch (the fused
-    streaming + merge kernel), from HIP events recorded around each launch on
-    the launch stream, for the diffusion and the verify view."""
+    """Average device duration of one block-attention call (streaming kernel
+    plus merge kernel), from HIP events recorded around each call on the
+    launch stream, for the diffusion and the verify view."""
     import torch
 
     stream = torch.cuda.current_stream()

@@ -79,8 +79,8 @@ def orthrus_consensus_workspace_size(batch: int, block_k: int, vocab: int) -> in
 
 
 def _workspace(nbytes: int, device, workspace):
-    if workspace is None:  # zero-filled: the attention calls keep counters in it
-        return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if workspace is None:  # scratch only: no initialisation needed
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
     _need(workspace, "workspace", torch.uint8, device=device)
     return workspace
 

@@ -57,10 +57,9 @@ AttnPlan make_plan(const orthrus_attn_desc* d) {
   if (s < 1) s = 1;
   p.splits = (int)s;
   const size_t slots = (size_t)groups * p.splits * p.rows_per_wg;
-  p.counter_bytes = round_up((size_t)groups * 32 * sizeof(uint32_t), kAlign);  // one 128-byte line per group
   p.ml_bytes = round_up(slots * 2 * sizeof(float), kAlign);
   p.acc_bytes = round_up(slots * d->head_dim * sizeof(uint16_t), kAlign);
-  p.ws_bytes = p.counter_bytes + p.ml_bytes + p.acc_bytes;
+  p.ws_bytes = p.ml_bytes + p.acc_bytes;
   return p;
 }
 
@@ -113,9 +112,8 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.out = out;
   a.lse = lse;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  a.counters = reinterpret_cast<uint32_t*>(ws);
-  a.ws_ml = reinterpret_cast<float*>(ws + plan.counter_bytes);
-  a.ws_acc = reinterpret_cast<uint16_t*>(ws + plan.counter_bytes + plan.ml_bytes);
+  a.ws_ml = reinterpret_cast<float*>(ws);
+  a.ws_acc = reinterpret_cast<uint16_t*>(ws + plan.ml_bytes);
   a.batch = d->batch;
   a.n_q_heads = d->n_q_heads;
   a.n_kv_heads = d->n_kv_heads;
@@ -135,8 +133,7 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
             d->head_dim, d->block_k, d->max_len, plan.rows, plan.qblocks, plan.row_groups,
             a.splits, plan.ws_bytes);
   // tuning switch: merge the splits inside the streaming kernel (one launch)
-  const bool fused = env_int("ORTHRUS_FUSED_MERGE", 0) > 0;
-  const hipError_t e = launch_block_attention(a, plan, phases, fused, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = launch_block_attention(a, plan, phases, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 

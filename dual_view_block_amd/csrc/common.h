@@ -25,7 +25,6 @@ struct AttnPlan {
   int rows_per_wg;   // 32 * qblocks
   int row_groups;    // ceil(R / rows_per_wg)
   int splits;        // most splits per (sequence, KV head, row group) the workspace holds
-  size_t counter_bytes;  // uint32 arrival/departure counters per split group
   size_t ml_bytes;       // fp32 (max, sum) per row and split
   size_t acc_bytes;      // bf16 normalised partial outputs per row and split
   size_t ws_bytes;       // total workspace
@@ -40,7 +39,6 @@ struct AttnArgs {
   const int32_t* cache_len;
   uint16_t* out;
   float* lse;
-  uint32_t* counters;
   float* ws_ml;       // fp32 (reference max, sum) per row and split
   uint16_t* ws_acc;   // bf16 normalised partial output per row and split
   int batch, n_q_heads, n_kv_heads, group, block_k, head_dim, max_len;
@@ -53,10 +51,9 @@ struct AttnArgs {
 int attn_launch_splits(const AttnPlan& plan, int batch, int n_kv_heads, int max_len, int cus);
 
 // phases: 1 = stream the cache into split partials, 2 = merge the splits,
-// 3 = the whole call (merge in a second kernel, or inside the streaming
-// kernel when `fused_merge`)
-hipError_t launch_block_attention(const AttnArgs& a, const AttnPlan& plan, int phases, bool fused_merge,
-                                  hipStream_t stream);
+// 3 = the whole call (a single split writes the output directly; otherwise
+// the merge runs as a second kernel on the same stream)
+hipError_t launch_block_attention(const AttnArgs& a, const AttnPlan& plan, int phases, hipStream_t stream);
 
 // ---------------------------------------------------------------- consensus
 struct ConsensusPlan {

@@ -95,11 +95,10 @@ int32_t orthrus_attn_num_splits(const orthrus_attn_desc* d);
  *   out      bf16 [B, Hq, K, D]  (written)
  *   lse      fp32 [B, Hq, K]     natural-log LSE (written; may be NULL)
  *   workspace  device scratch of at least orthrus_attn_workspace_size(d)
- *              bytes.  It must be zero-filled once before its first use
- *              (e.g. hipMemsetAsync); every call leaves it ready for the next
- *              one (its split-group counters back at zero), whatever the
- *              descriptor.  Calls that share a workspace must not overlap in
- *              time (use one workspace per stream).
+ *              bytes, owned by the caller; no initialisation is needed (each
+ *              call writes every byte it later reads).  Calls that share a
+ *              workspace must not overlap in time (use one workspace per
+ *              stream).
  * Neither k_blk/v_blk nor anything else is ever written into the cache. */
 orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, orthrus_mask_mode mode,
                                   const uint16_t* q, const uint16_t* k_blk,
@@ -129,8 +128,8 @@ orthrus_status orthrus_block_attn_verify(const orthrus_attn_desc* d, const uint1
 /* The two halves of orthrus_block_attn, for callers that schedule or time
  * them separately (or, later, combine partials from several cache shards).
  * orthrus_block_attn_partial streams the cache and the block and leaves one
- * unnormalised partial softmax state (running max, running sum, weighted
- * value sum) per query row and cache split in `workspace`;
+ * partial softmax state per query row and cache split in `workspace` (fp32
+ * reference max and sum, and the bf16 value sum normalised by that sum);
  * orthrus_block_attn_merge combines the splits into `out` and `lse` exactly as
  * orthrus_block_attn does (the pair gives bit-identical results).  Both calls
  * must get the same descriptor and workspace, in this order on one stream;

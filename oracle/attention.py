@@ -16,7 +16,7 @@ Sources (the Orthrus pages):
 * hotdry.top blog post on Orthrus dual-view diffusion decoding, sections on
   the dual-view attention architecture and on the training mask (same facts).
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
 
 * R1 -- the cache given holds every position strictly before the anchor
   (``cache_len[b]`` positions); the anchor itself is block row 0.

@@ -15,7 +15,7 @@ Sources (the Orthrus pages):
 * hotdry.top blog post on Orthrus, section on parallel block projection and
   in-model consensus (same facts).
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
 
 * R2 -- logits row i is the AR distribution checked against cand[i].
 * R3 -- no bonus token when all K candidates match: accept_len = K and
