@@ -26,6 +26,11 @@ import time
 
 METRIC = "dual-view step µs and achieved HBM TB/s at Qwen3-8B shape, L=32K, K=32"
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_stream_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "dual_view_block_amd", "csrc", "attention.hip")
+STREAM_KERNEL = "attn_stream_kernel"
+COPY_KERNEL = "copyBuffer"  # the runtime's device-to-device copy kernel
 
 
 def _parse():
@@ -41,18 +46,84 @@ def _parse():
                     help="block sizes timed for the latency-vs-K line ('' to skip)")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with rocprofv3-derived HBM bytes per partial-kernel launch")
+    ap.add_argument("--traffic", default=TRAFFIC_JSON,
+                    help="JSON record of rocprofv3-derived HBM bytes per streaming-kernel launch "
+                         "(ignored if attention.hip changed since it was taken)")
+    ap.add_argument("--profile-target", choices=["attn-stream", "copy"], default=None,
+                    help="run only the streaming kernel over every layer-view (or a plain copy "
+                         "kernel of --copy-mib MiB) --steps times, for rocprofv3 counter runs")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--make-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                        "COPY_WRITE_CSV"),
+                    help="turn four rocprofv3 --pmc counter_collection.csv files into the traffic "
+                         "record (written to --traffic) and exit")
     return ap.parse_args()
 
 
 def attn_bytes(w) -> int:
     """Algorithmic bytes of one layer-view: cache K+V rows [0, L), q, k/v block, out."""
+    return stream_bytes(w) + w.batch * w.n_q_heads * w.block_k * w.head_dim * 2  # out has q's shape
+
+
+def stream_bytes(w) -> int:
+    """Algorithmic bytes the streaming kernel reads: cache K+V rows [0, L), q, k/v block."""
     bf = 2
     cache = 2 * w.batch * w.n_kv_heads * w.cache_len * w.head_dim * bf
     q = w.batch * w.n_q_heads * w.block_k * w.head_dim * bf
     blk = 2 * w.batch * w.n_kv_heads * w.block_k * w.head_dim * bf
-    return cache + q + blk + q  # out has q's shape
+    return cache + q + blk
+
+
+def _sha256(path: str) -> str:
+    import hashlib
+
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _counter_kib(csv_path: str, kernel: str, counter: str) -> float:
+    """Mean per-dispatch value of `counter` over the dispatches of `kernel`."""
+    import csv
+
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel} in {csv_path}")
+    return sum(vals) / len(vals)
+
+
+def make_traffic(paths, out_path: str, copy_mib: int) -> None:
+    """HBM bytes per streaming launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) each scaled by what the same counter reads for a plain copy
+    kernel of known size (copy_mib MiB read, copy_mib MiB written)."""
+    f_csv, w_csv, cf_csv, cw_csv = paths
+    fetch = _counter_kib(f_csv, STREAM_KERNEL, "FETCH_SIZE")
+    write = _counter_kib(w_csv, STREAM_KERNEL, "WRITE_SIZE")
+    cfetch = _counter_kib(cf_csv, COPY_KERNEL, "FETCH_SIZE")
+    cwrite = _counter_kib(cw_csv, COPY_KERNEL, "WRITE_SIZE")
+    nbytes = copy_mib * 2**20
+    rf, rw = nbytes / cfetch, nbytes / cwrite  # true bytes per counted KiB
+    rec = {"kernel": STREAM_KERNEL, "source_sha256": _sha256(ATTN_SOURCE),
+           "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
+           "copy_bytes_each_way": nbytes, "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
+           "fetch_bytes_per_kib": rf, "write_bytes_per_kib": rw,
+           "read_bytes_per_launch": round(fetch * rf), "write_bytes_per_launch": round(write * rw),
+           "bytes_per_launch": round(fetch * rf + write * rw)}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
+def load_traffic(path: str):
+    """bytes_per_launch of the traffic record, or None if absent or stale."""
+    if not path or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != _sha256(ATTN_SOURCE):
+        print("[bench] traffic record predates the current attention.hip: reporting null",
+              file=sys.stderr, flush=True)
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def greedy_bytes(w) -> int:
@@ -141,31 +212,52 @@ def time_steps(step, steps: int, warmup: int, graph: bool):
     return t0.elapsed_time(t1) / steps, wall / steps * 1e3
 
 
-def time_kernels(step, reps: int = 2):
-    """Average device duration of one block-attention call (streaming kernel
-    plus merge kernel), from HIP events recorded around each call on the
-    launch stream, for the diffusion and the verify view."""
+def time_kernels(step, reps: int = 3):
+    """Average device duration per launch, from HIP events on the launch stream
+    around a run of back-to-back launches over every layer of both views: the
+    streaming kernel alone (orthrus_block_attn_partial), the merge kernel alone
+    (orthrus_block_attn_merge) and the whole call (orthrus_block_attn_*).  The
+    median over `reps` runs is reported."""
     import torch
 
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    pairs = []
-    for _ in range(reps):
-        for view in ("diff", "verify"):
-            for c in step.calls[view]:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                c(sp)
-                e1.record(stream)
-                pairs.append((e0, e1, view))
+    calls = step.calls["diff"] + step.calls["verify"]
+    out = {}
+    for what in ("stream", "merge", "call"):
+        per = []
+        for _ in range(reps):
+            fns = [c.partial if what == "stream" else (c.merge if what == "merge" else c.__call__) for c in calls]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for fn in fns:
+                fn(sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / len(fns))
+        out[f"attn_{what}_us"] = statistics.median(per)
+    out["launches_per_run"] = len(calls)
+    return out
+
+
+def profile_target(args, w, caches, device) -> None:
+    """Only the kernel under study, for rocprofv3 counter runs (no timing)."""
+    import torch
+
+    if args.profile_target == "copy":
+        src = torch.ones(args.copy_mib * 2**20, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)  # device-to-device: one copy kernel, reads and writes copy_mib MiB
+    else:
+        step = Step(w, caches, device)
+        sp = torch.cuda.current_stream().cuda_stream
+        for _ in range(args.steps):
+            for view in ("diff", "verify"):
+                for c in step.calls[view]:
+                    c.partial(sp)
     torch.cuda.synchronize()
-    per = {"diff": [], "verify": []}
-    for a, b, v in pairs:
-        per[v].append(a.elapsed_time(b) * 1e3)
-    allk = per["diff"] + per["verify"]
-    return {"attn_us": statistics.mean(allk), "attn_diff_us": statistics.mean(per["diff"]),
-            "attn_verify_us": statistics.mean(per["verify"]), "attn_min_us": min(allk),
-            "attn_max_us": max(allk)}
+    print(f"[bench] profile target {args.profile_target} done", file=sys.stderr, flush=True)
 
 
 def cpu_baseline(w, caches, device, budget_s: float = 10.0):
@@ -205,6 +297,9 @@ def cpu_baseline(w, caches, device, budget_s: float = 10.0):
 
 def main():
     args = _parse()
+    if args.make_traffic:
+        make_traffic(args.make_traffic, args.traffic, args.copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this decode step is "
               "not sharded across GPUs -- run with --gpus 1.", file=sys.stderr)
@@ -225,16 +320,23 @@ def main():
     if args.layers:
         w = w.replace(layers=args.layers)
     print(f"[bench] workload {w}", file=sys.stderr, flush=True)
+    if args.profile_target == "copy":
+        profile_target(args, w, None, device)
+        return
     caches = [layer_cache(w, layer, device) for layer in range(w.layers)]
     torch.cuda.synchronize()
     print(f"[bench] caches ready: {w.layers} layers x {2 * caches[0][0].numel() * 2 / 2**20:.0f} MiB",
           file=sys.stderr, flush=True)
 
+    if args.profile_target:
+        profile_target(args, w, caches, device)
+        return
     step = Step(w, caches, device)
     ms, wall_ms = time_steps(step, args.steps, args.warmup, args.graph)
     kern = time_kernels(step)
-    print(f"[bench] step {ms * 1e3:.1f} us (host wall {wall_ms * 1e3:.1f} us), attention kernel "
-          f"{kern['attn_us']:.2f} us", file=sys.stderr, flush=True)
+    print(f"[bench] step {ms * 1e3:.1f} us (host wall {wall_ms * 1e3:.1f} us), streaming kernel "
+          f"{kern['attn_stream_us']:.2f} us, merge {kern['attn_merge_us']:.2f} us, call "
+          f"{kern['attn_call_us']:.2f} us", file=sys.stderr, flush=True)
     acc = step.acc.cpu().tolist()
 
     sweep = {}
@@ -252,11 +354,9 @@ def main():
 
     step_bytes = 2 * w.layers * attn_bytes(w) + greedy_bytes(w)
     value = step_bytes / (ms * 1e-3) / 1e12
-    pbytes = attn_bytes(w)
-    achieved = pbytes / (kern["attn_us"] * 1e-6) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    pbytes = stream_bytes(w)
+    achieved = pbytes / (kern["attn_stream_us"] * 1e-6) / 1e9
+    traffic = load_traffic(args.traffic)
     flops = w.layers * (attn_flops(w, False) + attn_flops(w, True))
     line = {
         "metric": METRIC,
@@ -284,10 +384,11 @@ def main():
         "k32_over_k1": round(sweep[32] / sweep[1], 4) if 32 in sweep and 1 in sweep else None,
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
         "accept_len": acc,
-        "roofline": {"bound": "hbm", "kernel": "attn_stream_kernel (one launch per orthrus_block_attn_* call)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": pbytes},
+                     "kernel": "attn_stream_kernel<128,4> (one launch per orthrus_block_attn_* call)",
+                     "algorithmic_bytes_per_launch": pbytes,
+                     "call_achieved_gbs": round(attn_bytes(w) / (kern["attn_call_us"] * 1e-6) / 1e9, 1)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, caches, device)

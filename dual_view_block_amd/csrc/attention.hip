@@ -1,6 +1,5 @@
 // Dual-view block attention for gfx950 (MI355X): split-L cache streaming with
-// bf16 MFMA, online softmax in fp32, and a cross-split log-sum-exp merge that
-// runs inside the same launch.
+// bf16 MFMA, online softmax in fp32, and a cross-split log-sum-exp merge.
 //
 // What is computed (Orthrus paper notes, zhangshuibai.github.io, §2.1, §3.2,
 // §4.1): for every (sequence b, KV head g), the G*K query rows of the q heads
@@ -12,11 +11,12 @@
 // waves (512 threads) per CU.  A work-group owns one contiguous chunk of the
 // (b, g) cache rows and up to 128 query rows (4 blocks of 32); the last split
 // also takes the K block keys as one extra masked tile.
-//  * Streaming: the chunk is read in tiles of 64 keys.  Each thread keeps the
-//    next three tiles' 128-bit loads in flight in registers (the compiler
-//    tracks each with its own vmcnt) and writes the oldest into one of two
-//    LDS stages per tile, with the 16-byte chunks of row r XOR-swizzled by
-//    2*(r mod 8) so that both read patterns below are conflict-free.
+//  * Streaming: the chunk is read in tiles of 64 keys straight into a 5-stage
+//    LDS ring with global_load_lds (16 bytes per lane, no register staging);
+//    four tiles are in flight while one is computed.  The 16-byte chunks of
+//    every K and V row are XOR-permuted per row so that both read patterns
+//    below hit distinct LDS banks.  q is staged through the last ring stage
+//    before the first tile needs it.
 //  * Compute: wave w takes query block w%4 against key half w/4 of every
 //    tile.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 query rows;
 //    Q held in registers), so each lane owns one query row and its softmax
@@ -24,14 +24,17 @@
 //    MFMA: P^T is the S^T accumulator converted to bf16 in place; V^T comes
 //    from the row-major V tile through ds_read_b64_tr_b16, the transposing LDS
 //    read, with the key order matched to the accumulator's register order.
+//    The loop is software-pipelined: while the vector ALU exponentiates S(t),
+//    the same wave's matrix-core instructions compute S(t+1).
+//  * Softmax: P = 2^(s*scale*log2(e) - m_ref) with a lazily raised reference
+//    m_ref (raised only when a score exceeds it by more than 2^8), so the
+//    accumulator rescale is rare; the sum cancels the reference exactly.
 //  * The two key halves of a query block are combined through LDS.  With one
-//    split the work-group normalises and writes the rows itself.  Otherwise
-//    it stores an unnormalised partial (max, sum, weighted value sum) per row,
-//    counts itself in at the split group's arrival counter, waits (bounded)
-//    until all S splits have arrived, and merges its share of the group's
-//    rows: out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s,
-//    lse = (M + log2 sum) * ln 2.  The last work-group to leave resets the
-//    counters, so the workspace is ready for the next call.
+//    split the work-group normalises and writes the rows itself.  Otherwise it
+//    stores a partial per row -- fp32 (m_ref, sum) and the bf16 value sum
+//    normalised by that sum -- and a second kernel merges the S partials:
+//    out = sum_s 2^(m_s-M) l_s o_s / sum_s 2^(m_s-M) l_s,
+//    lse = (M + log2 sum_s 2^(m_s-M) l_s) * ln 2, with one wave per row.
 #include "common.h"
 
 #include <math.h>
