@@ -51,7 +51,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // plain vector: st
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = kAttnThreads;
-constexpr int kStages = 5;  // LDS ring stages (kStages - 1 tiles in flight; q uses the last one first)
+constexpr int kStages = 4;  // LDS ring stages: tiles t-1 .. t+2
 constexpr float kLazy = 8.0f;  // base-2 headroom before the softmax reference is raised
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994531f;
@@ -82,65 +82,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // lane `src`'s value of x, for the whole wave (the builtin moves 32-bit ints)
 __device__ __forceinline__ float readlane_f(float x, int src) {
   return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), src));
-}
-
-// 16-byte global -> LDS copies (global_load_lds_dwordx4, scalar-base form):
-// for each copy, lane l of the wave writes LDS bytes [lds + 16 l, lds + 16 l
-// + 16) from global address base + off_l, with `base` uniform across the wave
-// (an SGPR pair) and `off_l` a 32-bit per-lane byte offset.  The LDS address
-// goes through M0 and must be the same for the whole wave; M0 is saved and
-// restored around the batch (the compiler does not otherwise use M0 in these
-// kernels).  The copies are invisible to the compiler's wait-count tracking:
-// callers wait for them with wait_vmcnt() before reading the LDS they fill.
-__device__ __forceinline__ uint32_t uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ __forceinline__ void dma16x2(const void* b0, uint32_t o0, uint32_t l0, const void* b1, uint32_t o1,
-                                        uint32_t l1) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %5\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %6\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %4\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(o0), "s"(b0), "v"(o1), "s"(b1), "s"(uniform(l0)), "s"(uniform(l1))
-      : "memory");
-}
-
-__device__ __forceinline__ void dma16x4(const void* b0, uint32_t o0, uint32_t l0, const void* b1, uint32_t o1,
-                                        uint32_t l1, uint32_t o2, uint32_t l2, uint32_t o3, uint32_t l3) {
-  // copies 0 and 2 read from b0, copies 1 and 3 from b1
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %7\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %8\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, %4\n\t"
-      "s_mov_b32 m0, %9\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %5, %2\n\t"
-      "s_mov_b32 m0, %10\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %6, %4\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(o0), "s"(b0), "v"(o1), "s"(b1), "v"(o2), "v"(o3), "s"(uniform(l0)), "s"(uniform(l1)),
-        "s"(uniform(l2)), "s"(uniform(l3))
-      : "memory");
-}
-
-// s_waitcnt vmcnt(N) (N < 64), leaving the other counters unconstrained.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
@@ -254,23 +195,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   constexpr int DCH = D / 8;               // 16-byte chunks per row
   constexpr int ROWB = D * 2;              // bytes per row
   constexpr int TILEB = kTileKeys * ROWB;  // bytes of one K or V tile
+  constexpr int STAGEB = 2 * TILEB;        // one ring stage: a K tile and a V tile
+  constexpr int HALFB = 32 * ROWB;         // offset of a tile's second 32-key half
   constexpr int NDS = D / 16;              // MFMA steps over head_dim for S^T
   constexpr int NMB = D / 32;              // 32-wide head_dim blocks of O^T
   constexpr int NWAVES = kThreads / 64;
-  constexpr int CPT = kTileKeys * DCH / kThreads;     // 16-byte copies per thread per array per tile
-  constexpr int RED_FLOATS = NMB * 16 * 64 + 2 * 64;  // one donor wave's state
-  constexpr int STAGEB = 2 * TILEB;                    // one ring stage: a K tile and a V tile
-  constexpr int SMEM = kStages * STAGEB;
-  constexpr int RED_BYTES = 4 * RED_FLOATS * 4;
-  constexpr int QROWS = 32 * NQB;                      // query rows of the work-group block
-  constexpr int QCH_BLOCKS = QROWS * DCH / 64;         // 64-chunk blocks of q
-  constexpr int QSTAGE = kStages - 1;                  // q is staged where tile kStages-1 goes
-  static_assert(NWAVES == 8, "eight waves: four query blocks x two key halves");
-  static_assert(RED_BYTES <= SMEM, "the key-half exchange reuses the ring");
-  static_assert(QROWS * ROWB <= STAGEB, "q fits one ring stage");
+  constexpr int CPT = kTileKeys * DCH / kThreads;  // 16-byte chunks per thread per array per tile
+  static_assert(NWAVES == 4, "four waves, one 32-row query block each");
   static_assert(CPT >= 1, "tile too small for the work-group");
+  static_assert(4 * NMB == 2 * NDS, "two PV MFMAs per S step");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGEB];
 
   const int split = blockIdx.x;
   const int rg = blockIdx.y;
@@ -279,10 +214,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   const int b = bg / a.n_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb = __builtin_amdgcn_readfirstlane(tid >> 6);  // this wave's query block
   const int half = lane >> 5;
-  const int qb = wave & 3;   // query block of this wave
-  const int kh = wave >> 2;  // which 32-key half of every tile this wave takes
   const bool active = qb < NQB;
   const int R = plan.rows;
   const int K = a.block_k;
@@ -293,62 +226,55 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   const int wrow = qb * 32 + (lane & 31);         // row inside the work-group block
   const int qrow = rg * plan.rows_per_wg + wrow;  // row inside the (b, g) group
   const int qrow_i = qrow % K;                    // its block position (row = head_in_group*K + i)
-  // q rows of the block go to ring stage QSTAGE with the same copies and
-  // swizzle as the K tiles; every wave reads its fragments from there after
-  // the first tile's barrier, before the stage is handed to tile QSTAGE.  Rows
-  // past R re-read row R-1 (their outputs are never written).
-  const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
-  const uint32_t q_lds = lds_base + QSTAGE * STAGEB;
-  for (int cb = wave; cb < QCH_BLOCKS; cb += 2 * NWAVES) {
-    // two copies per batch; a wave's second block may lie past the end, then
-    // it repeats the first (same data to the same place)
-    const int cb2 = cb + NWAVES < QCH_BLOCKS ? cb + NWAVES : cb;
-    const int n1 = cb * 64 + lane, n2 = cb2 * 64 + lane;
-    const int row1 = n1 / DCH, row2 = n2 / DCH;
-    const int src1 = min(rg * plan.rows_per_wg + row1, R - 1);
-    const int src2 = min(rg * plan.rows_per_wg + row2, R - 1);
-    const uint16_t* qbase = a.q + row_base * D;
-    dma16x2(qbase, (uint32_t)(src1 * ROWB + swz_k<DCH>(row1, n1 % DCH) * 16), q_lds + cb * 1024, qbase,
-            (uint32_t)(src2 * ROWB + swz_k<DCH>(row2, n2 % DCH) * 16), q_lds + cb2 * 1024);
-  }
-  bf16x8 qf[NDS];
 
-  // ---- tile t -> LDS stage t % kStages by direct-to-LDS copies.  Wave w
-  // fills 64-chunk blocks w, w + 8, ... of the K tile and of the V tile in the
-  // swizzled layout: LDS chunk n = row * DCH + pc holds the row's logical
-  // chunk pc ^ swizzle(row).  Rows past the valid count re-read the last valid
-  // row (finite data; their scores are masked to -inf, so P = 0 exactly).
-  // Tiles past the end copy the first block-key row (one 256-byte row: no
-  // HBM traffic to speak of) into a stage nobody reads any more, so every wave
-  // always has the same number of copies in flight and the waits are constants.
-  int src_row[CPT];
-  uint32_t src_ck[CPT], src_cv[CPT];
+  // ---- tile copies: thread tid moves 16-byte chunks n = tid + c*kThreads of
+  // the K tile and of the V tile (row n / DCH, chunk n % DCH, so consecutive
+  // lanes read consecutive 16 bytes of the head-major cache) with
+  // nontemporal loads into registers, two tiles ahead, and later writes them
+  // into the LDS ring at the row's permuted chunk position.  Rows past the
+  // valid count re-read the last valid row (finite data; their scores are
+  // masked to -inf, so P = 0 exactly).  Tiles past the end re-read the first
+  // block-key row (no HBM traffic to speak of) into a stage nobody reads.
+  int crow[CPT];
+  uint32_t cchunk[CPT], dk[CPT], dv[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int n = (wave + NWAVES * c) * 64 + lane;
-    src_row[c] = n / DCH;
-    src_ck[c] = swz_k<DCH>(src_row[c], n % DCH);  // logical chunk stored at this slot of the K tile
-    src_cv[c] = swz_v<DCH>(src_row[c], n % DCH);  // ... of the V tile
+    const int n = tid + c * kThreads;
+    crow[c] = n / DCH;
+    cchunk[c] = (uint32_t)(n % DCH) * 16;
+    dk[c] = (uint32_t)(crow[c] * ROWB + swz_k<DCH>(crow[c], n % DCH) * 16);
+    dv[c] = (uint32_t)(TILEB + crow[c] * ROWB + swz_v<DCH>(crow[c], n % DCH) * 16);
   }
-  auto issue_tile = [&](int t) __attribute__((always_inline)) {
+  // tiles [0, nfull) are whole cache tiles: no masking, no row clamping
+  const int nfull = min((sr.kend - sr.kstart) / kTileKeys, sr.ncache);
+  const size_t split_off = ((size_t)bg * a.max_len + sr.kstart) * D;
+  const uint8_t* kc0 = reinterpret_cast<const uint8_t*>(a.k_cache + split_off);  // tile 0 of this split
+  const uint8_t* vc0 = reinterpret_cast<const uint8_t*>(a.v_cache + split_off);
+  const uint8_t* kblk = reinterpret_cast<const uint8_t*>(a.k_blk + (size_t)bg * K * D);
+  const uint8_t* vblk = reinterpret_cast<const uint8_t*>(a.v_blk + (size_t)bg * K * D);
+  typedef u32x4 Stage[2 * CPT];  // K chunks, then V chunks
+  auto load_tile = [&](int t, Stage& r) __attribute__((always_inline)) {
+    const bool whole = t < nfull;
     const bool real = t < sr.ntiles;
     const bool blk = sr.has_block && t == sr.ncache;
-    const int r0 = sr.kstart + t * kTileKeys;
-    const size_t cache_off = ((size_t)bg * a.max_len + r0) * D;
-    const size_t blk_off = (size_t)bg * K * D;
-    const uint16_t* kp = !real ? a.k_blk : (blk ? a.k_blk + blk_off : a.k_cache + cache_off);
-    const uint16_t* vp = !real ? a.k_blk : (blk ? a.v_blk + blk_off : a.v_cache + cache_off);
-    const int last = (!real ? 1 : (blk ? K : min(kTileKeys, sr.kend - r0))) - 1;
-    const uint32_t stage = lds_base + (uint32_t)((t % kStages) * STAGEB);
-    const uint32_t rk0 = (uint32_t)(min(src_row[0], last) * ROWB);
-    if constexpr (CPT == 1) {
-      dma16x2(kp, rk0 + src_ck[0] * 16, stage + wave * 1024, vp, rk0 + src_cv[0] * 16, stage + TILEB + wave * 1024);
-    } else {
-      static_assert(CPT == 2, "copy batches are written for one or two blocks per wave");
-      const uint32_t rk1 = (uint32_t)(min(src_row[1], last) * ROWB);
-      dma16x4(kp, rk0 + src_ck[0] * 16, stage + wave * 1024, vp, rk0 + src_cv[0] * 16, stage + TILEB + wave * 1024,
-              rk1 + src_ck[1] * 16, stage + (wave + NWAVES) * 1024, rk1 + src_cv[1] * 16,
-              stage + TILEB + (wave + NWAVES) * 1024);
+    const int last = whole ? kTileKeys - 1
+                           : (!real ? 0 : (blk ? K : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys))) - 1);
+    const size_t toff = (size_t)t * TILEB;
+    const uint8_t* kp = (whole || (real && !blk)) ? kc0 + toff : kblk;
+    const uint8_t* vp = (whole || (real && !blk)) ? vc0 + toff : (real ? vblk : kblk);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const uint32_t off = (uint32_t)(min(crow[c], last) * ROWB) + cchunk[c];
+      r[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
+      r[CPT + c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
+    }
+  };
+  auto store_tile = [&](int stage, const Stage& r) __attribute__((always_inline)) {
+    uint8_t* sb = smem + stage * STAGEB;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      *reinterpret_cast<u32x4*>(sb + dk[c]) = r[c];
+      *reinterpret_cast<u32x4*>(sb + dv[c]) = r[CPT + c];
     }
   };
 
@@ -358,51 +284,53 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   // (exact in bf16 and fp32) and the accumulator rescale runs on a handful of
   // tiles only; normalisation by the sum makes the reference cancel exactly.
   float mref = kNegInf, neg_mref = 0.0f;
-  float l_run = 0.0f;  // this lane's half of the keys of each 32-key block
+  float l_run = 0.0f;  // this lane's half of the keys of each 8-key group
   f32x16 oacc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[mb][r] = 0.0f;
   const float c2 = a.scale_log2;
-  const int kbase = kh * 32;  // first key of this wave's half
   const int grp16 = lane >> 4;
   const int jj = (lane & 15) >> 2;
   const int qq = lane & 3;
-  const int krow = kbase + (lane & 31);
+  const int krow = lane & 31;  // key inside a 32-key half
 
   // Keys of tile t: nvalid(t) of them are real; the block tile is the last.
   auto tile_valid = [&](int t) __attribute__((always_inline)) {
     return (sr.has_block && t == sr.ncache) ? K : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys));
   };
 
-  // K fragments of this wave's 32 keys of the tile in `stage`.  Logical chunk
+  // K fragments of both 32-key halves of the tile in `stage`.  Logical chunk
   // 2*ds + half of row krow sits at byte 16 * (chunk ^ f(krow)) of the row,
-  // i.e. at (32*ds) ^ kswz with kswz = 16 * (half ^ f(krow)) < ROWB, so one
-  // per-lane base and an XOR per read address all NDS fragments.
+  // i.e. at (32*ds) ^ kswz with kswz = 16 * (half ^ f(krow)) < ROWB; f is the
+  // same for row krow + 32, so the second half is a constant offset away.
   const uint32_t kswz = 16u * (uint32_t)swz_k<DCH>(krow, half);
-  auto load_k = [&](int stage, bf16x8 (&kf)[NDS]) __attribute__((always_inline)) {
-    const uint32_t rowb = (uint32_t)(stage * STAGEB + krow * ROWB);  // multiple of ROWB
+  auto load_k = [&](int stage, bf16x8 (&kf)[2][NDS]) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(stage * STAGEB + krow * ROWB) + kswz;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-      kf[ds] = *reinterpret_cast<const bf16x8*>(smem + ((rowb + kswz) ^ (32u * ds)));
+    for (int ds = 0; ds < NDS; ++ds) {
+      const uint8_t* p = smem + (base ^ (32u * ds));
+      kf[0][ds] = *reinterpret_cast<const bf16x8*>(p);
+      kf[1][ds] = *reinterpret_cast<const bf16x8*>(p + HALFB);
+    }
   };
   // V^T fragments of the tile in `stage`, in the key order of the S^T
-  // accumulator registers (two MFMA k-steps of 16 keys x NMB head_dim blocks).
-  // The lane reads keys kA = kbase + 4*half + jj + 16*tt and kA + 8; all four
-  // are congruent mod 4, and the V swizzle depends on the row mod 4 only, so
-  // one base per head_dim block plus constant row offsets address them all.
+  // accumulator registers: key half h, MFMA k-step tt of 16 keys, head_dim
+  // block mb.  The lane reads keys 32h + 16tt + 4*half + jj and that + 8; all
+  // are congruent mod 4 and the V swizzle depends on the row mod 4 only, so
+  // one base per head_dim block plus constant offsets address them all.
   uint32_t vbase[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
-    const int key0 = kbase + 4 * half + jj;
+    const int key0 = 4 * half + jj;
     const int d0 = 32 * mb + 16 * (grp16 & 1) + 4 * qq;
     vbase[mb] = (uint32_t)(TILEB + key0 * ROWB + swz_v<DCH>(key0, d0 >> 3) * 16 + (d0 & 7) * 2);
   }
-  auto load_v = [&](int stage, bf16x8 (&vf)[2][NMB]) __attribute__((always_inline)) {
-    // per-tile bases, opaque to the optimiser so that the constant row
-    // offsets below fold into the LDS instructions instead of being
-    // precomputed per read and held in registers
+  typedef bf16x8 VFrag[2][2][NMB];
+  auto load_v = [&](int stage, VFrag& vf) __attribute__((always_inline)) {
+    // per-tile bases, opaque to the optimiser so that the constant offsets
+    // below fold into the LDS instructions
     uint32_t vb[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
@@ -410,39 +338,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
       asm("" : "+v"(vb[mb]));
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const uint8_t* pa = smem + vb[mb] + (16 * tt) * ROWB;
-        const uint8_t* pbp = pa + 8 * ROWB;
-        // whole-vector bit casts: element-wise inserts of the i16 lanes into
-        // the bf16 operand were lowered incorrectly by the compiler
-        const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa)));
-        const bf16x4 vb = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pbp)));
-        vf[tt][mb] = __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-    }
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const uint8_t* pa = smem + vb[mb] + h * HALFB + (16 * tt) * ROWB;
+          const uint8_t* pbp = pa + 8 * ROWB;
+          // whole-vector bit casts: element-wise inserts of the i16 lanes into
+          // the bf16 operand were lowered incorrectly by the compiler
+          const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa)));
+          const bf16x4 vb2 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pbp)));
+          vf[h][tt][mb] = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
   };
   // Padded keys and, in the verify view, block keys after the row: -inf.
-  auto mask_scores = [&](f32x16& s, int nvalid, bool block_tile) __attribute__((always_inline)) {
+  auto mask_scores = [&](f32x16 (&s)[2], int nvalid, bool block_tile) __attribute__((always_inline)) {
     int lim = nvalid;
     if (block_tile && a.causal) lim = min(lim, qrow_i + 1);
-    // register r holds key kbase + 4*half + 8*(r/4) + r%4; compare the
-    // constant part against an opaque per-lane bound (keeps the 16 key
-    // indices from being precomputed and held in registers)
-    int rel = lim - (kbase + 4 * half);
+    // register r of half h holds key 32h + 8*(r/4) + 4*half + r%4; compare the
+    // constant part against an opaque per-lane bound
+    int rel = lim - 4 * half;
     asm volatile("" : "+v"(rel));
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) < rel ? s[r] : kNegInf;
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[h][r] = (32 * h + 8 * (r >> 2) + (r & 3)) < rel ? s[h][r] : kNegInf;
+  };
+  bf16x8 qf[NDS];
+  // O^T += V^T P^T over the 64 keys of a tile (k-step 2h + tt).
+  auto pv = [&](const bf16x8 (&pb)[4], const VFrag& vf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) oacc[mb] = mfma32(vf[ks >> 1][ks & 1][mb], pb[ks], oacc[mb]);
   };
   // Row maximum of the tile; raise the reference (rare) if it is exceeded by
-  // more than 2^kLazy, rescaling the running sum and accumulator.
-  auto update_ref = [&](const f32x16& s) __attribute__((always_inline)) {
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  // more than 2^kLazy.  The previous tile's P V, still pending, is added first
+  // (it belongs to the old reference), then the accumulator and the running
+  // sum are rescaled.
+  auto update_ref = [&](const f32x16 (&s)[2], bf16x8 (&pprev)[4], const VFrag& vprev) __attribute__((always_inline)) {
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[1][0], s[1][1]));
 #pragma unroll
-    for (int r = 4; r < 16; r += 4) mx = fmaxf(mx, fmaxf(fmaxf(s[r], s[r + 1]), fmaxf(s[r + 2], s[r + 3])));
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
     if (__ballot(mx > mref + kLazy)) {
+      pv(pprev, vprev);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pprev[ks] = bf16x8{};
       const float mnew = fmaxf(mref, mx);
       const float alpha = (mref == kNegInf) ? 0.0f : fast_exp2(mref - mnew);
       mref = mnew;
@@ -452,175 +395,156 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
       for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
     }
   };
-  // O^T += V^T P^T with P the exponentiated scores in bf16.
-  auto pv = [&](const bf16x8 (&pb)[2], const bf16x8 (&vf)[2][NMB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) oacc[mb] = mfma32(vf[tt][mb], pb[tt], oacc[mb]);
-  };
-  auto s_mfma = [&](const bf16x8 (&kf)[NDS]) __attribute__((always_inline)) {
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) acc = mfma32(kf[ds], qf[ds], acc);
-    return acc;
-  };
   // exp2 of one score in the base-2 frame of the reference
   auto expo = [&](float s) __attribute__((always_inline)) { return fast_exp2(fmaf(s, c2, neg_mref)); };
+  auto next_stage = [](int s) __attribute__((always_inline)) { return s == kStages - 1 ? 0 : s + 1; };
+  auto prev_stage = [](int s) __attribute__((always_inline)) { return s == 0 ? kStages - 1 : s - 1; };
 
-  // ---- software pipeline over an LDS ring of kStages stages with kStages-1
-  // tiles in flight.  Iteration t holds the scores S(t) in registers, waits for
-  // tile t+1 and, on the same wave, issues the S(t+1) MFMAs interleaved with
-  // the exponentials of S(t) (the matrix core and the vector ALU overlap),
-  // then accumulates P(t) V(t).  The only loads are the copies, so the waits
-  // below count them exactly: q plus tiles 0..kStages-2 are in flight at the
-  // first wait.  Waves whose query block lies past the work-group's rows run
-  // the same code on zero queries (no branches in the loop) and write nothing.
-  auto stage_of = [](int t) __attribute__((always_inline)) { return (int)((unsigned)t % (unsigned)kStages); };
+  // ---- software pipeline.  LDS holds four tiles: t-1 (its V for the pending
+  // P(t-1) V(t-1)), t (V next), t+1 (K for S(t+1)) and t+2 (being written);
+  // registers hold the next two.  Iteration t issues three independent pieces
+  // of work on one wave: the S(t+1) MFMAs, the P(t-1) V(t-1) MFMAs and the
+  // exponentials of S(t), so the matrix core and the vector ALU overlap.  One
+  // barrier per tile: after it every wave is past iteration t-1, so the
+  // stage of tile t-2 can take tile t+2, and tile t+1 (written in iteration
+  // t-1) is visible.  Waves whose query block lies past the work-group's rows
+  // run the same code on zero queries and write nothing.
+  Stage stg0, stg1;  // at iteration t: tiles t+2 and t+3 (in flight or landed)
+  {
+    const int row = min(rg * plan.rows_per_wg + wrow, R - 1);
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + (row_base + row) * D);
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) issue_tile(t);
-  f32x16 sa, sb;
-  if (sr.ntiles > 0) {  // work-group uniform
-    wait_vmcnt<2 * CPT * (kStages - 2)>();  // q and tile 0 have landed for this wave
-    __syncthreads();                          // ... and for every wave
-    const int row = qb * 32 + (lane & 31);
-    const uint8_t* qs = smem + QSTAGE * STAGEB + row * ROWB;
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      qf[ds] = *reinterpret_cast<const bf16x8*>(qs + swz_k<DCH>(row, 2 * ds + half) * 16);
-      if (!active) qf[ds] = bf16x8{};
-    }
-    if (tile_valid(0) > kbase) {
-      bf16x8 kf[NDS];
-      load_k(0, kf);
-      sa = s_mfma(kf);
-    }
+    for (int ds = 0; ds < NDS; ++ds) qf[ds] = active ? qp[2 * ds + half] : bf16x8{};
   }
-  // tiles [0, nfull) are whole cache tiles: no masking, every wave computes them
-  const int nfull = min((sr.kend - sr.kstart) / kTileKeys, sr.ncache);
+  {
+    Stage t0, t1;
+    load_tile(0, t0);
+    load_tile(1, t1);
+    store_tile(0, t0);
+    load_tile(2, stg0);
+    store_tile(1, t1);
+    load_tile(3, stg1);
+  }
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  bf16x8 pprev[4];  // P(t-1) in bf16, the pending product's left operand
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) pprev[ks] = bf16x8{};
+  auto s_mfma = [&](const bf16x8 (&kf)[2][NDS], f32x16 (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[h][r] = 0.0f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) s[h] = mfma32(kf[h][ds], qf[ds], s[h]);
+    }
+  };
+  if (sr.ntiles > 0) {
+    bf16x8 kf[2][NDS];
+    load_k(0, kf);
+    s_mfma(kf, sa);
+  }
   const int nmain = nfull > 0 ? nfull - 1 : 0;  // iterations whose next tile is whole too
 
-  // One steady-state iteration: cur = S(t) -> P(t) V(t), nxt = S(t+1).
-  auto steady = [&](int t, f32x16& cur, f32x16& nxt) __attribute__((always_inline)) {
-    update_ref(cur);
-    wait_vmcnt<2 * CPT * (kStages - 3)>();  // this wave's copies of tile t+1 have landed
-    __syncthreads();  // everyone's have; all waves are past iteration t-1 (and the q reads)
-    issue_tile(t + kStages - 1);  // into the stage tile t-1 used
-    bf16x8 kf[NDS];
-    load_k(stage_of(t + 1), kf);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nxt[r] = 0.0f;
-    constexpr int EPS = 16 / NDS;  // exponentials per MFMA step
+  // One iteration: cur = S(t) -> P(t); pending P(t-1) V(t-1) is added;
+  // nxt = S(t+1) if there is a next tile.  Tile t sits in stage st, the
+  // pending V in stage vst; `refill` holds tile t+2 and takes tile t+4.
+  auto iteration = [&](int t, int st, int vst, f32x16 (&cur)[2], f32x16 (&nxt)[2], Stage& refill, bool masked,
+                       bool has_next) __attribute__((always_inline)) {
+    const int st1 = next_stage(st);   // tile t+1
+    const int st2 = next_stage(st1);  // tile t+2 (the stage tile t-2 used)
+    VFrag vf;
+    load_v(vst, vf);
+    if (masked) {
+      const bool blk = sr.has_block && t == sr.ncache;
+      if (blk || tile_valid(t) < kTileKeys) mask_scores(cur, tile_valid(t), blk);
+    }
+    update_ref(cur, pprev, vf);
     float lsum = 0.0f;
+    bf16x8 pnew[4];
+    if (has_next) {
+      __syncthreads();
+      store_tile(st2, refill);
+      load_tile(t + 4, refill);
+      bf16x8 kf[2][NDS];
+      load_k(st1, kf);
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      nxt = mfma32(kf[ds], qf[ds], nxt);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int e = 0; e < EPS; ++e) {
-        const float p_ = expo(cur[EPS * ds + e]);
-        cur[EPS * ds + e] = p_;
+        for (int r = 0; r < 16; ++r) nxt[h][r] = 0.0f;
+      // per S step: two S MFMAs, four exponentials, two pending PV MFMAs
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        nxt[0] = mfma32(kf[0][ds], qf[ds], nxt[0]);
+#pragma unroll
+        for (int e = 0; e < 32 / NDS; ++e) {
+          const int i = ds * (32 / NDS) + e;  // score i of the 32 this lane holds
+          const float p_ = expo(cur[i >> 4][i & 15]);
+          cur[i >> 4][i & 15] = p_;
+          lsum += p_;
+        }
+        nxt[1] = mfma32(kf[1][ds], qf[ds], nxt[1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 2 * ds + u;  // pending PV MFMA j of 4 * NMB
+          const int ks = j / NMB, mb = j % NMB;
+          oacc[mb] = mfma32(vf[ks >> 1][ks & 1][mb], pprev[ks], oacc[mb]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float p_ = expo(cur[i >> 4][i & 15]);
+        cur[i >> 4][i & 15] = p_;
         lsum += p_;
       }
+      pv(pprev, vf);
     }
     l_run += lsum;
-    bf16x8 pb[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[tt][e] = (__bf16)cur[8 * tt + e];
-    bf16x8 vf[2][NMB];
-    load_v(stage_of(t), vf);
-    pv(pb, vf);
+      for (int e = 0; e < 8; ++e) pnew[ks][e] = (__bf16)cur[ks >> 1][8 * (ks & 1) + e];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pprev[ks] = pnew[ks];
   };
-  int t = 0;
-  for (; t + 2 <= nmain; t += 2) {  // unrolled by two: the score registers alternate
-    steady(t, sa, sb);
-    steady(t + 1, sb, sa);
+  int t = 0, st = 0;
+  for (; t + 2 <= nmain; t += 2) {  // unrolled by two: scores and staging registers alternate
+    iteration(t, st, t == 0 ? st : prev_stage(st), sa, sb, stg0, false, true);
+    st = next_stage(st);
+    iteration(t + 1, st, prev_stage(st), sb, sa, stg1, false, true);
+    st = next_stage(st);
   }
-  if (t < nmain) {
-    steady(t, sa, sb);
-    sa = sb;
-    ++t;
-  }
-  // ---- the remaining (at most three) tiles: the last whole tile, a partial
-  // tile, the block tile
+  // ---- the remaining tiles (the last whole tile, a partial tile, the block
+  // tile; all of them if there are fewer than two whole tiles)
   for (; t < sr.ntiles; ++t) {
-    const int nv = tile_valid(t);
-    const bool blk = sr.has_block && t == sr.ncache;
-    const bool does = nv > kbase;
-    if (does) {
-      if (blk || nv < kbase + 32) mask_scores(sa, nv, blk);
-      update_ref(sa);
-      float lsum = 0.0f;
+    const bool has_next = t + 1 < sr.ntiles;
+    iteration(t, st, t == 0 ? st : prev_stage(st), sa, sb, stg0, true, has_next);
+    if (has_next) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p_ = expo(sa[r]);
-        sa[r] = p_;
-        lsum += p_;
+      for (int h = 0; h < 2; ++h) sa[h] = sb[h];
+#pragma unroll
+      for (int c = 0; c < 2 * CPT; ++c) {  // keep "stg0 holds tile t+2"
+        const u32x4 x = stg0[c];
+        stg0[c] = stg1[c];
+        stg1[c] = x;
       }
-      l_run += lsum;
     }
-    if (t + 1 < sr.ntiles) {
-      wait_vmcnt<2 * CPT * (kStages - 3)>();
-      __syncthreads();
-      issue_tile(t + kStages - 1);
-    }
-    if (does) {
-      bf16x8 pb[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[tt][e] = (__bf16)sa[8 * tt + e];
-      bf16x8 vf[2][NMB];
-      load_v(stage_of(t), vf);
-      pv(pb, vf);
-    }
-    if (t + 1 < sr.ntiles && tile_valid(t + 1) > kbase) {
-      bf16x8 kf[NDS];
-      load_k(stage_of(t + 1), kf);
-      sa = s_mfma(kf);
-    }
+    st = has_next ? next_stage(st) : st;
   }
-  wait_vmcnt<0>();  // trailing copies land before the ring is reused below
-
-  // ---- per-row totals: this lane holds half of the keys of its 32-key blocks
-  float l_row = l_run + __shfl_xor(l_run, 32);
-  float m_out = mref;  // base-2 reference of acc and l
-
-  // ---- combine the two key halves of every query block through LDS
-  __syncthreads();
-  {
-    float* slot = reinterpret_cast<float*>(smem) + (size_t)qb * RED_FLOATS;
-    if (active && kh == 1) {
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) slot[(mb * 16 + r) * 64 + lane] = oacc[mb][r];
-      slot[NMB * 16 * 64 + lane] = m_out;
-      slot[NMB * 16 * 64 + 64 + lane] = l_row;
-    }
-    __syncthreads();
-    if (active && kh == 0) {
-      const float m2 = slot[NMB * 16 * 64 + lane];
-      const float l2 = slot[NMB * 16 * 64 + 64 + lane];
-      const float M = fmaxf(m_out, m2);
-      const float w1 = (m_out == kNegInf) ? 0.0f : fast_exp2(m_out - M);
-      const float w2 = (m2 == kNegInf) ? 0.0f : fast_exp2(m2 - M);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[mb][r] = oacc[mb][r] * w1 + slot[(mb * 16 + r) * 64 + lane] * w2;
-      l_row = l_row * w1 + l2 * w2;
-      m_out = M;
-    }
+  if (sr.ntiles > 0) {  // the last tile's P V
+    VFrag vf;
+    load_v(st, vf);
+    pv(pprev, vf);
   }
-  const bool owner = active && kh == 0;
+
+  // ---- per-row totals: this lane holds half of the keys of every 8-key group
+  const float l_row = l_run + __shfl_xor(l_run, 32);
+  const float m_out = mref;  // base-2 reference of acc and l
 
   if (a.splits == 1 && direct) {
     // ---- one split: this work-group holds the final softmax of its rows
-    if (owner && qrow < R) {
+    if (active && qrow < R) {
       const float inv = 1.0f / l_row;
       uint16_t* op = a.out + (row_base + qrow) * D;
 #pragma unroll
@@ -641,28 +565,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
 
   // ---- store this split's partial: (reference max, sum) in fp32 and the
   // normalised output acc / sum in bf16
-  {
+  if (active) {
     const size_t slot = (size_t)grp * a.splits + split;
-    if (owner) {
-      const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-      uint16_t* acc = a.ws_acc + (slot * plan.rows_per_wg + wrow) * D;
+    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
+    uint16_t* acc = a.ws_acc + (slot * plan.rows_per_wg + wrow) * D;
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
+    for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          ushort4 o;
-          o.x = to_bf16_bits(oacc[mb][4 * q4 + 0] * inv);
-          o.y = to_bf16_bits(oacc[mb][4 * q4 + 1] * inv);
-          o.z = to_bf16_bits(oacc[mb][4 * q4 + 2] * inv);
-          o.w = to_bf16_bits(oacc[mb][4 * q4 + 3] * inv);
-          *reinterpret_cast<ushort4*>(acc + 32 * mb + 8 * q4 + 4 * half) = o;
-        }
-      if (half == 0) {
-        float2 ml;
-        ml.x = m_out;
-        ml.y = l_row;
-        *reinterpret_cast<float2*>(a.ws_ml + (slot * plan.rows_per_wg + wrow) * 2) = ml;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        ushort4 o;
+        o.x = to_bf16_bits(oacc[mb][4 * q4 + 0] * inv);
+        o.y = to_bf16_bits(oacc[mb][4 * q4 + 1] * inv);
+        o.z = to_bf16_bits(oacc[mb][4 * q4 + 2] * inv);
+        o.w = to_bf16_bits(oacc[mb][4 * q4 + 3] * inv);
+        *reinterpret_cast<ushort4*>(acc + 32 * mb + 8 * q4 + 4 * half) = o;
       }
+    if (half == 0) {
+      float2 ml;
+      ml.x = m_out;
+      ml.y = l_row;
+      *reinterpret_cast<float2*>(a.ws_ml + (slot * plan.rows_per_wg + wrow) * 2) = ml;
     }
   }
 }
