@@ -542,33 +542,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   const float l_row = l_run + __shfl_xor(l_run, 32);
   const float m_out = mref;  // base-2 reference of acc and l
 
-  if (a.splits == 1 && direct) {
-    // ---- one split: this work-group holds the final softmax of its rows
-    if (active && qrow < R) {
-      const float inv = 1.0f / l_row;
-      uint16_t* op = a.out + (row_base + qrow) * D;
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          ushort4 o;
-          o.x = to_bf16_bits(oacc[mb][4 * q4 + 0] * inv);
-          o.y = to_bf16_bits(oacc[mb][4 * q4 + 1] * inv);
-          o.z = to_bf16_bits(oacc[mb][4 * q4 + 2] * inv);
-          o.w = to_bf16_bits(oacc[mb][4 * q4 + 3] * inv);
-          *reinterpret_cast<ushort4*>(op + 32 * mb + 8 * q4 + 4 * half) = o;
-        }
-      if (a.lse != nullptr && half == 0) a.lse[row_base + qrow] = (m_out + log2f(l_row)) * kLn2;
-    }
-    return;
-  }
-
-  // ---- store this split's partial: (reference max, sum) in fp32 and the
-  // normalised output acc / sum in bf16
+  // ---- normalised rows in bf16 -> LDS (row pitch ROWB + 16 spreads the 32
+  // rows a store instruction touches over the banks) -> coalesced 16-byte
+  // global stores of whole rows.  The ring is free once every wave is past
+  // its last P V.
+  constexpr int OPITCH = ROWB + 16;
+  static_assert(128 * OPITCH <= kStages * STAGEB, "output rows fit the ring");
+  __syncthreads();
   if (active) {
-    const size_t slot = (size_t)grp * a.splits + split;
     const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-    uint16_t* acc = a.ws_acc + (slot * plan.rows_per_wg + wrow) * D;
+    uint8_t* orow = smem + wrow * OPITCH;
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -578,9 +561,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
         o.y = to_bf16_bits(oacc[mb][4 * q4 + 1] * inv);
         o.z = to_bf16_bits(oacc[mb][4 * q4 + 2] * inv);
         o.w = to_bf16_bits(oacc[mb][4 * q4 + 3] * inv);
-        *reinterpret_cast<ushort4*>(acc + 32 * mb + 8 * q4 + 4 * half) = o;
+        *reinterpret_cast<ushort4*>(orow + 2 * (32 * mb + 8 * q4 + 4 * half)) = o;
       }
-    if (half == 0) {
+  }
+  __syncthreads();
+  const int nrows = plan.rows_per_wg;  // the rows of the active query blocks
+  const bool one_split = a.splits == 1 && direct;
+  // destination of row r: the output (one split) or this split's partial slot
+  const size_t slot = (size_t)grp * a.splits + split;
+  for (int n = tid; n < nrows * DCH; n += kThreads) {
+    const int r = n / DCH, ch = n % DCH;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * OPITCH + ch * 16);
+    if (one_split) {
+      const int gr = rg * plan.rows_per_wg + r;  // row inside the (b, g) group
+      if (gr < R) *reinterpret_cast<u32x4*>(a.out + (row_base + gr) * D + ch * 8) = v;
+    } else {
+      *reinterpret_cast<u32x4*>(a.ws_acc + (slot * plan.rows_per_wg + r) * D + ch * 8) = v;
+    }
+  }
+  if (active && half == 0) {
+    if (one_split) {
+      if (a.lse != nullptr && qrow < R) a.lse[row_base + qrow] = (m_out + log2f(l_row)) * kLn2;
+    } else {
       float2 ml;
       ml.x = m_out;
       ml.y = l_row;
