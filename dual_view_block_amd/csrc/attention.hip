@@ -373,30 +373,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) oacc[mb] = mfma32(vf[ks >> 1][ks & 1][mb], pb[ks], oacc[mb]);
   };
-  // Row maximum of the tile; raise the reference (rare) if it is exceeded by
-  // more than 2^kLazy.  The previous tile's P V, still pending, is added first
-  // (it belongs to the old reference), then the accumulator and the running
-  // sum are rescaled.
-  auto update_ref = [&](const f32x16 (&s)[2], bf16x8 (&pprev)[4], const VFrag& vprev) __attribute__((always_inline)) {
+  // Scores -> base-2 exponents relative to the reference, x = s*c2 - mref,
+  // in place; then the reference is raised (rare) if some x exceeds 2^kLazy
+  // or the row has none yet.  The raise first adds the previous tile's P V,
+  // still pending (it belongs to the old reference), then shifts x and
+  // rescales the accumulator and the running sum.  The maximum is taken over
+  // the x values (finite or -inf, never NaN) and across the lane pair that
+  // shares a row with one permlane32 swap.
+  auto update_ref = [&](f32x16 (&s)[2], bf16x8 (&pprev)[4], const VFrag& vprev) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[h][r] = fmaf(s[h][r], c2, neg_mref);
     float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[1][0], s[1][1]));
 #pragma unroll
     for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c2;
-    if (__ballot(mx > mref + kLazy)) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    if (__ballot(mx > kLazy || mref == kNegInf)) {
       pv(pprev, vprev);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) pprev[ks] = bf16x8{};
-      const float mnew = fmaxf(mref, mx);
-      const float alpha = (mref == kNegInf) ? 0.0f : fast_exp2(mref - mnew);
-      mref = mnew;
-      neg_mref = (mnew == kNegInf) ? 0.0f : -mnew;
+      // raise by mx where that helps (mx is relative to the current frame)
+      const bool raise = mx != kNegInf && (mx > kLazy || mref == kNegInf);
+      const float shift = raise ? mx : 0.0f;
+      const float alpha = (mref == kNegInf || !raise) ? (mref == kNegInf ? 0.0f : 1.0f) : fast_exp2(-mx);
+      mref = raise ? (mref == kNegInf ? mx : mref + mx) : mref;
+      neg_mref = (mref == kNegInf) ? 0.0f : -mref;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[h][r] -= shift;
       l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
     }
   };
   // exp2 of one score in the base-2 frame of the reference
-  auto expo = [&](float s) __attribute__((always_inline)) { return fast_exp2(fmaf(s, c2, neg_mref)); };
+  auto expo = [&](float x) __attribute__((always_inline)) { return fast_exp2(x); };
   auto next_stage = [](int s) __attribute__((always_inline)) { return s == kStages - 1 ? 0 : s + 1; };
   auto prev_stage = [](int s) __attribute__((always_inline)) { return s == 0 ? kStages - 1 : s - 1; };
 
