@@ -10,7 +10,10 @@ What is computed follows the Orthrus pages:
 
 * block attention of the diffusion view and of the AR verify pass over one
   shared KV cache -- ``oracle.attention``;
-* greedy and T>0 (rejection-sampling) consensus -- ``oracle.consensus``.
+* greedy and T>0 (rejection-sampling) consensus -- ``oracle.consensus``;
+* the commit that closes a decode cycle (verified rows into the cache, new
+  lengths, emitted tokens, next anchor) and whole synthetic decode cycles --
+  ``oracle.cycle``.
 
 Every function is the plain definition written out in float64 (or exact
 integers), one sequence / head at a time, with explicit masks.  Library
@@ -28,11 +31,12 @@ from .consensus import (greedy_consensus, row_argmax, sample_consensus,
                         accept_prefix, accepts, residual_weights, inverse_cdf_pick,
                         fixed_point_weight, uniform_to_grid_int,
                         tokens_committed)
+from .cycle import bits_to_bf16, commit_block, decode_cycles
 
 __all__ = [
     "MASK_DIFF_BIDIR", "MASK_VERIFY_CAUSAL", "block_attention",
     "block_attention_rows", "transient_kv_bytes", "greedy_consensus",
     "row_argmax", "sample_consensus", "accept_prefix", "accepts", "residual_weights",
     "inverse_cdf_pick", "fixed_point_weight", "uniform_to_grid_int",
-    "tokens_committed",
+    "tokens_committed", "bits_to_bf16", "commit_block", "decode_cycles",
 ]

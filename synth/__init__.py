@@ -196,3 +196,40 @@ def sample_inputs(w: Workload, device="cpu", draft_noise: Optional[float] = None
     u = quantise_uniforms(torch.rand((B, K + 1), generator=gu, dtype=torch.float64))
     return (p64.float().to(device), q64.float().to(device),
             cand.to(torch.int32).to(device), u.to(device))
+
+
+def first_mismatch_geometric(n: int, block_k: int, accept_rate: float, seed: int) -> torch.Tensor:
+    """int64 [n] first-mismatch indices j* in 0..K: the number of leading
+    successes of independent trials with success probability ``accept_rate``,
+    capped at K.  With accept_rate 0.815 and K = 32 the mean of
+    j* + [j* < K] is about 5.4 tokens per cycle, the average tokens per
+    forward the pages report for the 8B model."""
+    g = _gen(seed, "cpu")
+    u = torch.rand((n, block_k), generator=g, dtype=torch.float64)
+    fail = u >= float(accept_rate)
+    first = torch.where(fail.any(dim=1), fail.to(torch.int64).argmax(dim=1),
+                        torch.full((n,), block_k, dtype=torch.int64))
+    return first
+
+
+def cycle_inputs(w: Workload, n_cycles: int, accept_rate: float = 0.815, device="cpu",
+                 seed_offset: int = 0, layers: Optional[int] = None):
+    """Inputs of ``n_cycles`` synthetic decode cycles (no model between calls).
+
+    Each cycle gets fresh block inputs for every layer and both views (q,
+    k_blk, v_blk drawn as in ``view_inputs``) and fresh verify logits and
+    candidates (``greedy_inputs``) whose first-mismatch index per sequence is
+    drawn by ``first_mismatch_geometric``.  Returns a list of dicts with keys
+    "diff", "verify" (per-layer (q, k_blk, v_blk) tuples), "logits", "cand"
+    and "j_star".
+    """
+    n_layers = w.layers if layers is None else layers
+    out = []
+    for c in range(n_cycles):
+        wc = w.replace(seed=w.seed * 1009 + 31 * c + seed_offset)
+        js = first_mismatch_geometric(w.batch, w.block_k, accept_rate, wc.seed * 13 + 3)
+        diff = [view_inputs(wc, layer, "diff", device) for layer in range(n_layers)]
+        verify = [view_inputs(wc, layer, "verify", device) for layer in range(n_layers)]
+        logits, cand, j_star = greedy_inputs(wc, device, first_mismatch=js)
+        out.append({"diff": diff, "verify": verify, "logits": logits, "cand": cand, "j_star": j_star})
+    return out
