@@ -46,6 +46,14 @@ def _parse():
                     help="block sizes timed for the latency-vs-K line ('' to skip)")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cycles", type=int, default=64,
+                    help="synthetic decode cycles timed after the step (0 to skip): per cycle both "
+                         "views of every layer, greedy consensus and the cache commit, replayed "
+                         "from a HIP graph")
+    ap.add_argument("--cycle-sets", type=int, default=8,
+                    help="distinct input sets the cycles rotate through (one graph round)")
+    ap.add_argument("--accept-rate", type=float, default=0.815,
+                    help="per-candidate match probability of the synthetic acceptance law")
     ap.add_argument("--traffic", default=TRAFFIC_JSON,
                     help="JSON record of rocprofv3-derived HBM bytes per streaming-kernel launch "
                          "(ignored if attention.hip changed since it was taken)")
@@ -240,6 +248,74 @@ def time_kernels(step, reps: int = 3):
     return out
 
 
+def commit_bytes(w, rows: float) -> float:
+    """Algorithmic bytes of one all-layer commit of `rows` rows per sequence:
+    the block rows read and the cache rows written (K and V), plus the small
+    per-sequence state (length, accept count, correction, candidates in; length,
+    anchor, tokens, token count out)."""
+    kv = 2 * w.layers * w.batch * w.n_kv_heads * rows * w.head_dim * 2
+    state = w.batch * (4 * 4 + 2 * 4 * w.block_k + 4 * 3)
+    return 2 * kv + state
+
+
+def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_rate: float):
+    """Synthetic decode cycles (both views of every layer, greedy consensus,
+    commit) issued through dual_view_block_amd.cycle.DecodeCycles: one round of
+    `n_sets` cycles is captured into a HIP graph and replayed; lengths advance
+    on the device.  Returns a dict of the measured figures."""
+    import torch
+
+    from dual_view_block_amd.cycle import DecodeCycles
+    from synth import cache_lengths, cycle_inputs
+
+    lens = cache_lengths(w, device)
+    sets = cycle_inputs(w, n_sets, accept_rate=accept_rate, device=device)
+    for s in sets:
+        s["logits"], s["cand"] = s["logits"].to(device), s["cand"].to(device)
+    drv = DecodeCycles(kc_all, vc_all, lens, sets)
+    drv.run(n_sets)                      # eager warm-up round
+    torch.cuda.synchronize()
+    drv.capture()
+    torch.cuda.synchronize()
+    rounds = max(1, n_cycles // n_sets)
+    stream = torch.cuda.current_stream()
+    l0 = lens.clone()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    drv.replay(rounds)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    cycles = rounds * n_sets
+    us = e0.elapsed_time(e1) * 1e3 / cycles
+    tokens = int((lens - l0).sum().item())
+    n_tok = [int(x) for s in range(n_sets) for x in drv.n_tokens[s].cpu().tolist()]
+
+    # the commit alone: back-to-back all-layer commits of one input set on the same stream
+    commit = drv._calls[0][-1]
+    reps = 16
+    sp = stream.cuda_stream
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(reps):
+        commit(sp)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    commit_us = c0.elapsed_time(c1) * 1e3 / reps
+    rows = float(drv.n_tokens[0].float().mean().item())
+    del drv
+    return {"cycles": cycles, "input_sets": n_sets, "launch": "hip_graph",
+            "us_per_cycle": round(us, 2), "cycles_per_s": round(1e6 / us, 2),
+            "host_wall_us_per_cycle": round(wall / cycles * 1e6, 2),
+            "tokens_per_cycle": round(tokens / (cycles * w.batch), 3),
+            "tokens_per_s": round(tokens / (us * 1e-6 * cycles), 1),
+            "accept_rate": accept_rate, "n_tokens_per_set": n_tok,
+            "cache_len_after": lens.cpu().tolist(),
+            "commit_us": round(commit_us, 3), "commit_rows": rows,
+            "commit_achieved_gbs": round(commit_bytes(w, rows) / (commit_us * 1e-6) / 1e9, 1)}
+
+
 def profile_target(args, w, caches, device) -> None:
     """Only the kernel under study, for rocprofv3 counter runs (no timing)."""
     import torch
@@ -306,7 +382,7 @@ def main():
         sys.exit(2)
     import torch
 
-    from synth import WORKLOADS, layer_cache
+    from synth import WORKLOADS, model_cache
 
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU (no HIP device visible)", file=sys.stderr)
@@ -323,10 +399,14 @@ def main():
     if args.profile_target == "copy":
         profile_target(args, w, None, device)
         return
-    caches = [layer_cache(w, layer, device) for layer in range(w.layers)]
+    # one layer-major cache for all layers, with room past L for the rows the
+    # synthetic decode cycles commit (the step itself reads rows [0, L) only)
+    w = w.replace(max_len=max(w.capacity, w.cache_len + (args.cycles + 2 * args.cycle_sets) * w.block_k))
+    kc_all, vc_all = model_cache(w, device)
+    caches = [(kc_all[layer], vc_all[layer]) for layer in range(w.layers)]
     torch.cuda.synchronize()
-    print(f"[bench] caches ready: {w.layers} layers x {2 * caches[0][0].numel() * 2 / 2**20:.0f} MiB",
-          file=sys.stderr, flush=True)
+    print(f"[bench] caches ready: {w.layers} layers x {2 * caches[0][0].numel() * 2 / 2**20:.0f} MiB "
+          f"(capacity {w.capacity})", file=sys.stderr, flush=True)
 
     if args.profile_target:
         profile_target(args, w, caches, device)
@@ -351,6 +431,12 @@ def main():
         sweep[K] = mk * 1e3
         del sk
         print(f"[bench] K={K}: step {mk * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    cyc = None
+    if args.cycles > 0:
+        cyc = time_cycles(w, kc_all, vc_all, device, args.cycles, args.cycle_sets, args.accept_rate)
+        print(f"[bench] cycles: {cyc['us_per_cycle']:.1f} us/cycle, {cyc['tokens_per_cycle']:.2f} tokens/cycle, "
+              f"commit {cyc['commit_us']:.2f} us", file=sys.stderr, flush=True)
 
     step_bytes = 2 * w.layers * attn_bytes(w) + greedy_bytes(w)
     value = step_bytes / (ms * 1e-3) / 1e12
@@ -390,6 +476,8 @@ def main():
                      "algorithmic_bytes_per_launch": pbytes,
                      "call_achieved_gbs": round(attn_bytes(w) / (kern["attn_call_us"] * 1e-6) / 1e9, 1)},
     }
+    if cyc is not None:
+        line["decode_cycles"] = cyc
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, caches, device)
     print(json.dumps(line), flush=True)

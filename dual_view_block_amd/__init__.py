@@ -8,7 +8,8 @@ torch's current HIP stream.  All computation happens in the gfx950 kernels.
 Sources for what each call computes: Orthrus paper notes (zhangshuibai.github.io
 paper-notes), §2.1, §3.2 and §4.1 (block attention of both views over the
 shared KV cache), §4.2 (greedy consensus), §4.3 and §7.2 (rejection-sampling
-consensus).
+consensus), §4.1 step 3 (closing the cycle: the verified rows go into the cache,
+the correction becomes the next anchor).
 """
 from __future__ import annotations
 
@@ -17,15 +18,16 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (ORTHRUS_MASK_DIFF_BIDIR, ORTHRUS_MASK_VERIFY_CAUSAL, AttnDesc, OrthrusError,
-                   status_string)
+from ._lib import (ORTHRUS_MASK_DIFF_BIDIR, ORTHRUS_MASK_VERIFY_CAUSAL, AttnDesc, CommitDesc,
+                   OrthrusError, status_string)
 
 __all__ = [
     "AttnDesc", "OrthrusError", "ORTHRUS_MASK_DIFF_BIDIR", "ORTHRUS_MASK_VERIFY_CAUSAL",
     "attn_desc", "orthrus_attn_workspace_size", "orthrus_attn_num_splits", "orthrus_block_attn",
     "orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_consensus_workspace_size",
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_status_string",
-    "PreparedAttention", "PreparedGreedy", "library_path",
+    "PreparedAttention", "PreparedGreedy", "library_path", "CommitDesc", "orthrus_cache_commit",
+    "PreparedCommit",
 ]
 
 
@@ -254,3 +256,74 @@ def orthrus_consensus_sample(p_target, q_draft, cand, uniforms, accept_len=None,
         accept_len.data_ptr(), correction.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream))
     _lib.check("orthrus_consensus_sample", st)
     return accept_len, correction
+
+
+def _check_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand):
+    """Shapes of a commit; 4-D caches/blocks are one layer.  Returns the descriptor."""
+    if k_cache.dim() == 4:
+        k_cache, v_cache = k_cache.unsqueeze(0), v_cache.unsqueeze(0)
+    if k_blk.dim() == 4:
+        k_blk, v_blk = k_blk.unsqueeze(0), v_blk.unsqueeze(0)
+    if k_cache.dim() != 5 or k_blk.dim() != 5:
+        raise ValueError("caches must be [n_layers, B, Hkv, max_len, D] and blocks [n_layers, B, Hkv, K, D]")
+    n_layers, B, Hkv, max_len, D = k_cache.shape
+    K = k_blk.shape[3]
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, (n_layers, B, Hkv, max_len, D))
+    _need(v_cache, "v_cache", torch.bfloat16, (n_layers, B, Hkv, max_len, D), dev)
+    _need(k_blk, "k_blk", torch.bfloat16, (n_layers, B, Hkv, K, D), dev)
+    _need(v_blk, "v_blk", torch.bfloat16, (n_layers, B, Hkv, K, D), dev)
+    _need(cache_len, "cache_len", torch.int32, (B,), dev)
+    _need(accept_len, "accept_len", torch.int32, (B,), dev)
+    _need(correction, "correction", torch.int32, (B,), dev)
+    _need(cand, "cand", torch.int32, (B, K), dev)
+    return CommitDesc(n_layers, B, Hkv, D, K, max_len)
+
+
+class PreparedCommit:
+    """A cache-commit call with every pointer resolved once (see
+    ``orthrus_cache_commit``); calling it issues one C call on the stream."""
+
+    def __init__(self, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand,
+                 next_anchor, tokens, n_tokens):
+        self.desc = _check_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand)
+        B, K, dev = self.desc.batch, self.desc.block_k, k_cache.device
+        _need(next_anchor, "next_anchor", torch.int32, (B,), dev)
+        _need(tokens, "tokens", torch.int32, (B, K), dev)
+        _need(n_tokens, "n_tokens", torch.int32, (B,), dev)
+        self._keep = (k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand,
+                      next_anchor, tokens, n_tokens)
+        self._fn = _lib.load().orthrus_cache_commit
+        self._args = (ctypes.byref(self.desc),) + tuple(t.data_ptr() for t in self._keep)
+
+    def __call__(self, stream_ptr: int) -> None:
+        st = self._fn(*self._args, stream_ptr)
+        if st:
+            _lib.check("orthrus_cache_commit", st)
+
+
+def orthrus_cache_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand,
+                         next_anchor=None, tokens=None, n_tokens=None, stream=None):
+    """Close one decode cycle on the device: the verified block rows go into the
+    caches and ``cache_len`` advances, both in place.
+
+    Caches bf16 [n_layers, B, Hkv, max_len, D] (or [B, Hkv, max_len, D] for one
+    layer), blocks bf16 [n_layers, B, Hkv, K, D] (or 4-D).  Returns
+    (next_anchor [B], tokens [B, K], n_tokens [B]), all int32."""
+    desc = _check_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand)
+    B, K, dev = desc.batch, desc.block_k, k_cache.device
+    if next_anchor is None:
+        next_anchor = torch.empty(B, dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if n_tokens is None:
+        n_tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    _need(next_anchor, "next_anchor", torch.int32, (B,), dev)
+    _need(tokens, "tokens", torch.int32, (B, K), dev)
+    _need(n_tokens, "n_tokens", torch.int32, (B,), dev)
+    st = _lib.load().orthrus_cache_commit(
+        ctypes.byref(desc), k_cache.data_ptr(), v_cache.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
+        cache_len.data_ptr(), accept_len.data_ptr(), correction.data_ptr(), cand.data_ptr(),
+        next_anchor.data_ptr(), tokens.data_ptr(), n_tokens.data_ptr(), _stream_ptr(stream))
+    _lib.check("orthrus_cache_commit", st)
+    return next_anchor, tokens, n_tokens

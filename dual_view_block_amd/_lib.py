@@ -28,7 +28,8 @@ EXPORTS = (
     "orthrus_attn_workspace_size", "orthrus_attn_num_splits", "orthrus_block_attn",
     "orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_block_attn_partial",
     "orthrus_block_attn_merge", "orthrus_consensus_workspace_size",
-    "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_status_string",
+    "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_cache_commit",
+    "orthrus_status_string",
 )
 
 
@@ -41,6 +42,17 @@ class AttnDesc(ctypes.Structure):
         ("block_k", ctypes.c_int32),
         ("max_len", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class CommitDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_k", ctypes.c_int32),
+        ("max_len", ctypes.c_int32),
     ]
 
 
@@ -66,6 +78,8 @@ _SIGS = {
     "orthrus_consensus_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "orthrus_consensus_greedy": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "orthrus_consensus_sample": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "orthrus_cache_commit": (_I32, [ctypes.POINTER(CommitDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P]),
     "orthrus_status_string": (ctypes.c_char_p, [_I32]),
 }
 

@@ -163,6 +163,22 @@ ConsensusPlan make_consensus_plan(int32_t B, int32_t K, int32_t V) {
   return p;
 }
 
+orthrus_status check_commit_desc(const orthrus_commit_desc* d) {
+  if (d == nullptr) return ORTHRUS_ERR_NULL_PTR;
+  if (d->n_layers < 1 || d->batch < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->block_k < 1 ||
+      d->max_len < 0)
+    return ORTHRUS_ERR_BAD_SHAPE;
+  if (d->head_dim % 8 != 0 || d->head_dim > 1024 || d->block_k > 1024) return ORTHRUS_ERR_UNSUPPORTED;
+  if ((long long)d->n_layers * d->batch * d->n_kv_heads > 0x7fffffffLL) return ORTHRUS_ERR_BAD_SHAPE;
+  return ORTHRUS_OK;
+}
+
+// true if the byte ranges [p, p+n) and [q, q+m) overlap
+bool overlaps(const void* p, size_t n, const void* q, size_t m) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
 }  // namespace
 }  // namespace orthrus
 
@@ -259,6 +275,35 @@ orthrus_status orthrus_consensus_sample(int32_t batch, int32_t block_k, int32_t 
   const hipError_t e = launch_consensus_sample(batch, block_k, vocab, p_target, q_draft, cand, uniforms,
                                                accept_len, correction, workspace, plan,
                                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_cache, uint16_t* v_cache,
+                                    const uint16_t* k_blk, const uint16_t* v_blk, int32_t* cache_len,
+                                    const int32_t* accept_len, const int32_t* correction,
+                                    const int32_t* cand, int32_t* next_anchor, int32_t* tokens,
+                                    int32_t* n_tokens, void* stream) {
+  const orthrus_status st = check_commit_desc(d);
+  if (st != ORTHRUS_OK) return st;
+  if (!k_cache || !v_cache || !k_blk || !v_blk || !cache_len || !accept_len || !correction || !cand ||
+      !next_anchor || !tokens || !n_tokens)
+    return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_blk) || !aligned16(v_blk) ||
+      !aligned4(cache_len) || !aligned4(accept_len) || !aligned4(correction) || !aligned4(cand) ||
+      !aligned4(next_anchor) || !aligned4(tokens) || !aligned4(n_tokens))
+    return ORTHRUS_ERR_MISALIGNED;
+  // the copies read the block while writing the cache: the two must not share memory
+  const size_t planes = (size_t)d->n_layers * d->batch * d->n_kv_heads;
+  const size_t cache_bytes = planes * d->max_len * d->head_dim * sizeof(uint16_t);
+  const size_t blk_bytes = planes * d->block_k * d->head_dim * sizeof(uint16_t);
+  if (overlaps(k_cache, cache_bytes, k_blk, blk_bytes) || overlaps(k_cache, cache_bytes, v_blk, blk_bytes) ||
+      overlaps(v_cache, cache_bytes, k_blk, blk_bytes) || overlaps(v_cache, cache_bytes, v_blk, blk_bytes) ||
+      overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
+    return ORTHRUS_ERR_BAD_SHAPE;
+  const hipError_t e = launch_cache_commit(d->n_layers, d->batch, d->n_kv_heads, d->head_dim, d->block_k,
+                                           d->max_len, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len,
+                                           correction, cand, next_anchor, tokens, n_tokens,
+                                           reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 

@@ -1,0 +1,127 @@
+// Closing a decode cycle on the device: the verified rows of the AR verify
+// block go into the shared KV cache, and the per-sequence state (length,
+// emitted tokens, next anchor) advances -- all stream-ordered, with no host
+// synchronisation (Orthrus paper notes §4.1 step 3: keep the matching
+// candidates, emit the correction, cut the cache back to t+j; §2.2: only the
+// AR path writes the cache).
+//
+// The unverified rows are simply never written, so the cut-back costs
+// nothing.  For one sequence with length t and a accepted candidates, verify
+// rows 0..r-1 (r = a + [a < K]: the anchor and the accepted candidates) are
+// one contiguous run of r*D bf16 in the block and land as one contiguous run
+// at row t of the same (layer, KV head) plane of the cache, so each plane is a
+// plain 16-byte-vector copy of at most K*D*2 bytes.
+//
+// Two launches: the row copies (every work-group reads the old length) and
+// then the state update, which rewrites the length in place.  Stream order
+// keeps the second behind the first.
+#include "common.h"
+
+namespace orthrus {
+namespace {
+
+struct CommitArgs {
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const uint16_t* k_blk;
+  const uint16_t* v_blk;
+  int32_t* cache_len;
+  const int32_t* accept_len;
+  const int32_t* correction;
+  const int32_t* cand;
+  int32_t* next_anchor;
+  int32_t* tokens;
+  int32_t* n_tokens;
+  int planes;      // n_layers * B * Hkv
+  int batch, n_kv_heads, head_dim, block_k, max_len;
+};
+
+constexpr int kCommitThreads = 256;
+
+// Rows a sequence commits, or -1 if the commit is refused (length or accept
+// count out of range, or not enough room left in the cache).
+__device__ __forceinline__ int commit_rows(int t, int a, int K, int max_len) {
+  if (t < 0 || a < 0 || a > K) return -1;
+  const int r = a < K ? a + 1 : K;
+  return t <= max_len - r ? r : -1;
+}
+
+// grid.x = planes, grid.y = 2 (keys, values)
+__global__ __launch_bounds__(kCommitThreads) void commit_rows_kernel(const CommitArgs a) {
+  const int plane = blockIdx.x;
+  const int b = (plane / a.n_kv_heads) % a.batch;
+  const int t = a.cache_len[b];
+  const int r = commit_rows(t, a.accept_len[b], a.block_k, a.max_len);
+  if (r <= 0) return;
+  const bool vals = blockIdx.y != 0;
+  const uint16_t* src = (vals ? a.v_blk : a.k_blk) + (size_t)plane * a.block_k * a.head_dim;
+  uint16_t* dst = (vals ? a.v_cache : a.k_cache) + ((size_t)plane * a.max_len + t) * a.head_dim;
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  const int n = r * (a.head_dim / 8);  // 16-byte vectors in the run
+  for (int i = threadIdx.x; i < n; i += kCommitThreads) d4[i] = s4[i];
+}
+
+// one thread per sequence
+__global__ __launch_bounds__(kCommitThreads) void commit_state_kernel(const CommitArgs a) {
+  const int b = blockIdx.x * kCommitThreads + threadIdx.x;
+  if (b >= a.batch) return;
+  const int K = a.block_k;
+  const int t = a.cache_len[b];
+  const int acc = a.accept_len[b];
+  const int r = commit_rows(t, acc, K, a.max_len);
+  int32_t* tok = a.tokens + (size_t)b * K;
+  if (r < 0) {
+    for (int i = 0; i < K; ++i) tok[i] = -1;
+    a.n_tokens[b] = 0;
+    a.next_anchor[b] = -1;
+    return;
+  }
+  const int32_t* cd = a.cand + (size_t)b * K;
+  for (int i = 0; i < acc; ++i) tok[i] = cd[i];
+  int last = acc > 0 ? cd[acc - 1] : -1;
+  int n = acc;
+  if (acc < K) {
+    last = a.correction[b];
+    tok[n++] = last;
+  }
+  for (int i = n; i < K; ++i) tok[i] = -1;
+  a.n_tokens[b] = n;
+  a.next_anchor[b] = last;
+  a.cache_len[b] = t + r;
+}
+
+}  // namespace
+
+hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head_dim, int block_k,
+                               int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,
+                               const uint16_t* v_blk, int32_t* cache_len, const int32_t* accept_len,
+                               const int32_t* correction, const int32_t* cand, int32_t* next_anchor,
+                               int32_t* tokens, int32_t* n_tokens, hipStream_t stream) {
+  CommitArgs a{};
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.cache_len = cache_len;
+  a.accept_len = accept_len;
+  a.correction = correction;
+  a.cand = cand;
+  a.next_anchor = next_anchor;
+  a.tokens = tokens;
+  a.n_tokens = n_tokens;
+  a.planes = n_layers * batch * n_kv_heads;
+  a.batch = batch;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
+  a.block_k = block_k;
+  a.max_len = max_len;
+  hipLaunchKernelGGL(commit_rows_kernel, dim3(a.planes, 2), dim3(kCommitThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(commit_state_kernel, dim3((batch + kCommitThreads - 1) / kCommitThreads),
+                     dim3(kCommitThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace orthrus

@@ -75,4 +75,13 @@ hipError_t launch_consensus_sample(int batch, int block_k, int vocab, const floa
                                    int32_t* correction, void* workspace,
                                    const ConsensusPlan& plan, hipStream_t stream);
 
+// ---------------------------------------------------------------- commit
+// Row copies of the verified block into the cache, then the in-place state
+// update (two launches on `stream`).
+hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head_dim, int block_k,
+                               int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,
+                               const uint16_t* v_blk, int32_t* cache_len, const int32_t* accept_len,
+                               const int32_t* correction, const int32_t* cand, int32_t* next_anchor,
+                               int32_t* tokens, int32_t* n_tokens, hipStream_t stream);
+
 }  // namespace orthrus

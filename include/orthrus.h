@@ -186,6 +186,56 @@ orthrus_status orthrus_consensus_sample(int32_t batch, int32_t block_k, int32_t 
                                         void* workspace, size_t workspace_bytes,
                                         void* stream);
 
+/* Shapes of one cycle commit.  The cache and block arrays of all n_layers
+ * layers are laid out layer-major, one after the other (a caller with
+ * separate per-layer buffers commits one layer per call, n_layers = 1). */
+typedef struct {
+  int32_t n_layers;    /* >= 1 layers committed by one call */
+  int32_t batch;       /* B >= 1 */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;    /* D, a multiple of 8, at most 1024 */
+  int32_t block_k;     /* K, 1..1024 */
+  int32_t max_len;     /* cache capacity per sequence = row stride of the cache */
+} orthrus_commit_desc;
+
+/* Close one decode cycle on the device: write the verified rows of the AR
+ * verify block into the shared cache and advance every sequence's state
+ * (paper notes §4.1 step 3: keep the matching candidates, emit the correction
+ * drawn at the first mismatch, cut the cache back to just past the kept
+ * prefix; §2.2: only the AR path writes the cache).
+ *
+ * For sequence b with t = cache_len[b] (positions before the anchor) and
+ * a = accept_len[b] (from orthrus_consensus_greedy / _sample), let
+ * r = a + [a < K].  Verify block rows 0..r-1 -- the anchor and the a accepted
+ * candidates, the tokens at positions t..t+r-1 -- are copied, byte for byte,
+ * into cache rows t..t+r-1 of every layer and KV head; no other cache row is
+ * touched (the unverified rows are never written, which is the cut-back).
+ *   k_cache, v_cache  bf16 [n_layers, B, Hkv, max_len, D]   (updated)
+ *   k_blk, v_blk      bf16 [n_layers, B, Hkv, K, D]  the AR K/V of the verify
+ *                     block (the k_blk/v_blk of orthrus_block_attn_verify);
+ *                     must not overlap the cache
+ *   cache_len   int32 [B]  read, then advanced IN PLACE to t + r
+ *   accept_len  int32 [B]
+ *   correction  int32 [B]  used when a < K
+ *   cand        int32 [B, K]  the diffusion candidates y1..yK
+ *   next_anchor int32 [B]  (written) correction if a < K, else cand[b, K-1]
+ *                          (all K accepted, no bonus token)
+ *   tokens      int32 [B, K] (written) the tokens the cycle emits:
+ *                          cand[b, 0..a-1], then the correction if a < K; -1 after
+ *   n_tokens    int32 [B]  (written) r, the number of emitted tokens (1..K)
+ * A sequence whose commit cannot be done -- t < 0, a outside [0, K], or
+ * t + r > max_len -- is left alone: no cache row is written, cache_len[b]
+ * stays, n_tokens[b] = 0 and next_anchor[b] and its tokens row are -1 (the
+ * caller checks n_tokens; a full cache is the usual cause).  Everything runs
+ * on `stream` without synchronising; the int32 arrays must not overlap one
+ * another.  Returns ORTHRUS_ERR_BAD_SHAPE if the block overlaps the cache or
+ * the K and V caches overlap. */
+orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_cache, uint16_t* v_cache,
+                                    const uint16_t* k_blk, const uint16_t* v_blk, int32_t* cache_len,
+                                    const int32_t* accept_len, const int32_t* correction,
+                                    const int32_t* cand, int32_t* next_anchor, int32_t* tokens,
+                                    int32_t* n_tokens, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* orthrus_status_string(orthrus_status s);
 

@@ -116,6 +116,20 @@ def layer_cache(w: Workload, layer: int, device="cpu"):
     return _randn_bf16(shape, g, device), _randn_bf16(shape, g, device)
 
 
+def model_cache(w: Workload, device="cpu"):
+    """The shared KV cache of every layer as two layer-major tensors
+    (k_cache, v_cache) bf16 [layers, B, Hkv, max_len, D]; layer l holds the
+    same draws as ``layer_cache(w, l)``."""
+    shape = (w.layers, w.batch, w.n_kv_heads, w.capacity, w.head_dim)
+    k = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    v = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    for layer in range(w.layers):
+        g = _gen(w.seed * 7919 + 104729 * layer + 1, device)
+        k[layer] = _randn_bf16(shape[1:], g, device)
+        v[layer] = _randn_bf16(shape[1:], g, device)
+    return k, v
+
+
 def view_inputs(w: Workload, layer: int, view: str, device="cpu"):
     """The block inputs of one view at one layer: (q, k_blk, v_blk) bf16.
 

@@ -111,6 +111,44 @@ def test_consensus_argument_checks():
     assert lib.orthrus_consensus_sample(1, 4, 0, P, P, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
 
 
+def _commit(desc, **ptrs):
+    lib = _lib.load()
+    p = dict(kc=1 << 40, vc=2 << 40, kb=3 << 40, vb=4 << 40, lens=4096, acc=8192, corr=12288, cand=16384,
+             anchor=20480, toks=24576, ntok=28672)
+    p.update(ptrs)
+    return lib.orthrus_cache_commit(ctypes.byref(desc) if desc is not None else None, p["kc"], p["vc"],
+                                    p["kb"], p["vb"], p["lens"], p["acc"], p["corr"], p["cand"],
+                                    p["anchor"], p["toks"], p["ntok"], None)
+
+
+def _cdesc(**kw):
+    base = dict(n_layers=36, batch=1, n_kv_heads=8, head_dim=128, block_k=32, max_len=32768 + 64)
+    base.update(kw)
+    return _lib.CommitDesc(**base)
+
+
+@pytest.mark.parametrize("desc,ptrs,expected", [
+    (None, {}, _lib.ORTHRUS_ERR_NULL_PTR),
+    (_cdesc(n_layers=0), {}, _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (_cdesc(batch=0), {}, _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (_cdesc(block_k=0), {}, _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (_cdesc(max_len=-1), {}, _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (_cdesc(head_dim=12), {}, _lib.ORTHRUS_ERR_UNSUPPORTED),
+    (_cdesc(head_dim=2048), {}, _lib.ORTHRUS_ERR_UNSUPPORTED),
+    (_cdesc(block_k=2000), {}, _lib.ORTHRUS_ERR_UNSUPPORTED),
+    (_cdesc(n_layers=1 << 16, batch=1 << 16), {}, _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (_cdesc(), dict(kb=None), _lib.ORTHRUS_ERR_NULL_PTR),
+    (_cdesc(), dict(ntok=None), _lib.ORTHRUS_ERR_NULL_PTR),
+    (_cdesc(), dict(kc=(1 << 40) + 8), _lib.ORTHRUS_ERR_MISALIGNED),
+    (_cdesc(), dict(lens=4098), _lib.ORTHRUS_ERR_MISALIGNED),
+    # block rows inside the K cache, and K and V caches that overlap
+    (_cdesc(), dict(kb=(1 << 40) + 4096), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (_cdesc(), dict(vc=(1 << 40) + (1 << 20)), _lib.ORTHRUS_ERR_BAD_SHAPE),
+])
+def test_commit_argument_checks(desc, ptrs, expected):
+    assert _commit(desc, **ptrs) == expected
+
+
 def test_valid_call_without_gpu_reports_hip_error():
     """Run in a child process: a well-formed call on a host with no GPU must
     come back as ORTHRUS_ERR_HIP (validation passed, the launch was refused)."""
@@ -121,11 +159,14 @@ def test_valid_call_without_gpu_reports_hip_error():
         "d = _lib.AttnDesc(1, 2, 1, 64, 4, 256, 0.0)\n"
         "P = 4096\n"
         "print(lib.orthrus_block_attn(ctypes.byref(d), 0, P, P, P, P, P, P, P, P, P, 1 << 30, None))\n"
+        "c = _lib.CommitDesc(1, 1, 1, 64, 4, 256)\n"
+        "print(lib.orthrus_cache_commit(ctypes.byref(c), 1 << 40, 2 << 40, 3 << 40, 4 << 40, P, P, P, P, P, P, "
+        "P, None))\n"
     ) % ROOT
     env = dict(os.environ, HIP_VISIBLE_DEVICES="")
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, env=env)
     assert res.returncode == 0, res.stderr
-    assert int(res.stdout.strip().splitlines()[-1]) == _lib.ORTHRUS_ERR_HIP
+    assert [int(x) for x in res.stdout.strip().splitlines()[-2:]] == [_lib.ORTHRUS_ERR_HIP] * 2
 
 
 def test_product_path_never_touches_the_oracle():
