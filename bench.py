@@ -50,17 +50,22 @@ def _parse():
                     help="synthetic decode cycles timed after the step (0 to skip): per cycle both "
                          "views of every layer, greedy consensus and the cache commit, replayed "
                          "from a HIP graph")
-    ap.add_argument("--cycle-sets", type=int, default=8,
-                    help="distinct input sets the cycles rotate through (one graph round)")
-    ap.add_argument("--accept-rate", type=float, default=0.815,
-                    help="per-candidate match probability of the synthetic acceptance law")
+    ap.add_argument("--cycle-sets", type=int, default=32,
+                    help="distinct input sets the cycles rotate through (one graph round); their "
+                         "first-mismatch indices are the quantiles of the acceptance law")
+    ap.add_argument("--accept-rate", type=float, default=0.912,
+                    help="per-candidate match probability of the synthetic acceptance law "
+                         "(0.912: 10.8 tokens per cycle at K = 32)")
     ap.add_argument("--traffic", default=TRAFFIC_JSON,
                     help="JSON record of rocprofv3-derived HBM bytes per streaming-kernel launch "
-                         "(ignored if attention.hip changed since it was taken)")
+                         "(ignored if the code of attention.hip changed since it was taken)")
     ap.add_argument("--profile-target", choices=["attn-stream", "copy"], default=None,
                     help="run only the streaming kernel over every layer-view (or a plain copy "
                          "kernel of --copy-mib MiB) --steps times, for rocprofv3 counter runs")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
+                    help="print per-kernel durations (markdown) from a rocprofv3 --kernel-trace "
+                         "results database and exit")
     ap.add_argument("--make-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                         "COPY_WRITE_CSV"),
                     help="turn four rocprofv3 --pmc counter_collection.csv files into the traffic "
@@ -82,11 +87,18 @@ def stream_bytes(w) -> int:
     return cache + q + blk
 
 
-def _sha256(path: str) -> str:
+def _code_sha256(path: str) -> str:
+    """SHA-256 of a C++/HIP source with comments and whitespace removed: it
+    changes whenever the code does, not when only its comments do."""
     import hashlib
+    import re
 
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(path) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = re.sub(r"\s+", " ", src).strip()
+    return hashlib.sha256(src.encode()).hexdigest()
 
 
 def _counter_kib(csv_path: str, kernel: str, counter: str) -> float:
@@ -111,7 +123,7 @@ def make_traffic(paths, out_path: str, copy_mib: int) -> None:
     cwrite = _counter_kib(cw_csv, COPY_KERNEL, "WRITE_SIZE")
     nbytes = copy_mib * 2**20
     rf, rw = nbytes / cfetch, nbytes / cwrite  # true bytes per counted KiB
-    rec = {"kernel": STREAM_KERNEL, "source_sha256": _sha256(ATTN_SOURCE),
+    rec = {"kernel": STREAM_KERNEL, "code_sha256": _code_sha256(ATTN_SOURCE),
            "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
            "copy_bytes_each_way": nbytes, "copy_fetch_kib": cfetch, "copy_write_kib": cwrite,
            "fetch_bytes_per_kib": rf, "write_bytes_per_kib": rw,
@@ -127,11 +139,43 @@ def load_traffic(path: str):
     if not path or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != _sha256(ATTN_SOURCE):
+    if rec.get("code_sha256") != _code_sha256(ATTN_SOURCE):
         print("[bench] traffic record predates the current attention.hip: reporting null",
               file=sys.stderr, flush=True)
         return None
     return rec.get("bytes_per_launch")
+
+
+def summarize_trace(db_path: str) -> None:
+    """Per-kernel duration statistics of a rocprofv3 kernel-trace database
+    (every dispatch of the library's kernels it holds), as a markdown table,
+    plus the median idle gap between consecutive dispatches."""
+    import re
+    import sqlite3
+
+    con = sqlite3.connect(db_path)
+    rows = list(con.execute("select name, start, end, grid_x, grid_y, grid_z, workgroup_x from kernels "
+                            "order by start"))
+    rows = [r for r in rows if "orthrus::" in r[0]]   # the library's kernels only
+    groups = {}
+    for name, t0, t1, gx, gy, gz, wg in rows:
+        nm = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", "").replace("void ", ""))
+        groups.setdefault((nm, gx, gy, gz, wg), []).append((t1 - t0) / 1e3)
+    print("| kernel | grid (threads) | wg | dispatches | mean µs | median µs | min µs | p90 µs |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (nm, gx, gy, gz, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        print(f"| {nm} | {gx} × {gy} × {gz} | {wg} | {len(v)} | {statistics.mean(v):.2f} | "
+              f"{statistics.median(v):.2f} | {v[0]:.2f} | {v[int(0.9 * (len(v) - 1))]:.2f} |")
+    gaps = {}
+    for a, b in zip(rows, rows[1:]):
+        key = tuple(re.sub(r"[<(].*", "", x[0].replace("(anonymous namespace)::", "")).split("::")[-1]
+                    for x in (a, b))
+        gaps.setdefault(key, []).append((b[1] - a[2]) / 1e3)
+    print()
+    for (na, nb), v in sorted(gaps.items()):
+        if len(v) > 3:
+            print(f"- gap {na} -> {nb}: {len(v)} pairs, median {statistics.median(v):.2f} µs")
 
 
 def greedy_bytes(w) -> int:
@@ -269,7 +313,7 @@ def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_ra
     from synth import cache_lengths, cycle_inputs
 
     lens = cache_lengths(w, device)
-    sets = cycle_inputs(w, n_sets, accept_rate=accept_rate, device=device)
+    sets = cycle_inputs(w, n_sets, accept_rate=accept_rate, device=device, stratified=True)
     for s in sets:
         s["logits"], s["cand"] = s["logits"].to(device), s["cand"].to(device)
     drv = DecodeCycles(kc_all, vc_all, lens, sets)
@@ -373,6 +417,9 @@ def cpu_baseline(w, caches, device, budget_s: float = 10.0):
 
 def main():
     args = _parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.make_traffic:
         make_traffic(args.make_traffic, args.traffic, args.copy_mib)
         return

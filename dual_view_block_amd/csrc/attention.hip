@@ -7,32 +7,36 @@
 // one softmax; block key j is visible to block row i always (diffusion view)
 // or iff j <= i (AR verify view).
 //
-// Work layout.  grid = (S splits, row groups, B * Hkv); one work-group of 8
-// waves (512 threads) per CU.  A work-group owns one contiguous chunk of the
-// (b, g) cache rows and up to 128 query rows (4 blocks of 32); the last split
-// also takes the K block keys as one extra masked tile.
-//  * Streaming: the chunk is read in tiles of 64 keys straight into a 5-stage
-//    LDS ring with global_load_lds (16 bytes per lane, no register staging);
-//    four tiles are in flight while one is computed.  The 16-byte chunks of
-//    every K and V row are XOR-permuted per row so that both read patterns
-//    below hit distinct LDS banks.  q is staged through the last ring stage
-//    before the first tile needs it.
-//  * Compute: wave w takes query block w%4 against key half w/4 of every
-//    tile.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 query rows;
-//    Q held in registers), so each lane owns one query row and its softmax
-//    statistics need one exchange with lane^32.  O^T += V^T P^T on the same
-//    MFMA: P^T is the S^T accumulator converted to bf16 in place; V^T comes
-//    from the row-major V tile through ds_read_b64_tr_b16, the transposing LDS
-//    read, with the key order matched to the accumulator's register order.
-//    The loop is software-pipelined: while the vector ALU exponentiates S(t),
-//    the same wave's matrix-core instructions compute S(t+1).
+// Work layout.  grid = (S splits, row groups, B * Hkv); one work-group of 4
+// waves (256 threads, one wave per SIMD) per CU.  A work-group owns one
+// contiguous chunk of the (b, g) cache rows and up to 128 query rows (4
+// blocks of 32, one per wave); the last split also takes the K block keys as
+// one extra masked tile.
+//  * Streaming: the chunk is read in tiles of 64 keys (16 KiB of K and 16 KiB
+//    of V at D = 128).  Every thread issues coalesced 16-byte nontemporal
+//    loads into registers two tiles ahead of use, then writes them into a
+//    4-stage LDS ring (tiles t-1 .. t+2, 128 KiB) at the row's permuted chunk
+//    position; one barrier per tile orders writes and reads.  The 16-byte
+//    chunks of every K and V row are XOR-permuted per row so that both read
+//    patterns below hit distinct LDS banks.
+//  * Compute: each wave takes its query block against both 32-key halves of
+//    every tile.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 query
+//    rows; Q held in registers), so each lane owns one query row and its
+//    softmax statistics need one exchange with lane^32 (a permlane32 swap).
+//    O^T += V^T P^T on the same MFMA: P^T is the S^T accumulator converted to
+//    bf16 in place; V^T comes from the row-major V tile through
+//    ds_read_b64_tr_b16, the transposing LDS read, with the key order matched
+//    to the accumulator's register order.  The loop is software-pipelined
+//    with P V delayed by one tile: iteration t interleaves the S(t+1) MFMAs,
+//    the P(t-1) V(t-1) MFMAs and the exponentials of S(t).
 //  * Softmax: P = 2^(s*scale*log2(e) - m_ref) with a lazily raised reference
-//    m_ref (raised only when a score exceeds it by more than 2^8), so the
-//    accumulator rescale is rare; the sum cancels the reference exactly.
-//  * The two key halves of a query block are combined through LDS.  With one
-//    split the work-group normalises and writes the rows itself.  Otherwise it
-//    stores a partial per row -- fp32 (m_ref, sum) and the bf16 value sum
-//    normalised by that sum -- and a second kernel merges the S partials:
+//    m_ref (raised only when a shifted score exceeds it by more than 2^8; a
+//    raise first flushes the pending P V), so the accumulator rescale is
+//    rare; the sum cancels the reference exactly.
+//  * Epilogue: with one split the work-group normalises and writes the rows
+//    itself.  Otherwise it stores a partial per row -- fp32 (m_ref, sum) and
+//    the bf16 value sum normalised by that sum, staged through LDS and written
+//    as whole coalesced rows -- and a second kernel merges the S partials:
 //    out = sum_s 2^(m_s-M) l_s o_s / sum_s 2^(m_s-M) l_s,
 //    lse = (M + log2 sum_s 2^(m_s-M) l_s) * ln 2, with one wave per row.
 #include "common.h"

@@ -215,9 +215,9 @@ def sample_inputs(w: Workload, device="cpu", draft_noise: Optional[float] = None
 def first_mismatch_geometric(n: int, block_k: int, accept_rate: float, seed: int) -> torch.Tensor:
     """int64 [n] first-mismatch indices j* in 0..K: the number of leading
     successes of independent trials with success probability ``accept_rate``,
-    capped at K.  With accept_rate 0.815 and K = 32 the mean of
-    j* + [j* < K] is about 5.4 tokens per cycle, the average tokens per
-    forward the pages report for the 8B model."""
+    capped at K.  With accept_rate 0.912 and K = 32 the mean of
+    j* + [j* < K] is about 10.8 tokens per cycle: two forwards per cycle at
+    the average 5.39 tokens per forward the pages report for the 8B model."""
     g = _gen(seed, "cpu")
     u = torch.rand((n, block_k), generator=g, dtype=torch.float64)
     fail = u >= float(accept_rate)
@@ -226,22 +226,47 @@ def first_mismatch_geometric(n: int, block_k: int, accept_rate: float, seed: int
     return first
 
 
-def cycle_inputs(w: Workload, n_cycles: int, accept_rate: float = 0.815, device="cpu",
-                 seed_offset: int = 0, layers: Optional[int] = None):
+def first_mismatch_quantiles(n: int, block_k: int, accept_rate: float, seed: int) -> torch.Tensor:
+    """int64 [n] first-mismatch indices that follow the law of
+    ``first_mismatch_geometric`` as closely as n values can: the (s + 1/2)/n
+    quantiles, s = 0..n-1, in a seeded random order.  For a benchmark that
+    cycles through a few input sets, this keeps the mean tokens per cycle at
+    the law's mean instead of a small random sample's."""
+    vals = []
+    for s in range(n):
+        u = (s + 0.5) / n
+        j = 0
+        while j < block_k and 1.0 - float(accept_rate) ** (j + 1) < u:
+            j += 1
+        vals.append(j)
+    perm = torch.randperm(n, generator=_gen(seed, "cpu"))
+    return torch.tensor(vals, dtype=torch.int64)[perm]
+
+
+def cycle_inputs(w: Workload, n_cycles: int, accept_rate: float = 0.912, device="cpu",
+                 seed_offset: int = 0, layers: Optional[int] = None, stratified: bool = False):
     """Inputs of ``n_cycles`` synthetic decode cycles (no model between calls).
 
     Each cycle gets fresh block inputs for every layer and both views (q,
     k_blk, v_blk drawn as in ``view_inputs``) and fresh verify logits and
     candidates (``greedy_inputs``) whose first-mismatch index per sequence is
-    drawn by ``first_mismatch_geometric``.  Returns a list of dicts with keys
+    drawn by ``first_mismatch_geometric`` (or, with ``stratified``, taken from
+    ``first_mismatch_quantiles`` over all cycles and sequences).  Returns a list of dicts with keys
     "diff", "verify" (per-layer (q, k_blk, v_blk) tuples), "logits", "cand"
     and "j_star".
     """
     n_layers = w.layers if layers is None else layers
+    strata = None
+    if stratified:
+        strata = first_mismatch_quantiles(n_cycles * w.batch, w.block_k, accept_rate,
+                                          w.seed * 1009 + seed_offset + 5).reshape(n_cycles, w.batch)
     out = []
     for c in range(n_cycles):
         wc = w.replace(seed=w.seed * 1009 + 31 * c + seed_offset)
-        js = first_mismatch_geometric(w.batch, w.block_k, accept_rate, wc.seed * 13 + 3)
+        if strata is not None:
+            js = strata[c].clone()
+        else:
+            js = first_mismatch_geometric(w.batch, w.block_k, accept_rate, wc.seed * 13 + 3)
         diff = [view_inputs(wc, layer, "diff", device) for layer in range(n_layers)]
         verify = [view_inputs(wc, layer, "verify", device) for layer in range(n_layers)]
         logits, cand, j_star = greedy_inputs(wc, device, first_mismatch=js)

@@ -285,9 +285,27 @@ def test_decode_cycles_follow_the_planted_acceptance():
     assert np.array_equal(state["cache_len"], cur)
 
 
-def test_geometric_first_mismatch_mean():
-    j = first_mismatch_geometric(100000, 32, 0.815, 1)
+@pytest.mark.parametrize("rate", [0.815, 0.912])
+def test_geometric_first_mismatch_mean(rate):
+    j = first_mismatch_geometric(100000, 32, rate, 1)
     assert j.min() >= 0 and j.max() <= 32
     n = (j + (j < 32).long()).double().mean().item()
-    expected = sum(0.815 ** i for i in range(1, 33)) + 1 - 0.815 ** 32
-    assert abs(n - expected) < 0.05
+    # E[j*] = sum_{i=1..K} P(j* >= i) = sum rate^i; plus P(j* < K) = 1 - rate^K
+    expected = sum(rate ** i for i in range(1, 33)) + 1 - rate ** 32
+    assert abs(n - expected) < 0.05 * expected
+    if rate == 0.912:
+        assert abs(expected - 2 * 5.39) < 0.1
+
+
+def test_quantile_first_mismatch_follow_the_law():
+    from synth import first_mismatch_quantiles
+    j = first_mismatch_quantiles(16, 32, 0.815, 3)
+    # P(j* <= j) = 1 - 0.815^(j+1): the (s+1/2)/16 quantiles, worked out by hand
+    assert sorted(j.tolist()) == [0, 0, 0, 1, 1, 2, 2, 3, 3, 4, 5, 6, 7, 9, 11, 16]
+    n = j + (j < 32).long()
+    assert abs(n.double().mean().item() - 5.4) < 0.1
+    j = first_mismatch_quantiles(32, 32, 0.912, 3)
+    n = j + (j < 32).long()
+    assert abs(n.double().mean().item() - 10.8) < 0.1
+    assert first_mismatch_quantiles(4, 8, 1.0, 0).tolist() == [8, 8, 8, 8]
+    assert first_mismatch_quantiles(4, 8, 0.0, 0).tolist() == [0, 0, 0, 0]
