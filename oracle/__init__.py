@@ -13,7 +13,9 @@ What is computed follows the Orthrus pages:
 * greedy and T>0 (rejection-sampling) consensus -- ``oracle.consensus``;
 * the commit that closes a decode cycle (verified rows into the cache, new
   lengths, emitted tokens, next anchor) and whole synthetic decode cycles --
-  ``oracle.cycle``.
+  ``oracle.cycle``;
+* the training objective's forward KL(P_AR || P_Diff) over the vocabulary and
+  its draft-logit gradient -- ``oracle.kl``.
 
 Every function is the plain definition written out in float64 (or exact
 integers), one sequence / head at a time, with explicit masks.  Library
@@ -32,11 +34,13 @@ from .consensus import (greedy_consensus, row_argmax, sample_consensus,
                         fixed_point_weight, uniform_to_grid_int,
                         tokens_committed)
 from .cycle import bits_to_bf16, commit_block, decode_cycles
+from .kl import forward_kl, forward_kl_rows
 
 __all__ = [
     "MASK_DIFF_BIDIR", "MASK_VERIFY_CAUSAL", "block_attention",
     "block_attention_rows", "transient_kv_bytes", "greedy_consensus",
     "row_argmax", "sample_consensus", "accept_prefix", "accepts", "residual_weights",
     "inverse_cdf_pick", "fixed_point_weight", "uniform_to_grid_int",
-    "tokens_committed", "bits_to_bf16", "commit_block", "decode_cycles",
+    "tokens_committed", "bits_to_bf16", "commit_block", "decode_cycles", "forward_kl",
+    "forward_kl_rows",
 ]
