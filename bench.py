@@ -53,15 +53,19 @@ def _parse():
     ap.add_argument("--cycle-sets", type=int, default=32,
                     help="distinct input sets the cycles rotate through (one graph round); their "
                          "first-mismatch indices are the quantiles of the acceptance law")
+    ap.add_argument("--kl-rows", type=int, default=8192,
+                    help="rows of the forward-KL measurement (256 blocks x K = 32 diffusion positions "
+                         "of one packed training sequence; 0 to skip)")
     ap.add_argument("--accept-rate", type=float, default=0.912,
                     help="per-candidate match probability of the synthetic acceptance law "
                          "(0.912: 10.8 tokens per cycle at K = 32)")
     ap.add_argument("--traffic", default=TRAFFIC_JSON,
                     help="JSON record of rocprofv3-derived HBM bytes per streaming-kernel launch "
                          "(ignored if the code of attention.hip changed since it was taken)")
-    ap.add_argument("--profile-target", choices=["attn-stream", "copy"], default=None,
+    ap.add_argument("--profile-target", choices=["attn-stream", "copy", "forward-kl"], default=None,
                     help="run only the streaming kernel over every layer-view (or a plain copy "
-                         "kernel of --copy-mib MiB) --steps times, for rocprofv3 counter runs")
+                         "kernel of --copy-mib MiB, or the forward KL with its gradient at "
+                         "--kl-rows x vocab) --steps times, for rocprofv3 counter runs")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
                     help="print per-kernel durations (markdown) from a rocprofv3 --kernel-trace "
@@ -360,6 +364,44 @@ def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_ra
             "commit_achieved_gbs": round(commit_bytes(w, rows) / (commit_us * 1e-6) / 1e9, 1)}
 
 
+def time_forward_kl(device, rows: int, vocab: int, reps: int = 10):
+    """Fused forward KL(P_AR || P_Diff) over the vocabulary (the distillation
+    loss) on bf16 logits [rows, vocab]: the loss alone and the loss with its
+    draft-logit gradient, each timed with HIP events around `reps` back-to-back
+    calls on the launch stream.  Algorithmic bytes: both logit arrays read once
+    (+ the bf16 gradient written once, + the fp32 losses)."""
+    import torch
+
+    import dual_view_block_amd as dvb
+    from synth import kl_inputs
+
+    a, b = kl_inputs(rows, vocab, 3.0, torch.bfloat16, seed=5, device=device)
+    kl = torch.empty(rows, dtype=torch.float32, device=device)
+    grad = torch.empty_like(a)
+    ws = torch.empty(dvb.orthrus_kl_workspace_size(rows, vocab, torch.bfloat16), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    out = {"rows": rows, "vocab": vocab, "dtype": "bf16"}
+    for name, g in (("loss", None), ("loss_and_grad", grad)):
+        call = dvb.PreparedForwardKL(a, b, kl, g, ws, grad_scale=1.0 / rows)
+        call(sp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call(sp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nbytes = 2 * rows * vocab * 2 + rows * 4 + (rows * vocab * 2 if g is not None else 0)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 2), "algorithmic_bytes": nbytes, "achieved_gbs": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    out["mean_kl"] = round(float(kl.mean().item()), 4)
+    del a, b, grad
+    return out
+
+
 def profile_target(args, w, caches, device) -> None:
     """Only the kernel under study, for rocprofv3 counter runs (no timing)."""
     import torch
@@ -369,6 +411,13 @@ def profile_target(args, w, caches, device) -> None:
         dst = torch.empty_like(src)
         for _ in range(args.steps):
             dst.copy_(src)  # device-to-device: one copy kernel, reads and writes copy_mib MiB
+    elif args.profile_target == "forward-kl":
+        import dual_view_block_amd as dvb
+        from synth import kl_inputs
+
+        a, b = kl_inputs(args.kl_rows, w.vocab, 3.0, torch.bfloat16, seed=5, device=device)
+        for _ in range(args.steps):
+            dvb.orthrus_forward_kl(a, b, want_grad=True, grad_scale=1.0 / args.kl_rows)
     else:
         step = Step(w, caches, device)
         sp = torch.cuda.current_stream().cuda_stream
@@ -443,7 +492,7 @@ def main():
     if args.layers:
         w = w.replace(layers=args.layers)
     print(f"[bench] workload {w}", file=sys.stderr, flush=True)
-    if args.profile_target == "copy":
+    if args.profile_target in ("copy", "forward-kl"):
         profile_target(args, w, None, device)
         return
     # one layer-major cache for all layers, with room past L for the rows the
@@ -485,6 +534,13 @@ def main():
         print(f"[bench] cycles: {cyc['us_per_cycle']:.1f} us/cycle, {cyc['tokens_per_cycle']:.2f} tokens/cycle, "
               f"commit {cyc['commit_us']:.2f} us", file=sys.stderr, flush=True)
 
+    fkl = None
+    if args.kl_rows > 0:
+        fkl = time_forward_kl(device, args.kl_rows, w.vocab)
+        print(f"[bench] forward KL {fkl['rows']}x{fkl['vocab']} bf16: loss {fkl['loss']['us']:.1f} us "
+              f"({fkl['loss']['achieved_gbs']:.0f} GB/s), loss+grad {fkl['loss_and_grad']['us']:.1f} us "
+              f"({fkl['loss_and_grad']['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+
     step_bytes = 2 * w.layers * attn_bytes(w) + greedy_bytes(w)
     value = step_bytes / (ms * 1e-3) / 1e12
     pbytes = stream_bytes(w)
@@ -525,6 +581,8 @@ def main():
     }
     if cyc is not None:
         line["decode_cycles"] = cyc
+    if fkl is not None:
+        line["forward_kl"] = fkl
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, caches, device)
     print(json.dumps(line), flush=True)

@@ -9,7 +9,8 @@ Sources for what each call computes: Orthrus paper notes (zhangshuibai.github.io
 paper-notes), §2.1, §3.2 and §4.1 (block attention of both views over the
 shared KV cache), §4.2 (greedy consensus), §4.3 and §7.2 (rejection-sampling
 consensus), §4.1 step 3 (closing the cycle: the verified rows go into the cache,
-the correction becomes the next anchor).
+the correction becomes the next anchor), §3.3 (the forward-KL distillation loss
+of training).
 """
 from __future__ import annotations
 
@@ -27,7 +28,7 @@ __all__ = [
     "orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_consensus_workspace_size",
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_status_string",
     "PreparedAttention", "PreparedGreedy", "library_path", "CommitDesc", "orthrus_cache_commit",
-    "PreparedCommit",
+    "PreparedCommit", "orthrus_kl_workspace_size", "orthrus_forward_kl", "PreparedForwardKL",
 ]
 
 
@@ -327,3 +328,70 @@ def orthrus_cache_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, 
         next_anchor.data_ptr(), tokens.data_ptr(), n_tokens.data_ptr(), _stream_ptr(stream))
     _lib.check("orthrus_cache_commit", st)
     return next_anchor, tokens, n_tokens
+
+
+_KL_DTYPES = {torch.float32: _lib.ORTHRUS_DTYPE_F32, torch.bfloat16: _lib.ORTHRUS_DTYPE_BF16}
+
+
+def orthrus_kl_workspace_size(rows: int, vocab: int, dtype) -> int:
+    return int(_lib.load().orthrus_kl_workspace_size(rows, vocab, _KL_DTYPES[dtype]))
+
+
+def _check_kl(target, draft):
+    if target.dim() != 2:
+        raise ValueError("logits must be [rows, V]")
+    if target.dtype not in _KL_DTYPES:
+        raise TypeError("logits must be float32 or bfloat16")
+    rows, V = target.shape
+    _need(target, "target_logits", target.dtype, (rows, V))
+    _need(draft, "draft_logits", target.dtype, (rows, V), target.device)
+    return rows, V
+
+
+class PreparedForwardKL:
+    """A forward-KL call with every pointer resolved once (see ``orthrus_forward_kl``)."""
+
+    def __init__(self, target, draft, kl, grad, workspace, grad_scale: float = 1.0):
+        rows, V = _check_kl(target, draft)
+        dev = target.device
+        _need(kl, "kl", torch.float32, (rows,), dev)
+        if grad is not None:
+            _need(grad, "grad", target.dtype, (rows, V), dev)
+        nbytes = orthrus_kl_workspace_size(rows, V, target.dtype)
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")
+        self._keep = (target, draft, kl, grad, workspace)
+        self._fn = _lib.load().orthrus_forward_kl
+        self._args = (rows, V, _KL_DTYPES[target.dtype], target.data_ptr(), draft.data_ptr(), kl.data_ptr(),
+                      grad.data_ptr() if grad is not None else None, float(grad_scale), workspace.data_ptr(),
+                      workspace.numel())
+
+    def __call__(self, stream_ptr: int) -> None:
+        st = self._fn(*self._args, stream_ptr)
+        if st:
+            _lib.check("orthrus_forward_kl", st)
+
+
+def orthrus_forward_kl(target_logits, draft_logits, kl=None, grad=None, want_grad: bool = False,
+                       grad_scale: float = 1.0, workspace=None, stream=None):
+    """Forward KL(softmax(target) || softmax(draft)) per row, and optionally its
+    gradient with respect to the draft logits (times ``grad_scale``).
+
+    Logits [rows, V], float32 or bfloat16.  Returns (kl fp32 [rows], grad
+    [rows, V] in the logits' dtype, or None)."""
+    rows, V = _check_kl(target_logits, draft_logits)
+    dev = target_logits.device
+    if kl is None:
+        kl = torch.empty(rows, dtype=torch.float32, device=dev)
+    _need(kl, "kl", torch.float32, (rows,), dev)
+    if grad is None and want_grad:
+        grad = torch.empty_like(target_logits)
+    if grad is not None:
+        _need(grad, "grad", target_logits.dtype, (rows, V), dev)
+    ws = _workspace(orthrus_kl_workspace_size(rows, V, target_logits.dtype), dev, workspace)
+    st = _lib.load().orthrus_forward_kl(
+        rows, V, _KL_DTYPES[target_logits.dtype], target_logits.data_ptr(), draft_logits.data_ptr(),
+        kl.data_ptr(), grad.data_ptr() if grad is not None else None, float(grad_scale), ws.data_ptr(),
+        ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_forward_kl", st)
+    return kl, grad

@@ -22,6 +22,8 @@ ORTHRUS_ERR_WORKSPACE_TOO_SMALL = 5
 ORTHRUS_ERR_HIP = 6
 ORTHRUS_MASK_DIFF_BIDIR = 0
 ORTHRUS_MASK_VERIFY_CAUSAL = 1
+ORTHRUS_DTYPE_F32 = 0
+ORTHRUS_DTYPE_BF16 = 1
 
 # every symbol include/orthrus.h declares
 EXPORTS = (
@@ -29,7 +31,7 @@ EXPORTS = (
     "orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_block_attn_partial",
     "orthrus_block_attn_merge", "orthrus_consensus_workspace_size",
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_cache_commit",
-    "orthrus_status_string",
+    "orthrus_kl_workspace_size", "orthrus_forward_kl", "orthrus_status_string",
 )
 
 
@@ -80,6 +82,8 @@ _SIGS = {
     "orthrus_consensus_sample": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "orthrus_cache_commit": (_I32, [ctypes.POINTER(CommitDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _P]),
+    "orthrus_kl_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "orthrus_forward_kl": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _SZ, _P]),
     "orthrus_status_string": (ctypes.c_char_p, [_I32]),
 }
 

@@ -173,6 +173,34 @@ orthrus_status check_commit_desc(const orthrus_commit_desc* d) {
   return ORTHRUS_OK;
 }
 
+orthrus_status check_kl_sizes(int32_t rows, int32_t vocab, int dtype) {
+  if (dtype != ORTHRUS_DTYPE_F32 && dtype != ORTHRUS_DTYPE_BF16) return ORTHRUS_ERR_BAD_SHAPE;
+  if (rows < 1 || vocab < 1) return ORTHRUS_ERR_BAD_SHAPE;
+  if (rows > 65535) return ORTHRUS_ERR_UNSUPPORTED;
+  return ORTHRUS_OK;
+}
+
+// work-groups per CU of the persistent partial pass of the forward KL
+constexpr int kKlWgPerCu = 8;
+
+struct KlPlan {
+  int esize;
+  bool vec;
+  int chunks;
+  size_t part_bytes, lse_bytes, ws_bytes;
+};
+
+KlPlan make_kl_plan(int32_t rows, int32_t vocab, int dtype) {
+  KlPlan p{};
+  p.esize = dtype == ORTHRUS_DTYPE_F32 ? 4 : 2;
+  p.vec = ((size_t)vocab * p.esize) % 16 == 0;
+  p.chunks = kl_chunks(vocab, p.esize, p.vec);
+  p.part_bytes = round_up((size_t)rows * p.chunks * 8 * sizeof(float), kAlign);
+  p.lse_bytes = round_up((size_t)rows * 2 * sizeof(float), kAlign);
+  p.ws_bytes = p.part_bytes + p.lse_bytes;
+  return p;
+}
+
 // true if the byte ranges [p, p+n) and [q, q+m) overlap
 bool overlaps(const void* p, size_t n, const void* q, size_t m) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
@@ -304,6 +332,33 @@ orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_ca
                                            d->max_len, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len,
                                            correction, cand, next_anchor, tokens, n_tokens,
                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, orthrus_dtype dtype) {
+  if (check_kl_sizes(rows, vocab, (int)dtype) != ORTHRUS_OK) return 0;
+  return make_kl_plan(rows, vocab, (int)dtype).ws_bytes;
+}
+
+orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, orthrus_dtype dtype, const void* target_logits,
+                                  const void* draft_logits, float* kl, void* grad, float grad_scale,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const orthrus_status st = check_kl_sizes(rows, vocab, (int)dtype);
+  if (st != ORTHRUS_OK) return st;
+  if (!target_logits || !draft_logits || !kl || !workspace) return ORTHRUS_ERR_NULL_PTR;
+  if (!isfinite(grad_scale)) return ORTHRUS_ERR_BAD_SHAPE;
+  if (!aligned16(target_logits) || !aligned16(draft_logits) || !aligned4(kl) || (grad && !aligned16(grad)) ||
+      !aligned16(workspace))
+    return ORTHRUS_ERR_MISALIGNED;
+  const KlPlan plan = make_kl_plan(rows, vocab, (int)dtype);
+  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+  const int cus = device_cus();
+  if (cus < 1) return ORTHRUS_ERR_HIP;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const hipError_t e = launch_forward_kl(rows, vocab, plan.esize, plan.vec, target_logits, draft_logits, kl, grad,
+                                         grad_scale, reinterpret_cast<float*>(ws),
+                                         reinterpret_cast<float*>(ws + plan.part_bytes), kKlWgPerCu * cus,
+                                         reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 

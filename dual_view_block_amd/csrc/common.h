@@ -84,4 +84,15 @@ hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head
                                const int32_t* correction, const int32_t* cand, int32_t* next_anchor,
                                int32_t* tokens, int32_t* n_tokens, hipStream_t stream);
 
+// ---------------------------------------------------------------- forward KL
+// Vocabulary chunks per row (one work-group each) for a logits element size
+// and load form (16-byte vectors when every row starts 16-byte aligned).
+int kl_chunks(int vocab, int dtype_bytes, bool vec);
+// Partials (a persistent grid of `groups` work-groups), finalize, and (if
+// grad != NULL) the gradient pass, on `stream`.  part: rows * chunks * 8
+// floats; lse: rows * 2 floats.
+hipError_t launch_forward_kl(int rows, int vocab, int dtype_bytes, bool vec, const void* target,
+                             const void* draft, float* kl, void* grad, float scale, float* part, float* lse,
+                             int groups, hipStream_t stream);
+
 }  // namespace orthrus

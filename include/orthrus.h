@@ -236,6 +236,37 @@ orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_ca
                                     const int32_t* cand, int32_t* next_anchor, int32_t* tokens,
                                     int32_t* n_tokens, void* stream);
 
+/* Element type of logits for orthrus_forward_kl. */
+typedef enum {
+  ORTHRUS_DTYPE_F32 = 0,
+  ORTHRUS_DTYPE_BF16 = 1
+} orthrus_dtype;
+
+/* Workspace bytes orthrus_forward_kl needs (0 if the sizes are invalid). */
+size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, orthrus_dtype dtype);
+
+/* Forward KL of the diffusion view against the frozen AR model over the whole
+ * vocabulary -- the distillation loss of paper notes §3.1 and §3.3,
+ * KL(P_AR || P_Diff) at every trained position -- and optionally its gradient
+ * with respect to the draft (diffusion) logits.
+ *   target_logits  [rows, V] (dtype)  AR logits; p = softmax(row)
+ *   draft_logits   [rows, V] (dtype)  diffusion logits; q = softmax(row)
+ *   kl    fp32 [rows]       (written) sum_v p_v (ln p_v - ln q_v)
+ *   grad  [rows, V] (dtype) (written; may be NULL) grad_scale * (q_v - p_v),
+ *                           the derivative of kl[n] * grad_scale with respect to
+ *                           draft_logits[n, v]; the AR side is frozen
+ *   workspace  device scratch of at least orthrus_kl_workspace_size bytes,
+ *              owned by the caller; no initialisation needed; calls sharing it
+ *              must not overlap in time.
+ * Logits must be finite; no temperature is applied (the caller scales the
+ * logits for one).  Sums run in fp32 in a fixed order, so results are
+ * deterministic.  Rows are contiguous with stride V; rows up to 65535
+ * (more: ORTHRUS_ERR_UNSUPPORTED).  grad may alias neither input. */
+orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, orthrus_dtype dtype,
+                                  const void* target_logits, const void* draft_logits, float* kl,
+                                  void* grad, float grad_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* orthrus_status_string(orthrus_status s);
 

@@ -272,3 +272,18 @@ def cycle_inputs(w: Workload, n_cycles: int, accept_rate: float = 0.912, device=
         logits, cand, j_star = greedy_inputs(wc, device, first_mismatch=js)
         out.append({"diff": diff, "verify": verify, "logits": logits, "cand": cand, "j_star": j_star})
     return out
+
+
+def kl_inputs(rows: int, vocab: int, sigma: float = 3.0, dtype=torch.float32, seed: int = 0,
+              draft_noise: Optional[float] = None, device="cpu"):
+    """Target (AR) and draft (diffusion) logits [rows, vocab] for the forward-KL
+    loss: target ~ N(0, sigma); draft independent N(0, sigma), or target +
+    N(0, draft_noise) for a draft close to its teacher (late in training).
+    Drawn in float32 and rounded once to ``dtype``."""
+    g = _gen(seed * 7 + 101, device)
+    a = torch.randn((rows, vocab), generator=g, device=device, dtype=torch.float32) * float(sigma)
+    if draft_noise is None:
+        b = torch.randn((rows, vocab), generator=g, device=device, dtype=torch.float32) * float(sigma)
+    else:
+        b = a + torch.randn((rows, vocab), generator=g, device=device, dtype=torch.float32) * float(draft_noise)
+    return a.to(dtype), b.to(dtype)

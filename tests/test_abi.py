@@ -149,6 +149,26 @@ def test_commit_argument_checks(desc, ptrs, expected):
     assert _commit(desc, **ptrs) == expected
 
 
+def test_forward_kl_argument_checks():
+    lib = _lib.load()
+    P, Q, K, G, W = 1 << 40, 2 << 40, 4096, 3 << 40, 8192
+    ok = lib.orthrus_kl_workspace_size(8192, 151936, _lib.ORTHRUS_DTYPE_BF16)
+    assert ok > 0 and lib.orthrus_kl_workspace_size(8192, 151936, 7) == 0
+    assert lib.orthrus_kl_workspace_size(70000, 10, _lib.ORTHRUS_DTYPE_F32) == 0
+    f = lib.orthrus_forward_kl
+    BF = _lib.ORTHRUS_DTYPE_BF16
+    assert f(0, 10, BF, P, Q, K, G, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert f(4, 0, BF, P, Q, K, G, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert f(4, 10, 5, P, Q, K, G, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert f(70000, 10, BF, P, Q, K, G, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert f(4, 10, BF, None, Q, K, G, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert f(4, 10, BF, P, Q, None, G, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert f(4, 10, BF, P, Q, K, G, float("inf"), W, ok, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert f(4, 10, BF, P + 2, Q, K, G, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_MISALIGNED
+    assert f(4, 10, BF, P, Q, K, G + 8, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_MISALIGNED
+    assert f(8192, 151936, BF, P, Q, K, G, 1.0, W, ok - 1, None) == _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_valid_call_without_gpu_reports_hip_error():
     """Run in a child process: a well-formed call on a host with no GPU must
     come back as ORTHRUS_ERR_HIP (validation passed, the launch was refused)."""
