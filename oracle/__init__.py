@@ -15,7 +15,9 @@ What is computed follows the Orthrus pages:
   lengths, emitted tokens, next anchor) and whole synthetic decode cycles --
   ``oracle.cycle``;
 * the training objective's forward KL(P_AR || P_Diff) over the vocabulary and
-  its draft-logit gradient -- ``oracle.kl``.
+  its draft-logit gradient -- ``oracle.kl``;
+* the training-time dual-pass block-mask attention, forward and the backward
+  of the diffusion rows -- ``oracle.train_attn``.
 
 Every function is the plain definition written out in float64 (or exact
 integers), one sequence / head at a time, with explicit masks.  Library
@@ -35,6 +37,7 @@ from .consensus import (greedy_consensus, row_argmax, sample_consensus,
                         tokens_committed)
 from .cycle import bits_to_bf16, commit_block, decode_cycles
 from .kl import forward_kl, forward_kl_rows
+from .train_attn import dual_pass_backward, dual_pass_forward, training_attention_flops
 
 __all__ = [
     "MASK_DIFF_BIDIR", "MASK_VERIFY_CAUSAL", "block_attention",
@@ -42,5 +45,5 @@ __all__ = [
     "row_argmax", "sample_consensus", "accept_prefix", "accepts", "residual_weights",
     "inverse_cdf_pick", "fixed_point_weight", "uniform_to_grid_int",
     "tokens_committed", "bits_to_bf16", "commit_block", "decode_cycles", "forward_kl",
-    "forward_kl_rows",
+    "forward_kl_rows", "dual_pass_forward", "dual_pass_backward", "training_attention_flops",
 ]
