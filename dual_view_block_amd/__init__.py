@@ -10,7 +10,7 @@ paper-notes), §2.1, §3.2 and §4.1 (block attention of both views over the
 shared KV cache), §4.2 (greedy consensus), §4.3 and §7.2 (rejection-sampling
 consensus), §4.1 step 3 (closing the cycle: the verified rows go into the cache,
 the correction becomes the next anchor), §3.3 (the forward-KL distillation loss
-of training).
+of training), §3.1-3.2 (the training-time dual-pass block-mask attention).
 """
 from __future__ import annotations
 
@@ -20,7 +20,7 @@ import torch
 
 from . import _lib
 from ._lib import (ORTHRUS_MASK_DIFF_BIDIR, ORTHRUS_MASK_VERIFY_CAUSAL, AttnDesc, CommitDesc,
-                   OrthrusError, status_string)
+                   OrthrusError, TrainAttnDesc, status_string)
 
 __all__ = [
     "AttnDesc", "OrthrusError", "ORTHRUS_MASK_DIFF_BIDIR", "ORTHRUS_MASK_VERIFY_CAUSAL",
@@ -29,6 +29,7 @@ __all__ = [
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_status_string",
     "PreparedAttention", "PreparedGreedy", "library_path", "CommitDesc", "orthrus_cache_commit",
     "PreparedCommit", "orthrus_kl_workspace_size", "orthrus_forward_kl", "PreparedForwardKL",
+    "TrainAttnDesc", "orthrus_train_attn_fwd",
 ]
 
 
@@ -395,3 +396,58 @@ def orthrus_forward_kl(target_logits, draft_logits, kl=None, grad=None, want_gra
         ws.numel(), _stream_ptr(stream))
     _lib.check("orthrus_forward_kl", st)
     return kl, grad
+
+
+def _check_train(q_ar, k_ar, v_ar, q_diff, k_diff, v_diff, anchors, block_k):
+    if k_ar.dim() != 3:
+        raise ValueError("k_ar must be [Hkv, L, D]")
+    Hkv, L, D = k_ar.shape
+    dev = k_ar.device
+    _need(k_ar, "k_ar", torch.bfloat16, (Hkv, L, D))
+    _need(v_ar, "v_ar", torch.bfloat16, (Hkv, L, D), dev)
+    Hq = None
+    if q_ar is not None:
+        Hq = q_ar.shape[0]
+        _need(q_ar, "q_ar", torch.bfloat16, (Hq, L, D), dev)
+    N = 0
+    if q_diff is not None:
+        Hq = q_diff.shape[0] if Hq is None else Hq
+        N = anchors.shape[0]
+        _need(q_diff, "q_diff", torch.bfloat16, (Hq, N * block_k, D), dev)
+        _need(k_diff, "k_diff", torch.bfloat16, (Hkv, N * block_k, D), dev)
+        _need(v_diff, "v_diff", torch.bfloat16, (Hkv, N * block_k, D), dev)
+        _need(anchors, "anchors", torch.int32, (N,), dev)
+    if Hq is None:
+        raise ValueError("need q_ar or q_diff")
+    return Hq, Hkv, L, D, N
+
+
+def orthrus_train_attn_fwd(q_ar, k_ar, v_ar, q_diff=None, k_diff=None, v_diff=None, anchors=None, block_k=32,
+                           out_ar=None, lse_ar=None, out_diff=None, lse_diff=None, want_lse: bool = True,
+                           softmax_scale: float = 0.0, stream=None):
+    """Training dual-pass attention forward of one packed sequence (head-major
+    bf16 layouts).  q_ar may be None to skip the AR rows, q_diff None for no
+    blocks.  Returns (out_ar, lse_ar, out_diff, lse_diff); absent parts are None."""
+    Hq, Hkv, L, D, N = _check_train(q_ar, k_ar, v_ar, q_diff, k_diff, v_diff, anchors, block_k)
+    dev = k_ar.device
+    if q_ar is not None:
+        out_ar = torch.empty_like(q_ar) if out_ar is None else out_ar
+        _need(out_ar, "out_ar", torch.bfloat16, tuple(q_ar.shape), dev)
+        if lse_ar is None and want_lse:
+            lse_ar = torch.empty((Hq, L), dtype=torch.float32, device=dev)
+    else:
+        out_ar = lse_ar = None
+    if q_diff is not None:
+        out_diff = torch.empty_like(q_diff) if out_diff is None else out_diff
+        _need(out_diff, "out_diff", torch.bfloat16, tuple(q_diff.shape), dev)
+        if lse_diff is None and want_lse:
+            lse_diff = torch.empty((Hq, N * block_k), dtype=torch.float32, device=dev)
+    else:
+        out_diff = lse_diff = None
+    desc = TrainAttnDesc(L, N, block_k, Hq, Hkv, D, float(softmax_scale))
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    st = _lib.load().orthrus_train_attn_fwd(
+        ctypes.byref(desc), ptr(q_ar), k_ar.data_ptr(), v_ar.data_ptr(), ptr(q_diff), ptr(k_diff), ptr(v_diff),
+        ptr(anchors), ptr(out_ar), ptr(lse_ar), ptr(out_diff), ptr(lse_diff), _stream_ptr(stream))
+    _lib.check("orthrus_train_attn_fwd", st)
+    return out_ar, lse_ar, out_diff, lse_diff

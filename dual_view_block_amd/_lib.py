@@ -31,7 +31,7 @@ EXPORTS = (
     "orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_block_attn_partial",
     "orthrus_block_attn_merge", "orthrus_consensus_workspace_size",
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_cache_commit",
-    "orthrus_kl_workspace_size", "orthrus_forward_kl", "orthrus_status_string",
+    "orthrus_kl_workspace_size", "orthrus_forward_kl", "orthrus_train_attn_fwd", "orthrus_status_string",
 )
 
 
@@ -55,6 +55,18 @@ class CommitDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("block_k", ctypes.c_int32),
         ("max_len", ctypes.c_int32),
+    ]
+
+
+class TrainAttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("seq_len", ctypes.c_int32),
+        ("n_blocks", ctypes.c_int32),
+        ("block_k", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
     ]
 
 
@@ -84,6 +96,7 @@ _SIGS = {
                                     _P, _P]),
     "orthrus_kl_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "orthrus_forward_kl": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _SZ, _P]),
+    "orthrus_train_attn_fwd": (_I32, [ctypes.POINTER(TrainAttnDesc)] + [_P] * 12),
     "orthrus_status_string": (ctypes.c_char_p, [_I32]),
 }
 

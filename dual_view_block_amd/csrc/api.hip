@@ -122,6 +122,7 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.head_dim = d->head_dim;
   a.max_len = d->max_len;
   a.causal = mode == ORTHRUS_MASK_VERIFY_CAUSAL ? 1 : 0;
+  set_decode_strides(a);
   a.splits = attn_launch_splits(plan, d->batch, d->n_kv_heads, d->max_len, cus);
   const int cap = env_int("ORTHRUS_MAX_SPLITS", a.splits);  // tuning: may only lower the split count
   if (cap < a.splits) a.splits = cap;
@@ -199,6 +200,54 @@ KlPlan make_kl_plan(int32_t rows, int32_t vocab, int dtype) {
   p.lse_bytes = round_up((size_t)rows * 2 * sizeof(float), kAlign);
   p.ws_bytes = p.part_bytes + p.lse_bytes;
   return p;
+}
+
+// Rows of the AR (clean, causal) part are processed in groups of this many:
+// group m is a verify-mode block of rows [32m, 32m+32) over the cache [0, 32m).
+constexpr int kTrainArGroup = 32;
+
+orthrus_status check_train_desc(const orthrus_train_attn_desc* d) {
+  if (d == nullptr) return ORTHRUS_ERR_NULL_PTR;
+  if (d->seq_len < 1 || d->n_blocks < 0 || d->block_k < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 ||
+      d->head_dim < 1)
+    return ORTHRUS_ERR_BAD_SHAPE;
+  if (d->n_q_heads % d->n_kv_heads != 0) return ORTHRUS_ERR_BAD_SHAPE;
+  if (!(isfinite(d->softmax_scale) && d->softmax_scale >= 0.0f)) return ORTHRUS_ERR_BAD_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return ORTHRUS_ERR_UNSUPPORTED;
+  if (d->block_k > 32 || d->seq_len % kTrainArGroup != 0) return ORTHRUS_ERR_UNSUPPORTED;
+  const long long G = d->n_q_heads / d->n_kv_heads;
+  if (G * 32 > (1LL << 20)) return ORTHRUS_ERR_BAD_SHAPE;
+  if ((long long)(d->seq_len / kTrainArGroup) * d->n_kv_heads > 65535LL ||
+      (long long)d->n_blocks * d->n_kv_heads > 65535LL)
+    return ORTHRUS_ERR_BAD_SHAPE;
+  return ORTHRUS_OK;
+}
+
+// One single-split block-attention launch of the training forward.
+orthrus_status run_train_part(const orthrus_train_attn_desc* d, int batch, int block_k, int causal,
+                              AttnArgs a, void* stream) {
+  orthrus_attn_desc ad{};
+  ad.batch = batch;
+  ad.n_q_heads = d->n_q_heads;
+  ad.n_kv_heads = d->n_kv_heads;
+  ad.head_dim = d->head_dim;
+  ad.block_k = block_k;
+  ad.max_len = d->seq_len;
+  ad.softmax_scale = d->softmax_scale;
+  const AttnPlan plan = make_plan(&ad);
+  a.batch = batch;
+  a.n_q_heads = d->n_q_heads;
+  a.n_kv_heads = d->n_kv_heads;
+  a.group = d->n_q_heads / d->n_kv_heads;
+  a.block_k = block_k;
+  a.head_dim = d->head_dim;
+  a.max_len = d->seq_len;
+  a.causal = causal;
+  a.splits = 1;  // every work-group streams its whole prefix and writes its rows itself
+  const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = launch_block_attention(a, plan, 3, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 
 // true if the byte ranges [p, p+n) and [q, q+m) overlap
@@ -360,6 +409,72 @@ orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, orthrus_dtype dty
                                          reinterpret_cast<float*>(ws + plan.part_bytes), kKlWgPerCu * cus,
                                          reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status orthrus_train_attn_fwd(const orthrus_train_attn_desc* d, const uint16_t* q_ar,
+                                      const uint16_t* k_ar, const uint16_t* v_ar, const uint16_t* q_diff,
+                                      const uint16_t* k_diff, const uint16_t* v_diff, const int32_t* anchors,
+                                      uint16_t* out_ar, float* lse_ar, uint16_t* out_diff, float* lse_diff,
+                                      void* stream) {
+  const orthrus_status st = check_train_desc(d);
+  if (st != ORTHRUS_OK) return st;
+  const bool ar = q_ar != nullptr || out_ar != nullptr;
+  const bool diff = d->n_blocks > 0;
+  if (!k_ar || !v_ar) return ORTHRUS_ERR_NULL_PTR;
+  if (ar && (!q_ar || !out_ar)) return ORTHRUS_ERR_NULL_PTR;
+  if (diff && (!q_diff || !k_diff || !v_diff || !anchors || !out_diff)) return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(k_ar) || !aligned16(v_ar) || (ar && (!aligned16(q_ar) || !aligned16(out_ar))) ||
+      (lse_ar && !aligned4(lse_ar)) ||
+      (diff && (!aligned16(q_diff) || !aligned16(k_diff) || !aligned16(v_diff) || !aligned4(anchors) ||
+                !aligned16(out_diff) || (lse_diff && !aligned4(lse_diff)))))
+    return ORTHRUS_ERR_MISALIGNED;
+  if (device_cus() < 1) return ORTHRUS_ERR_HIP;
+  const long long D = d->head_dim, L = d->seq_len, K = d->block_k, NK = (long long)d->n_blocks * d->block_k;
+  if (ar) {  // clean rows: groups of 32 causal rows over the clean prefix before the group
+    AttnArgs a{};
+    a.q = q_ar;
+    a.k_blk = k_ar;
+    a.v_blk = v_ar;
+    a.k_cache = k_ar;
+    a.v_cache = v_ar;
+    a.cache_len = nullptr;
+    a.out = out_ar;
+    a.lse = lse_ar;
+    a.q_bs = a.o_bs = kTrainArGroup * D;
+    a.q_hs = a.o_hs = L * D;
+    a.l_bs = kTrainArGroup;
+    a.l_hs = L;
+    a.blk_bs = kTrainArGroup * D;
+    a.blk_gs = L * D;
+    a.c_bs = 0;
+    a.c_gs = L * D;
+    a.len_step = kTrainArGroup;
+    const orthrus_status r = run_train_part(d, (int)(L / kTrainArGroup), kTrainArGroup, 1, a, stream);
+    if (r != ORTHRUS_OK) return r;
+  }
+  if (diff) {  // block n: clean prefix [0, anchors[n]) shared by all blocks, plus its own K keys
+    AttnArgs a{};
+    a.q = q_diff;
+    a.k_blk = k_diff;
+    a.v_blk = v_diff;
+    a.k_cache = k_ar;
+    a.v_cache = v_ar;
+    a.cache_len = anchors;
+    a.out = out_diff;
+    a.lse = lse_diff;
+    a.q_bs = a.o_bs = K * D;
+    a.q_hs = a.o_hs = NK * D;
+    a.l_bs = K;
+    a.l_hs = NK;
+    a.blk_bs = K * D;
+    a.blk_gs = NK * D;
+    a.c_bs = 0;
+    a.c_gs = L * D;
+    a.len_step = 0;
+    const orthrus_status r = run_train_part(d, d->n_blocks, (int)K, 0, a, stream);
+    if (r != ORTHRUS_OK) return r;
+  }
+  return ORTHRUS_OK;
 }
 
 const char* orthrus_status_string(orthrus_status s) {

@@ -98,7 +98,7 @@ struct SplitRange {
 
 __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int split) {
   SplitRange r;
-  int L = a.cache_len[b];
+  int L = a.len_step > 0 ? b * a.len_step : a.cache_len[b];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int S = a.splits;
   int chunk = (L + S - 1) / S;
@@ -183,13 +183,14 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
   }
   if (myrow < row_end) {
     const int rg = grp % p.row_groups;
-    const int r = rg * p.rows_per_wg + myrow;  // row inside the (b, g) group
+    const int r = rg * p.rows_per_wg + myrow;  // row inside the (b, g) group: head_in_group*K + i
     if (r < p.rows) {
-      const size_t orow = (size_t)(grp / p.row_groups) * p.rows + r;  // == (b*Hq + g*G)*K + r
+      const int bg = grp / p.row_groups;
+      const int b = bg / a.n_kv_heads, h = (bg % a.n_kv_heads) * a.group + r / a.block_k, i = r % a.block_k;
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       const uint32_t o = (uint32_t)to_bf16_bits(acc0 * inv) | ((uint32_t)to_bf16_bits(acc1 * inv) << 16);
-      *reinterpret_cast<uint32_t*>(a.out + orow * D + 2 * j) = o;
-      if (a.lse != nullptr && j == 0) a.lse[orow] = (M + log2f(L)) * kLn2;
+      *reinterpret_cast<uint32_t*>(a.out + b * a.o_bs + h * a.o_hs + (long long)i * D + 2 * j) = o;
+      if (a.lse != nullptr && j == 0) a.lse[b * a.l_bs + h * a.l_hs + i] = (M + log2f(L)) * kLn2;
     }
   }
 }
@@ -224,7 +225,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   const int R = plan.rows;
   const int K = a.block_k;
   const SplitRange sr = split_range(a, b, split);
-  const size_t row_base = (size_t)bg * R;  // first output row of the (b, g) group
+  const int g = bg % a.n_kv_heads;
+  // q / out / lse element offset of row r (= head_in_group * K + i) of the (b, g) group
+  const long long q_grp = b * a.q_bs + (long long)g * a.group * a.q_hs;
+  const long long o_grp = b * a.o_bs + (long long)g * a.group * a.o_hs;
+  const long long l_grp = b * a.l_bs + (long long)g * a.group * a.l_hs;
 
   // ---- this lane's query row (the N index of every MFMA it joins)
   const int wrow = qb * 32 + (lane & 31);         // row inside the work-group block
@@ -251,11 +256,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   }
   // tiles [0, nfull) are whole cache tiles: no masking, no row clamping
   const int nfull = min((sr.kend - sr.kstart) / kTileKeys, sr.ncache);
-  const size_t split_off = ((size_t)bg * a.max_len + sr.kstart) * D;
+  const long long split_off = b * a.c_bs + g * a.c_gs + (long long)sr.kstart * D;
   const uint8_t* kc0 = reinterpret_cast<const uint8_t*>(a.k_cache + split_off);  // tile 0 of this split
   const uint8_t* vc0 = reinterpret_cast<const uint8_t*>(a.v_cache + split_off);
-  const uint8_t* kblk = reinterpret_cast<const uint8_t*>(a.k_blk + (size_t)bg * K * D);
-  const uint8_t* vblk = reinterpret_cast<const uint8_t*>(a.v_blk + (size_t)bg * K * D);
+  const long long blk_off = b * a.blk_bs + g * a.blk_gs;
+  const uint8_t* kblk = reinterpret_cast<const uint8_t*>(a.k_blk + blk_off);
+  const uint8_t* vblk = reinterpret_cast<const uint8_t*>(a.v_blk + blk_off);
   typedef u32x4 Stage[2 * CPT];  // K chunks, then V chunks
   auto load_tile = [&](int t, Stage& r) __attribute__((always_inline)) {
     const bool whole = t < nfull;
@@ -430,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   Stage stg0, stg1;  // at iteration t: tiles t+2 and t+3 (in flight or landed)
   {
     const int row = min(rg * plan.rows_per_wg + wrow, R - 1);
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + (row_base + row) * D);
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + q_grp + (row / K) * a.q_hs + (long long)(row % K) * D);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) qf[ds] = active ? qp[2 * ds + half] : bf16x8{};
   }
@@ -592,14 +598,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * OPITCH + ch * 16);
     if (one_split) {
       const int gr = rg * plan.rows_per_wg + r;  // row inside the (b, g) group
-      if (gr < R) *reinterpret_cast<u32x4*>(a.out + (row_base + gr) * D + ch * 8) = v;
+      if (gr < R)
+        *reinterpret_cast<u32x4*>(a.out + o_grp + (gr / K) * a.o_hs + (long long)(gr % K) * D + ch * 8) = v;
     } else {
       *reinterpret_cast<u32x4*>(a.ws_acc + (slot * plan.rows_per_wg + r) * D + ch * 8) = v;
     }
   }
   if (active && half == 0) {
     if (one_split) {
-      if (a.lse != nullptr && qrow < R) a.lse[row_base + qrow] = (m_out + log2f(l_row)) * kLn2;
+      if (a.lse != nullptr && qrow < R) a.lse[l_grp + (qrow / K) * a.l_hs + qrow % K] = (m_out + log2f(l_row)) * kLn2;
     } else {
       float2 ml;
       ml.x = m_out;

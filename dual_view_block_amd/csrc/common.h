@@ -45,7 +45,32 @@ struct AttnArgs {
   int causal;
   int splits;        // splits of this launch (<= plan.splits)
   float scale_log2;  // softmax scale * log2(e)
+  // Element strides.  Block row i of q head h in sequence b is at
+  // q + b*q_bs + h*q_hs + i*head_dim (out likewise with o_*, lse with l_*, in
+  // elements of lse); block key j of KV head g at k_blk + b*blk_bs + g*blk_gs
+  // + j*head_dim; cache row r at k_cache + b*c_bs + g*c_gs + r*head_dim.
+  // The decode layouts are the contiguous ones; c_bs = 0 shares one cache
+  // between all sequences.
+  long long q_bs, q_hs, o_bs, o_hs, l_bs, l_hs, blk_bs, blk_gs, c_bs, c_gs;
+  // > 0: sequence b attends to cache rows [0, b*len_step) and cache_len is
+  // not read (causal rows processed in groups of block_k)
+  int len_step;
 };
+
+// Contiguous decode layouts: q/out [B,Hq,K,D], lse [B,Hq,K], blocks
+// [B,Hkv,K,D], caches [B,Hkv,max_len,D].
+inline void set_decode_strides(AttnArgs& a) {
+  const long long D = a.head_dim, K = a.block_k;
+  a.q_hs = a.o_hs = K * D;
+  a.q_bs = a.o_bs = (long long)a.n_q_heads * K * D;
+  a.l_hs = K;
+  a.l_bs = (long long)a.n_q_heads * K;
+  a.blk_gs = K * D;
+  a.blk_bs = (long long)a.n_kv_heads * K * D;
+  a.c_gs = (long long)a.max_len * D;
+  a.c_bs = (long long)a.n_kv_heads * a.max_len * D;
+  a.len_step = 0;
+}
 
 // Splits a launch uses on a device with `cus` compute units.
 int attn_launch_splits(const AttnPlan& plan, int batch, int n_kv_heads, int max_len, int cus);

@@ -267,6 +267,43 @@ orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, orthrus_dtype dty
                                   void* grad, float grad_scale, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Shapes of the training-time dual-pass attention of one packed sequence. */
+typedef struct {
+  int32_t seq_len;      /* L clean positions; a multiple of 32 */
+  int32_t n_blocks;     /* N anchor blocks (0: AR rows only) */
+  int32_t block_k;      /* K positions per block, 1..32 */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* Hkv; q head h reads KV head h / (Hq / Hkv) */
+  int32_t head_dim;     /* D, 64 or 128 */
+  float softmax_scale;  /* 0 -> 1/sqrt(D) */
+} orthrus_train_attn_desc;
+
+/* Forward of the dual-pass block-mask attention used to train the diffusion
+ * view (paper notes §3.1-3.2): one packed sequence of L clean tokens carries
+ * N anchor blocks of K positions.  In one softmax per row:
+ *   AR row i (clean position i) attends to clean keys 0..i (causal);
+ *   diffusion row p of block n attends to the clean keys before the block's
+ *   anchor, [0, anchors[n]), and to the K diffusion keys of block n
+ *   (bidirectionally); blocks never see each other.
+ * Layouts are head-major, bf16:
+ *   q_ar [Hq, L, D], k_ar / v_ar [Hkv, L, D]      the AR path's q and the
+ *                                                 clean keys/values
+ *   q_diff [Hq, N*K, D], k_diff / v_diff [Hkv, N*K, D]   block n holds rows
+ *                                                 n*K .. n*K+K-1
+ *   anchors int32 [N] on the device (clamped to [0, L])
+ *   out_ar [Hq, L, D], lse_ar fp32 [Hq, L] (may be NULL)
+ *   out_diff [Hq, N*K, D], lse_diff fp32 [Hq, N*K] (may be NULL; the
+ *   backward needs it)
+ * lse is the natural-log normaliser of each row.  q_ar and out_ar may both be
+ * NULL to skip the AR rows.  No workspace: every work-group streams its
+ * row's whole prefix.  Asynchronous on `stream`. */
+orthrus_status orthrus_train_attn_fwd(const orthrus_train_attn_desc* d, const uint16_t* q_ar,
+                                      const uint16_t* k_ar, const uint16_t* v_ar,
+                                      const uint16_t* q_diff, const uint16_t* k_diff,
+                                      const uint16_t* v_diff, const int32_t* anchors,
+                                      uint16_t* out_ar, float* lse_ar, uint16_t* out_diff,
+                                      float* lse_diff, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* orthrus_status_string(orthrus_status s);
 

@@ -287,3 +287,27 @@ def kl_inputs(rows: int, vocab: int, sigma: float = 3.0, dtype=torch.float32, se
     else:
         b = a + torch.randn((rows, vocab), generator=g, device=device, dtype=torch.float32) * float(draft_noise)
     return a.to(dtype), b.to(dtype)
+
+
+def train_attn_inputs(n_q_heads: int, n_kv_heads: int, seq_len: int, n_blocks: int, block_k: int,
+                      head_dim: int, seed: int = 0, device="cpu", anchors=None):
+    """One packed training sequence for the dual-pass attention: head-major
+    bf16 N(0, 1) q/k/v of the clean path ([H, L, D]) and of the diffusion
+    blocks ([H, N*K, D]), and N anchor positions drawn uniformly from
+    [0, L - K] (the pages sample 256 random anchors per 2048-token sequence)."""
+    g = _gen(seed * 613 + 29, device)
+    Hq, Hkv, L, N, K, D = n_q_heads, n_kv_heads, seq_len, n_blocks, block_k, head_dim
+    out = {
+        "q_ar": _randn_bf16((Hq, L, D), g, device),
+        "k_ar": _randn_bf16((Hkv, L, D), g, device),
+        "v_ar": _randn_bf16((Hkv, L, D), g, device),
+        "q_diff": _randn_bf16((Hq, N * K, D), g, device),
+        "k_diff": _randn_bf16((Hkv, N * K, D), g, device),
+        "v_diff": _randn_bf16((Hkv, N * K, D), g, device),
+    }
+    if anchors is None:
+        ga = _gen(seed * 613 + 30, "cpu")
+        anchors = torch.randint(0, max(L - K, 0) + 1, (N,), generator=ga)
+    out["anchors"] = torch.as_tensor(anchors, dtype=torch.int32).to(device)
+    out["block_k"] = K
+    return out
