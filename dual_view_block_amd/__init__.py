@@ -29,7 +29,7 @@ __all__ = [
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_status_string",
     "PreparedAttention", "PreparedGreedy", "library_path", "CommitDesc", "orthrus_cache_commit",
     "PreparedCommit", "orthrus_kl_workspace_size", "orthrus_forward_kl", "PreparedForwardKL",
-    "TrainAttnDesc", "orthrus_train_attn_fwd",
+    "TrainAttnDesc", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd",
 ]
 
 
@@ -451,3 +451,27 @@ def orthrus_train_attn_fwd(q_ar, k_ar, v_ar, q_diff=None, k_diff=None, v_diff=No
         ptr(anchors), ptr(out_ar), ptr(lse_ar), ptr(out_diff), ptr(lse_diff), _stream_ptr(stream))
     _lib.check("orthrus_train_attn_fwd", st)
     return out_ar, lse_ar, out_diff, lse_diff
+
+
+def orthrus_train_attn_bwd(k_ar, v_ar, q_diff, k_diff, v_diff, anchors, block_k, out_diff, lse_diff, d_out_diff,
+                           dq=None, dk=None, dv=None, softmax_scale: float = 0.0, stream=None):
+    """Backward of the diffusion rows of the training dual-pass attention.
+    Returns (dq_diff [Hq,N*K,D], dk_diff [Hkv,N*K,D], dv_diff [Hkv,N*K,D]) bf16."""
+    Hq, Hkv, L, D, N = _check_train(None, k_ar, v_ar, q_diff, k_diff, v_diff, anchors, block_k)
+    dev = k_ar.device
+    _need(out_diff, "out_diff", torch.bfloat16, tuple(q_diff.shape), dev)
+    _need(lse_diff, "lse_diff", torch.float32, (Hq, N * block_k), dev)
+    _need(d_out_diff, "d_out_diff", torch.bfloat16, tuple(q_diff.shape), dev)
+    dq = torch.empty_like(q_diff) if dq is None else dq
+    dk = torch.empty_like(k_diff) if dk is None else dk
+    dv = torch.empty_like(v_diff) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, tuple(q_diff.shape), dev)
+    _need(dk, "dk", torch.bfloat16, tuple(k_diff.shape), dev)
+    _need(dv, "dv", torch.bfloat16, tuple(v_diff.shape), dev)
+    desc = TrainAttnDesc(L, N, block_k, Hq, Hkv, D, float(softmax_scale))
+    st = _lib.load().orthrus_train_attn_bwd(
+        ctypes.byref(desc), k_ar.data_ptr(), v_ar.data_ptr(), q_diff.data_ptr(), k_diff.data_ptr(),
+        v_diff.data_ptr(), anchors.data_ptr(), out_diff.data_ptr(), lse_diff.data_ptr(), d_out_diff.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream_ptr(stream))
+    _lib.check("orthrus_train_attn_bwd", st)
+    return dq, dk, dv

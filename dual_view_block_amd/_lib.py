@@ -31,7 +31,8 @@ EXPORTS = (
     "orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_block_attn_partial",
     "orthrus_block_attn_merge", "orthrus_consensus_workspace_size",
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_cache_commit",
-    "orthrus_kl_workspace_size", "orthrus_forward_kl", "orthrus_train_attn_fwd", "orthrus_status_string",
+    "orthrus_kl_workspace_size", "orthrus_forward_kl", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd",
+    "orthrus_status_string",
 )
 
 
@@ -97,6 +98,7 @@ _SIGS = {
     "orthrus_kl_workspace_size": (_SZ, [_I32, _I32, _I32]),
     "orthrus_forward_kl": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _SZ, _P]),
     "orthrus_train_attn_fwd": (_I32, [ctypes.POINTER(TrainAttnDesc)] + [_P] * 12),
+    "orthrus_train_attn_bwd": (_I32, [ctypes.POINTER(TrainAttnDesc)] + [_P] * 13),
     "orthrus_status_string": (ctypes.c_char_p, [_I32]),
 }
 

@@ -477,6 +477,48 @@ orthrus_status orthrus_train_attn_fwd(const orthrus_train_attn_desc* d, const ui
   return ORTHRUS_OK;
 }
 
+orthrus_status orthrus_train_attn_bwd(const orthrus_train_attn_desc* d, const uint16_t* k_ar,
+                                      const uint16_t* v_ar, const uint16_t* q_diff, const uint16_t* k_diff,
+                                      const uint16_t* v_diff, const int32_t* anchors, const uint16_t* out_diff,
+                                      const float* lse_diff, const uint16_t* d_out_diff, uint16_t* dq_diff,
+                                      uint16_t* dk_diff, uint16_t* dv_diff, void* stream) {
+  const orthrus_status st = check_train_desc(d);
+  if (st != ORTHRUS_OK) return st;
+  if ((long long)(d->n_q_heads / d->n_kv_heads) * d->block_k > 128) return ORTHRUS_ERR_UNSUPPORTED;
+  if (d->n_blocks == 0) return ORTHRUS_OK;
+  if (!k_ar || !v_ar || !q_diff || !k_diff || !v_diff || !anchors || !out_diff || !lse_diff || !d_out_diff ||
+      !dq_diff || !dk_diff || !dv_diff)
+    return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(k_ar) || !aligned16(v_ar) || !aligned16(q_diff) || !aligned16(k_diff) || !aligned16(v_diff) ||
+      !aligned4(anchors) || !aligned16(out_diff) || !aligned4(lse_diff) || !aligned16(d_out_diff) ||
+      !aligned16(dq_diff) || !aligned16(dk_diff) || !aligned16(dv_diff))
+    return ORTHRUS_ERR_MISALIGNED;
+  if (device_cus() < 1) return ORTHRUS_ERR_HIP;
+  TrainBwdArgs a{};
+  a.k_ar = k_ar;
+  a.v_ar = v_ar;
+  a.q_diff = q_diff;
+  a.k_diff = k_diff;
+  a.v_diff = v_diff;
+  a.anchors = anchors;
+  a.out_diff = out_diff;
+  a.lse_diff = lse_diff;
+  a.d_out = d_out_diff;
+  a.dq = dq_diff;
+  a.dk = dk_diff;
+  a.dv = dv_diff;
+  a.seq_len = d->seq_len;
+  a.n_blocks = d->n_blocks;
+  a.block_k = d->block_k;
+  a.group = d->n_q_heads / d->n_kv_heads;
+  a.n_kv_heads = d->n_kv_heads;
+  a.head_dim = d->head_dim;
+  a.scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  const hipError_t e = launch_train_bwd(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
 const char* orthrus_status_string(orthrus_status s) {
   switch (s) {
     case ORTHRUS_OK: return "ORTHRUS_OK";

@@ -100,6 +100,29 @@ hipError_t launch_consensus_sample(int batch, int block_k, int vocab, const floa
                                    int32_t* correction, void* workspace,
                                    const ConsensusPlan& plan, hipStream_t stream);
 
+// ---------------------------------------------------------------- training backward
+// Diffusion-row backward of the dual-pass training attention, head-major
+// layouts: q/out/d_out/dq [Hq, N*K, D], k/v/dk/dv_diff [Hkv, N*K, D],
+// k/v_ar [Hkv, L, D], lse_diff [Hq, N*K] (natural log), anchors [N].
+struct TrainBwdArgs {
+  const uint16_t* k_ar;
+  const uint16_t* v_ar;
+  const uint16_t* q_diff;
+  const uint16_t* k_diff;
+  const uint16_t* v_diff;
+  const int32_t* anchors;
+  const uint16_t* out_diff;
+  const float* lse_diff;
+  const uint16_t* d_out;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int seq_len, n_blocks, block_k, group, n_kv_heads, head_dim;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+};
+hipError_t launch_train_bwd(const TrainBwdArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- commit
 // Row copies of the verified block into the cache, then the in-place state
 // update (two launches on `stream`).

@@ -1,0 +1,385 @@
+// Backward of the training dual-pass block-mask attention for the diffusion
+// rows (Orthrus paper notes §3.1-3.2; the AR backbone is frozen, so only the
+// diffusion queries, keys and values get gradients).
+//
+// For every anchor block n and KV head g, the G*K diffusion rows of the q
+// heads that share g attend to the clean keys [0, a_n) and to the K keys of
+// block n.  With the forward's log-sum-exp per row, P = exp(scale*QK^T - lse)
+// is recomputed exactly, and
+//   dP = dO V^T,  D_i = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale * dS K          (over every key of the row)
+//   dV_blk = P_blk^T dO,  dK_blk = scale * dS_blk^T Q   (block keys; the sum
+//                                                          over rows covers all G heads)
+//
+// One work-group of 4 waves per (block, KV head); wave w owns rows
+// 32w..32w+31 (each lane one row, as in the streaming kernel).  Per 64-key
+// tile, with the tile in LDS:
+//   S^T  = K Q^T      (A = K rows, B = Q fragments in registers)
+//   dP^T = V dO^T     (A = V rows, B = dO fragments in registers)
+//   dS^T = P^T * (dP^T - D) elementwise, rounded to bf16 in place
+//   dQ^T += K^T dS^T  (A = K^T through the transposing LDS read)
+// all on v_mfma_f32_32x32x16_bf16.  K is kept in LDS twice, once in the
+// layout the row reads want and once in the layout the transposing read
+// wants, and V once in the row-read layout, so no read conflicts.  Tiles come
+// in through registers one tile ahead into a 2-stage LDS ring (one barrier
+// per tile).  After the last (block) tile the waves put P_blk, dS_blk, Q and
+// dO in LDS and wave w forms dV_blk and dK_blk for head_dim block w with the
+// row sum as the MFMA contraction.
+#include "attn_frag.h"
+#include "common.h"
+
+#include <math.h>
+
+namespace orthrus {
+namespace {
+
+using namespace frag;
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdTile = 64;
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads, 1) void train_bwd_kernel(const TrainBwdArgs a) {
+  constexpr int DCH = D / 8;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = kBwdTile * ROWB;
+  constexpr int SLOT_KK = 0, SLOT_KV = TILEB, SLOT_VK = 2 * TILEB;  // K row layout, K^T layout, V row layout
+  constexpr int STAGEB = 3 * TILEB;
+  constexpr int HALFB = 32 * ROWB;
+  constexpr int NDS = D / 16;
+  constexpr int NMB = D / 32;
+  constexpr int CPT = kBwdTile * DCH / kBwdThreads;
+  static_assert(CPT >= 1, "tile too small for the work-group");
+
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGEB];
+
+  const int n = blockIdx.x;   // anchor block
+  const int g = blockIdx.y;   // KV head
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int qb = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int K = a.block_k;
+  const int R = a.group * K;
+  const int wrow = qb * 32 + (lane & 31);  // this lane's row: head_in_group * K + i
+  const bool active = wrow < R;
+  const int hh = active ? wrow / K : 0, ii = active ? wrow % K : 0;
+  const long long NK = (long long)a.n_blocks * K;
+  // element offset of this lane's row in the [Hq, N*K, D] arrays
+  const long long row_off = ((long long)(g * a.group + hh) * NK + (long long)n * K + ii) * D;
+  int La = a.anchors[n];
+  La = La < 0 ? 0 : (La > a.seq_len ? a.seq_len : La);
+  const int ncache = (La + kBwdTile - 1) / kBwdTile;
+  const int ntiles = ncache + 1;  // + the block tile
+
+  // ---- tile copies through registers (thread tid moves chunks tid + c*256)
+  int crow[CPT];
+  uint32_t cchunk[CPT], dkk[CPT], dkv[CPT], dvk[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int m = tid + c * kBwdThreads;
+    crow[c] = m / DCH;
+    const int ch = m % DCH;
+    cchunk[c] = (uint32_t)ch * 16;
+    dkk[c] = (uint32_t)(SLOT_KK + crow[c] * ROWB + swz_k<DCH>(crow[c], ch) * 16);
+    dkv[c] = (uint32_t)(SLOT_KV + crow[c] * ROWB + swz_v<DCH>(crow[c], ch) * 16);
+    dvk[c] = (uint32_t)(SLOT_VK + crow[c] * ROWB + swz_k<DCH>(crow[c], ch) * 16);
+  }
+  const uint8_t* kc0 = reinterpret_cast<const uint8_t*>(a.k_ar + (long long)g * a.seq_len * D);
+  const uint8_t* vc0 = reinterpret_cast<const uint8_t*>(a.v_ar + (long long)g * a.seq_len * D);
+  const long long blk_off = ((long long)g * NK + (long long)n * K) * D;
+  const uint8_t* kb0 = reinterpret_cast<const uint8_t*>(a.k_diff + blk_off);
+  const uint8_t* vb0 = reinterpret_cast<const uint8_t*>(a.v_diff + blk_off);
+  typedef u32x4 Stage[2 * CPT];
+  // Rows past the valid count re-read the last valid row (finite data; their
+  // scores are masked to -inf, so P = 0 exactly).
+  auto load_tile = [&](int t, Stage& r) __attribute__((always_inline)) {
+    const bool blk = t == ncache;
+    const int last = blk ? K - 1 : min(kBwdTile, La - t * kBwdTile) - 1;
+    const uint8_t* kp = blk ? kb0 : kc0 + (size_t)t * TILEB;
+    const uint8_t* vp = blk ? vb0 : vc0 + (size_t)t * TILEB;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const uint32_t off = (uint32_t)(min(crow[c], last) * ROWB) + cchunk[c];
+      r[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + off));
+      r[CPT + c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + off));
+    }
+  };
+  auto store_tile = [&](int stage, const Stage& r) __attribute__((always_inline)) {
+    uint8_t* sb = smem + stage * STAGEB;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      *reinterpret_cast<u32x4*>(sb + dkk[c]) = r[c];
+      *reinterpret_cast<u32x4*>(sb + dkv[c]) = r[c];
+      *reinterpret_cast<u32x4*>(sb + dvk[c]) = r[CPT + c];
+    }
+  };
+
+  // ---- this lane's row: Q and dO fragments (B operands), O, lse, D_i
+  bf16x8 qf[NDS], df[NDS];
+  float di = 0.0f;
+  {
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q_diff + row_off);
+    const bf16x8* gp = reinterpret_cast<const bf16x8*>(a.d_out + row_off);
+    const bf16x8* op = reinterpret_cast<const bf16x8*>(a.out_diff + row_off);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      qf[ds] = active ? qp[2 * ds + half] : bf16x8{};
+      df[ds] = active ? gp[2 * ds + half] : bf16x8{};
+      const bf16x8 o = active ? op[2 * ds + half] : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) di = fmaf((float)df[ds][e], (float)o[e], di);
+    }
+    di += __shfl_xor(di, 32);
+  }
+  // P = 2^(s*c2 - m2) with m2 = lse * log2(e); inactive rows get P = 0
+  const float c2 = a.scale_log2;
+  const float m2 = active ? a.lse_diff[((long long)(g * a.group + hh) * NK + (long long)n * K + ii)] *
+                                1.4426950408889634f
+                          : __builtin_inff();
+
+  const int grp16 = lane >> 4;
+  const int jj = (lane & 15) >> 2;
+  const int qq = lane & 3;
+  const int krow = lane & 31;
+  // row-layout reads (K and V as A operands): both 32-key halves
+  auto load_rows = [&](int base_slot, int stage, bf16x8 (&f)[2][NDS]) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(stage * STAGEB + base_slot + krow * ROWB) + 16u * (uint32_t)swz_k<DCH>(krow, half);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const uint8_t* p = smem + (base ^ (32u * ds));
+      f[0][ds] = *reinterpret_cast<const bf16x8*>(p);
+      f[1][ds] = *reinterpret_cast<const bf16x8*>(p + HALFB);
+    }
+  };
+  // transposed reads of the K^T layout: keys in the S^T accumulator order
+  uint32_t tbase[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+    const int key0 = 4 * half + jj;
+    const int d0 = 32 * mb + 16 * (grp16 & 1) + 4 * qq;
+    tbase[mb] = (uint32_t)(SLOT_KV + key0 * ROWB + swz_v<DCH>(key0, d0 >> 3) * 16 + (d0 & 7) * 2);
+  }
+  typedef bf16x8 TFrag[2][2][NMB];
+  auto load_kt = [&](int stage, TFrag& tf) __attribute__((always_inline)) {
+    uint32_t tb[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      tb[mb] = (uint32_t)(stage * STAGEB) + tbase[mb];
+      asm("" : "+v"(tb[mb]));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const uint8_t* pa = smem + tb[mb] + h * HALFB + (16 * tt) * ROWB;
+          const bf16x4 x0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa)));
+          const bf16x4 x1 =
+              __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa + 8 * ROWB)));
+          tf[h][tt][mb] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+  };
+
+  f32x16 dq[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[mb][r] = 0.0f;
+  bf16x8 pblk[2], dsblk[2];  // block tile, keys 0..31: P^T and dS^T in bf16 (k-steps 0, 1)
+
+  Stage stg;
+  load_tile(0, stg);
+  store_tile(0, stg);
+  if (ntiles > 1) load_tile(1, stg);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    if (t + 1 < ntiles) {
+      store_tile(st ^ 1, stg);  // readers of that stage finished before the last barrier
+      if (t + 2 < ntiles) load_tile(t + 2, stg);
+    }
+    const bool blk = t == ncache;
+    const int nvalid = blk ? K : min(kBwdTile, La - t * kBwdTile);
+    f32x16 s[2], dp[2];
+    {
+      bf16x8 kf[2][NDS];
+      load_rows(SLOT_KK, st, kf);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[h][r] = 0.0f;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) s[h] = mfma32(kf[h][ds], qf[ds], s[h]);
+      }
+    }
+    {
+      bf16x8 vf[2][NDS];
+      load_rows(SLOT_VK, st, vf);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[h][r] = 0.0f;
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) dp[h] = mfma32(vf[h][ds], df[ds], dp[h]);
+      }
+    }
+    // register r of half h holds key 32h + 8*(r/4) + 4*half + r%4
+    int rel = nvalid - 4 * half;
+    asm volatile("" : "+v"(rel));
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = (32 * h + 8 * (r >> 2) + (r & 3)) < rel;
+        const float p = ok ? fast_exp2(fmaf(s[h][r], c2, -m2)) : 0.0f;
+        s[h][r] = p;
+        dp[h][r] = p * (dp[h][r] - di);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsb[ks][e] = (__bf16)dp[ks >> 1][8 * (ks & 1) + e];
+    if (blk) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dsblk[ks] = dsb[ks];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pblk[ks][e] = (__bf16)s[0][8 * ks + e];
+      }
+    }
+    TFrag tf;
+    load_kt(st, tf);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) dq[mb] = mfma32(tf[ks >> 1][ks & 1][mb], dsb[ks], dq[mb]);
+    __syncthreads();
+  }
+
+  // ---- dQ: scale, bf16 rows via LDS, coalesced stores (the ring is free)
+  constexpr int OPITCH = ROWB + 16;
+  static_assert(128 * OPITCH <= 2 * STAGEB, "rows fit the ring");
+  {
+    uint8_t* orow = smem + wrow * OPITCH;
+    const float sc = a.scale;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        ushort4 o;
+        o.x = to_bf16_bits(dq[mb][4 * q4 + 0] * sc);
+        o.y = to_bf16_bits(dq[mb][4 * q4 + 1] * sc);
+        o.z = to_bf16_bits(dq[mb][4 * q4 + 2] * sc);
+        o.w = to_bf16_bits(dq[mb][4 * q4 + 3] * sc);
+        *reinterpret_cast<ushort4*>(orow + 2 * (32 * mb + 8 * q4 + 4 * half)) = o;
+      }
+  }
+  __syncthreads();
+  for (int m = tid; m < 128 * DCH; m += kBwdThreads) {
+    const int r = m / DCH, ch = m % DCH;
+    if (r < R) {
+      const long long off = ((long long)(g * a.group + r / K) * NK + (long long)n * K + r % K) * D + ch * 8;
+      *reinterpret_cast<u32x4*>(a.dq + off) = *reinterpret_cast<const u32x4*>(smem + r * OPITCH + ch * 16);
+    }
+  }
+  __syncthreads();
+
+  // ---- block keys: dV_blk^T = dO^T P_blk, dK_blk^T = scale * Q^T dS_blk,
+  // contracted over all 128 rows.  LDS: P and dS as [key][row] bf16 (row
+  // pitch 128 rows), Q and dO as [row][D] in the transposing-read layout.
+  constexpr int PB = 0;                       // P_blk   [32][128] bf16
+  constexpr int DSB = 32 * 128 * 2;           // dS_blk  [32][128] bf16
+  constexpr int QB = 2 * DSB;                 // Q       [128][D]
+  constexpr int GB = QB + 128 * ROWB;         // dO      [128][D]
+  static_assert(GB + 128 * ROWB <= 2 * STAGEB, "block operands fit the ring");
+  {
+    const int key_lo = 4 * half;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // register 8*ks + e of half 0 holds key 8*((8*ks + e)/4) + 4*half + e%4
+        const int key = 8 * ((8 * ks + e) >> 2) + key_lo + (e & 3);
+        *reinterpret_cast<__bf16*>(smem + PB + (key * 128 + wrow) * 2) = pblk[ks][e];
+        *reinterpret_cast<__bf16*>(smem + DSB + (key * 128 + wrow) * 2) = dsblk[ks][e];
+      }
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int ch = 2 * ds + half;
+      *reinterpret_cast<bf16x8*>(smem + QB + wrow * ROWB + swz_v<DCH>(wrow, ch) * 16) = qf[ds];
+      *reinterpret_cast<bf16x8*>(smem + GB + wrow * ROWB + swz_v<DCH>(wrow, ch) * 16) = df[ds];
+    }
+  }
+  __syncthreads();
+  if (qb < NMB) {
+    const int mb = qb;  // head_dim block of this wave
+    f32x16 dv, dk;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dv[r] = dk[r] = 0.0f;
+    const int row0 = 4 * half + jj;
+    const int d0 = 32 * mb + 16 * (grp16 & 1) + 4 * qq;
+    const uint32_t qoff = (uint32_t)(QB + row0 * ROWB + swz_v<DCH>(row0, d0 >> 3) * 16 + (d0 & 7) * 2);
+    const uint32_t goff = qoff + (GB - QB);
+    // B operand rows for k-step (h, tt): the same two runs of 4 rows the
+    // transposing read returns, rows 32h + 16tt + 4*half + {0..3} and + 8
+    const int key = lane & 31;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)  // 4 x 32 rows
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int rb = 32 * h + 16 * tt;
+        const uint8_t* pq = smem + qoff + rb * ROWB;
+        const uint8_t* pg = smem + goff + rb * ROWB;
+        const bf16x4 q0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pq)));
+        const bf16x4 q1 =
+            __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pq + 8 * ROWB)));
+        const bf16x4 g0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pg)));
+        const bf16x4 g1 =
+            __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pg + 8 * ROWB)));
+        const bf16x8 qa = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 ga = __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const int r0 = rb + 4 * half;
+        const bf16x4 p0 = *reinterpret_cast<const bf16x4*>(smem + PB + (key * 128 + r0) * 2);
+        const bf16x4 p1 = *reinterpret_cast<const bf16x4*>(smem + PB + (key * 128 + r0 + 8) * 2);
+        const bf16x4 s0 = *reinterpret_cast<const bf16x4*>(smem + DSB + (key * 128 + r0) * 2);
+        const bf16x4 s1 = *reinterpret_cast<const bf16x4*>(smem + DSB + (key * 128 + r0 + 8) * 2);
+        dv = mfma32(ga, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7), dv);
+        dk = mfma32(qa, __builtin_shufflevector(s0, s1, 0, 1, 2, 3, 4, 5, 6, 7), dk);
+      }
+    // lane: key = lane % 32, head_dim 32*mb + 8i + 4*half + j in register 4i + j
+    if (key < K) {
+      const long long off = blk_off + (long long)key * D + 32 * mb + 4 * half;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ushort4 ov, ok;
+        ov.x = to_bf16_bits(dv[4 * i + 0]);
+        ov.y = to_bf16_bits(dv[4 * i + 1]);
+        ov.z = to_bf16_bits(dv[4 * i + 2]);
+        ov.w = to_bf16_bits(dv[4 * i + 3]);
+        ok.x = to_bf16_bits(dk[4 * i + 0] * a.scale);
+        ok.y = to_bf16_bits(dk[4 * i + 1] * a.scale);
+        ok.z = to_bf16_bits(dk[4 * i + 2] * a.scale);
+        ok.w = to_bf16_bits(dk[4 * i + 3] * a.scale);
+        *reinterpret_cast<ushort4*>(a.dv + off + 8 * i) = ov;
+        *reinterpret_cast<ushort4*>(a.dk + off + 8 * i) = ok;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_train_bwd(const TrainBwdArgs& a, hipStream_t stream) {
+  dim3 grid(a.n_blocks, a.n_kv_heads);
+  if (a.head_dim == 64)
+    hipLaunchKernelGGL(train_bwd_kernel<64>, grid, dim3(kBwdThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(train_bwd_kernel<128>, grid, dim3(kBwdThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace orthrus

@@ -304,6 +304,30 @@ orthrus_status orthrus_train_attn_fwd(const orthrus_train_attn_desc* d, const ui
                                       uint16_t* out_ar, float* lse_ar, uint16_t* out_diff,
                                       float* lse_diff, void* stream);
 
+/* Backward of the training dual-pass attention for the diffusion rows (the
+ * AR backbone is frozen, paper notes §2.1-2.2, so only the diffusion queries,
+ * keys and values get gradients).  With P the forward's softmax of a
+ * diffusion row (recomputed from lse_diff), O its output and dO the upstream
+ * gradient:  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dq_diff = scale * dS K        over all keys of the row,
+ *   dk_diff = scale * dS^T Q,  dv_diff = P^T dO   for the block's own keys,
+ * summed over the q heads that share a KV head.
+ *   k_ar, v_ar, q_diff, k_diff, v_diff, anchors   as orthrus_train_attn_fwd
+ *   out_diff [Hq, N*K, D], lse_diff fp32 [Hq, N*K]   from the forward
+ *   d_out_diff [Hq, N*K, D] bf16   upstream gradient of out_diff
+ *   dq_diff [Hq, N*K, D], dk_diff / dv_diff [Hkv, N*K, D]   bf16 (written;
+ *   every element, no accumulation into existing values)
+ * Needs (Hq / Hkv) * K <= 128 (else ORTHRUS_ERR_UNSUPPORTED): one work-group
+ * holds every row that reads a block's keys.  No workspace; asynchronous on
+ * `stream`. */
+orthrus_status orthrus_train_attn_bwd(const orthrus_train_attn_desc* d, const uint16_t* k_ar,
+                                      const uint16_t* v_ar, const uint16_t* q_diff,
+                                      const uint16_t* k_diff, const uint16_t* v_diff,
+                                      const int32_t* anchors, const uint16_t* out_diff,
+                                      const float* lse_diff, const uint16_t* d_out_diff,
+                                      uint16_t* dq_diff, uint16_t* dk_diff, uint16_t* dv_diff,
+                                      void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* orthrus_status_string(orthrus_status s);
 

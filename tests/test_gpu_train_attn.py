@@ -90,3 +90,80 @@ def test_packed_sequence_full_shape_sampled_heads():
     benchmark launch, checked on q heads 0, 13 and 31 (every row of each)."""
     x = train_attn_inputs(32, 8, 2048, 256, 32, 128, seed=5, device=DEV)
     _check(x, "packed2048", heads=[0, 13, 31])
+
+
+# ------------------------------------------------------------ backward ----
+def _rel_l2(got, ref):
+    g = got.detach().cpu().double().numpy()
+    return float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)), float(np.abs(g - ref).max())
+
+
+def _check_bwd(x, what, seed, blocks=None, kv_head=None):
+    """GPU forward + backward against the fp64 oracle backward (optionally on
+    selected blocks of one KV head).  The bar: relative L2 <= 1e-2 per
+    gradient -- bf16 P and dS as MFMA operands (2^-9 each), bf16 O in the row
+    sums and bf16 outputs give ~4e-3 -- and max-abs <= 2e-2 of the gradient's
+    largest magnitude."""
+    K = x["block_k"]
+    _, _, out_d, lse_d = _run(x)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    d_out = torch.randn(x["q_diff"].shape, generator=g, device=DEV).to(torch.bfloat16)
+    dq, dk, dv = dvb.orthrus_train_attn_bwd(x["k_ar"], x["v_ar"], x["q_diff"], x["k_diff"], x["v_diff"],
+                                            x["anchors"], K, out_d, lse_d, d_out)
+    torch.cuda.synchronize()
+    Hq, Hkv = x["q_ar"].shape[0], x["k_ar"].shape[0]
+    G = Hq // Hkv
+    N = x["anchors"].shape[0]
+    blocks = list(range(N)) if blocks is None else blocks
+    heads = list(range(Hkv)) if kv_head is None else [kv_head]
+    rows = torch.cat([torch.arange(b * K, (b + 1) * K) for b in blocks]).to(DEV)
+    qh = torch.cat([torch.arange(h * G, (h + 1) * G) for h in heads]).to(DEV)
+    kh = torch.tensor(heads, device=DEV)
+    sel = lambda t, hs: t[hs][:, rows].cpu()
+    ref = oracle.dual_pass_backward(x["k_ar"][kh].cpu(), x["v_ar"][kh].cpu(), sel(x["q_diff"], qh),
+                                    sel(x["k_diff"], kh), sel(x["v_diff"], kh),
+                                    x["anchors"].cpu()[torch.tensor(blocks)].clamp(0, x["k_ar"].shape[1]), K,
+                                    sel(d_out, qh))
+    worst = []
+    for name, got, r in (("dq", dq[qh][:, rows], ref[0]), ("dk", dk[kh][:, rows], ref[1]),
+                         ("dv", dv[kh][:, rows], ref[2])):
+        rl2, mabs = _rel_l2(got, r)
+        bound = 2e-2 * float(np.abs(r).max())
+        assert rl2 <= 1e-2 and mabs <= bound, f"{what}/{name}: rel_l2 {rl2:.2e} max_abs {mabs:.2e} (bound {bound:.2e})"
+        worst.append(f"{name} rel_l2={rl2:.2e} max_abs={mabs:.2e}")
+    print(f"{what}: " + "; ".join(worst), flush=True)
+
+
+@pytest.mark.parametrize("shape", [
+    (4, 2, 256, 8, 32, 128),
+    (2, 1, 128, 5, 16, 64),
+    (8, 8, 96, 7, 8, 64),
+    (4, 1, 320, 6, 32, 128),
+])
+def test_backward_matches_oracle(shape):
+    Hq, Hkv, L, N, K, D = shape
+    x = train_attn_inputs(Hq, Hkv, L, N, K, D, seed=100 + sum(shape), device=DEV)
+    _check_bwd(x, f"bwd{shape}", seed=sum(shape))
+
+
+def test_backward_anchor_edges():
+    x = train_attn_inputs(4, 1, 128, 5, 32, 128, seed=13, device=DEV, anchors=[0, 96, 128, 5000, 1])
+    _check_bwd(x, "bwd-anchors", seed=13)
+
+
+def test_backward_rejects_groups_past_128_rows():
+    x = train_attn_inputs(8, 1, 64, 2, 32, 128, seed=1, device=DEV)
+    _, _, out_d, lse_d = _run(x)
+    with pytest.raises(dvb.OrthrusError) as e:
+        dvb.orthrus_train_attn_bwd(x["k_ar"], x["v_ar"], x["q_diff"], x["k_diff"], x["v_diff"], x["anchors"], 32,
+                                   out_d, lse_d, out_d)
+    assert e.value.status == 3
+
+
+def test_backward_packed_sequence_full_shape_sampled():
+    """L 2048, 256 blocks of 32, 32 / 8 heads, D 128: KV heads 0 and 7 on six
+    blocks each (every row, key and head_dim of them)."""
+    x = train_attn_inputs(32, 8, 2048, 256, 32, 128, seed=6, device=DEV)
+    for kvh in (0, 7):
+        _check_bwd(x, f"bwd-packed2048-g{kvh}", seed=6, blocks=[0, 1, 100, 128, 200, 255], kv_head=kvh)
