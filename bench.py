@@ -56,13 +56,16 @@ def _parse():
     ap.add_argument("--kl-rows", type=int, default=8192,
                     help="rows of the forward-KL measurement (256 blocks x K = 32 diffusion positions "
                          "of one packed training sequence; 0 to skip)")
+    ap.add_argument("--train-attn", type=int, default=1,
+                    help="time the training dual-pass attention (forward and diffusion-row backward) of "
+                         "one packed 2048-token sequence at the workload's heads (0 to skip)")
     ap.add_argument("--accept-rate", type=float, default=0.912,
                     help="per-candidate match probability of the synthetic acceptance law "
                          "(0.912: 10.8 tokens per cycle at K = 32)")
     ap.add_argument("--traffic", default=TRAFFIC_JSON,
                     help="JSON record of rocprofv3-derived HBM bytes per streaming-kernel launch "
                          "(ignored if the code of attention.hip changed since it was taken)")
-    ap.add_argument("--profile-target", choices=["attn-stream", "copy", "forward-kl"], default=None,
+    ap.add_argument("--profile-target", choices=["attn-stream", "copy", "forward-kl", "train-attn"], default=None,
                     help="run only the streaming kernel over every layer-view (or a plain copy "
                          "kernel of --copy-mib MiB, or the forward KL with its gradient at "
                          "--kl-rows x vocab) --steps times, for rocprofv3 counter runs")
@@ -402,6 +405,65 @@ def time_forward_kl(device, rows: int, vocab: int, reps: int = 10):
     return out
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def train_attn_flops(seq_len: int, anchors, block_k: int, n_q_heads: int, head_dim: int):
+    """Matrix flops of the training attention.  Forward: QK^T and PV over the
+    allowed keys of every row (AR row i: i+1 keys; diffusion row of block n:
+    a_n + K keys).  Backward (diffusion rows): QK^T, dO V^T and dS K over all
+    their keys, plus dS^T Q and P^T dO over the block's own keys."""
+    diff_keys = sum(int(a) + block_k for a in anchors) * block_k  # sum over diffusion rows
+    ar_keys = seq_len * (seq_len + 1) // 2
+    fwd = 4 * n_q_heads * head_dim * (ar_keys + diff_keys)
+    n_rows = len(anchors) * block_k
+    bwd = 2 * n_q_heads * head_dim * (3 * diff_keys + 2 * n_rows * block_k)
+    return fwd, bwd
+
+
+def time_train_attn(w, device, reps: int = 10):
+    """Training dual-pass attention of one packed sequence (L 2048, 256
+    anchor blocks of K 32, the workload's heads): forward (AR + diffusion
+    rows) and the diffusion-row backward, HIP events around `reps`
+    back-to-back calls each."""
+    import torch
+
+    import dual_view_block_amd as dvb
+    from synth import train_attn_inputs
+
+    L, N, K = 2048, 256, 32
+    x = train_attn_inputs(w.n_q_heads, w.n_kv_heads, L, N, K, w.head_dim, seed=5, device=device)
+    stream = torch.cuda.current_stream()
+    fwd = lambda: dvb.orthrus_train_attn_fwd(x["q_ar"], x["k_ar"], x["v_ar"], x["q_diff"], x["k_diff"],
+                                             x["v_diff"], x["anchors"], K, out_ar=out_ar, lse_ar=lse_ar,
+                                             out_diff=out_d, lse_diff=lse_d)
+    out_ar, lse_ar, out_d, lse_d = dvb.orthrus_train_attn_fwd(x["q_ar"], x["k_ar"], x["v_ar"], x["q_diff"],
+                                                              x["k_diff"], x["v_diff"], x["anchors"], K)
+    g = torch.Generator(device=device)
+    g.manual_seed(7)
+    d_out = torch.randn(x["q_diff"].shape, generator=g, device=device).to(torch.bfloat16)
+    dq, dk, dv = (torch.empty_like(x["q_diff"]), torch.empty_like(x["k_diff"]), torch.empty_like(x["v_diff"]))
+    bwd = lambda: dvb.orthrus_train_attn_bwd(x["k_ar"], x["v_ar"], x["q_diff"], x["k_diff"], x["v_diff"],
+                                             x["anchors"], K, out_d, lse_d, d_out, dq=dq, dk=dk, dv=dv)
+    f_fwd, f_bwd = train_attn_flops(L, x["anchors"].cpu().tolist(), K, w.n_q_heads, w.head_dim)
+    out = {"seq_len": L, "n_blocks": N, "block_k": K, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+           "head_dim": w.head_dim, "dtype": "bf16"}
+    for name, fn, flops in (("forward", fwd, f_fwd), ("backward", bwd, f_bwd)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tf = flops / (us * 1e-6) / 1e12
+        out[name] = {"us": round(us, 2), "flops": flops, "tflops": round(tf, 1),
+                     "frac_mfma_bf16_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
 def profile_target(args, w, caches, device) -> None:
     """Only the kernel under study, for rocprofv3 counter runs (no timing)."""
     import torch
@@ -411,6 +473,9 @@ def profile_target(args, w, caches, device) -> None:
         dst = torch.empty_like(src)
         for _ in range(args.steps):
             dst.copy_(src)  # device-to-device: one copy kernel, reads and writes copy_mib MiB
+    elif args.profile_target == "train-attn":
+        for _ in range(args.steps):
+            time_train_attn(w, device, reps=1)
     elif args.profile_target == "forward-kl":
         import dual_view_block_amd as dvb
         from synth import kl_inputs
@@ -492,7 +557,7 @@ def main():
     if args.layers:
         w = w.replace(layers=args.layers)
     print(f"[bench] workload {w}", file=sys.stderr, flush=True)
-    if args.profile_target in ("copy", "forward-kl"):
+    if args.profile_target in ("copy", "forward-kl", "train-attn"):
         profile_target(args, w, None, device)
         return
     # one layer-major cache for all layers, with room past L for the rows the
@@ -533,6 +598,13 @@ def main():
         cyc = time_cycles(w, kc_all, vc_all, device, args.cycles, args.cycle_sets, args.accept_rate)
         print(f"[bench] cycles: {cyc['us_per_cycle']:.1f} us/cycle, {cyc['tokens_per_cycle']:.2f} tokens/cycle, "
               f"commit {cyc['commit_us']:.2f} us", file=sys.stderr, flush=True)
+
+    tra = None
+    if args.train_attn:
+        tra = time_train_attn(w, device)
+        print(f"[bench] training attention L2048 x 256 blocks: forward {tra['forward']['us']:.1f} us "
+              f"({tra['forward']['tflops']:.0f} TFLOP/s), backward {tra['backward']['us']:.1f} us "
+              f"({tra['backward']['tflops']:.0f} TFLOP/s)", file=sys.stderr, flush=True)
 
     fkl = None
     if args.kl_rows > 0:
@@ -583,6 +655,8 @@ def main():
         line["decode_cycles"] = cyc
     if fkl is not None:
         line["forward_kl"] = fkl
+    if tra is not None:
+        line["train_attention"] = tra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, caches, device)
     print(json.dumps(line), flush=True)
