@@ -17,7 +17,9 @@ What is computed follows the Orthrus pages:
 * the training objective's forward KL(P_AR || P_Diff) over the vocabulary and
   its draft-logit gradient -- ``oracle.kl``;
 * the training-time dual-pass block-mask attention, forward and the backward
-  of the diffusion rows -- ``oracle.train_attn``.
+  of the diffusion rows -- ``oracle.train_attn``;
+* tree verification (draft trees from top-M marginals, ancestor masks, greedy
+  consensus along the tree, path commit) -- ``oracle.tree``.
 
 Every function is the plain definition written out in float64 (or exact
 integers), one sequence / head at a time, with explicit masks.  Library
@@ -29,7 +31,7 @@ against closed forms, library routines (``torch`` SDPA in float64), brute
 force on tiny inputs, invariants the pages fix, and exact enumeration of the
 sampler's uniforms.  No function is "parity unpinned".
 """
-from .attention import (MASK_DIFF_BIDIR, MASK_VERIFY_CAUSAL, block_attention,
+from .attention import (MASK_DIFF_BIDIR, MASK_EXPLICIT, MASK_VERIFY_CAUSAL, block_attention,
                         block_attention_rows, transient_kv_bytes)
 from .consensus import (greedy_consensus, row_argmax, sample_consensus,
                         accept_prefix, accepts, residual_weights, inverse_cdf_pick,
@@ -38,6 +40,8 @@ from .consensus import (greedy_consensus, row_argmax, sample_consensus,
 from .cycle import bits_to_bf16, commit_block, decode_cycles
 from .kl import forward_kl, forward_kl_rows
 from .train_attn import dual_pass_backward, dual_pass_forward, training_attention_flops
+from .tree import (ancestor_masks, build_tree, commit_path, masks_to_bits, topk_logprobs,
+                   tree_greedy_consensus)
 
 __all__ = [
     "MASK_DIFF_BIDIR", "MASK_VERIFY_CAUSAL", "block_attention",
@@ -46,4 +50,6 @@ __all__ = [
     "inverse_cdf_pick", "fixed_point_weight", "uniform_to_grid_int",
     "tokens_committed", "bits_to_bf16", "commit_block", "decode_cycles", "forward_kl",
     "forward_kl_rows", "dual_pass_forward", "dual_pass_backward", "training_attention_flops",
+    "MASK_EXPLICIT", "ancestor_masks", "build_tree", "commit_path", "masks_to_bits", "topk_logprobs",
+    "tree_greedy_consensus",
 ]

@@ -37,6 +37,7 @@ import numpy as np
 
 MASK_DIFF_BIDIR = 0      # diffusion view: every block row sees every block key
 MASK_VERIFY_CAUSAL = 1   # AR verify: block row i sees block keys j <= i
+MASK_EXPLICIT = 2        # a given per-row set of visible block keys (tree / ragged blocks)
 
 
 def _as_f64(x) -> np.ndarray:
@@ -60,7 +61,7 @@ def _as_int(x) -> np.ndarray:
     return np.asarray(x, dtype=np.int64)
 
 
-def block_mask(L: int, K: int, mode: int) -> np.ndarray:
+def block_mask(L: int, K: int, mode: int, explicit=None) -> np.ndarray:
     """Boolean mask [K, L+K]: row i (block position i) may attend key column c.
 
     Columns 0..L-1 are the cached positions (all before the anchor: visible to
@@ -75,6 +76,11 @@ def block_mask(L: int, K: int, mode: int) -> np.ndarray:
     elif mode == MASK_VERIFY_CAUSAL:
         for i in range(K):
             m[i, L:L + i + 1] = True
+    elif mode == MASK_EXPLICIT:
+        # explicit[i][j]: block key j visible to block row i (R22)
+        for i in range(K):
+            for j in range(K):
+                m[i, L + j] = bool(explicit[i][j])
     else:
         raise ValueError(f"unknown mask mode {mode}")
     return m
@@ -89,21 +95,27 @@ def _attend(qrows: np.ndarray, keys: np.ndarray, vals: np.ndarray,
     """
     s = scale * (qrows @ keys.T)
     s = np.where(mask, s, -np.inf)
-    smax = s.max(axis=1, keepdims=True)
-    e = np.exp(s - smax)
-    denom = e.sum(axis=1, keepdims=True)
-    p = e / denom
-    out = p @ vals
-    lse = smax[:, 0] + np.log(denom[:, 0])
+    out = np.zeros((qrows.shape[0], vals.shape[1]))
+    lse = np.full(qrows.shape[0], -np.inf)
+    for r in range(qrows.shape[0]):
+        if not mask[r].any():  # a row with no visible key: output 0, lse -inf (R22)
+            continue
+        smax = s[r].max()
+        e = np.exp(s[r] - smax)
+        denom = e.sum()
+        out[r] = (e / denom) @ vals
+        lse[r] = smax + np.log(denom)
     return out, lse
 
 
 def block_attention(q, k_blk, v_blk, k_cache, v_cache, cache_len, mode: int,
-                    scale: float | None = None):
+                    scale: float | None = None, block_masks=None):
     """Dual-view block attention for every (sequence, q head, block row).
 
     Shapes: q [B,Hq,K,D]; k_blk, v_blk [B,Hkv,K,D]; k_cache, v_cache
-    [B,Hkv,max_len,D]; cache_len [B] (clamped to [0, max_len]).
+    [B,Hkv,max_len,D]; cache_len [B] (clamped to [0, max_len]).  With mode
+    MASK_EXPLICIT, block_masks [B,K,K] (bool) gives the visible block keys of
+    every row.
     Returns (out [B,Hq,K,D] float64, lse [B,Hq,K] float64).
     """
     qd, kb, vb = _as_f64(q), _as_f64(k_blk), _as_f64(v_blk)
@@ -120,7 +132,7 @@ def block_attention(q, k_blk, v_blk, k_cache, v_cache, cache_len, mode: int,
     lse = np.zeros((B, Hq, K))
     for b in range(B):
         L = int(min(max(int(lens[b]), 0), max_len))
-        mask = block_mask(L, K, mode)
+        mask = block_mask(L, K, mode, None if block_masks is None else block_masks[b])
         for h in range(Hq):
             g = h // G
             keys = np.concatenate([kc[b, g, :L], kb[b, g]], axis=0)
