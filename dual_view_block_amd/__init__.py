@@ -19,7 +19,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (ORTHRUS_MASK_DIFF_BIDIR, ORTHRUS_MASK_VERIFY_CAUSAL, AttnDesc, CommitDesc,
+from ._lib import (ORTHRUS_MASK_DIFF_BIDIR, ORTHRUS_MASK_EXPLICIT, ORTHRUS_MASK_VERIFY_CAUSAL, AttnDesc, CommitDesc,
                    OrthrusError, TrainAttnDesc, status_string)
 
 __all__ = [
@@ -29,7 +29,9 @@ __all__ = [
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_status_string",
     "PreparedAttention", "PreparedGreedy", "library_path", "CommitDesc", "orthrus_cache_commit",
     "PreparedCommit", "orthrus_kl_workspace_size", "orthrus_forward_kl", "PreparedForwardKL",
-    "TrainAttnDesc", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd",
+    "TrainAttnDesc", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd", "orthrus_block_attn_masked",
+    "orthrus_topk_logprobs", "orthrus_tree_build", "orthrus_tree_masks", "orthrus_consensus_tree_greedy",
+    "orthrus_cache_commit_path",
 ]
 
 
@@ -475,3 +477,116 @@ def orthrus_train_attn_bwd(k_ar, v_ar, q_diff, k_diff, v_diff, anchors, block_k,
         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream_ptr(stream))
     _lib.check("orthrus_train_attn_bwd", st)
     return dq, dk, dv
+
+
+# ------------------------------------------------------------ tree verification
+def orthrus_block_attn_masked(q, k_blk, v_blk, k_cache, v_cache, cache_len, block_mask, out=None, lse=None,
+                              workspace=None, softmax_scale: float = 0.0, want_lse: bool = True, stream=None):
+    """Block attention with explicit per-row block masks (int64 [B, K], bit j
+    = block key j visible).  Returns (out, lse)."""
+    _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len)
+    desc = attn_desc(q, k_cache, softmax_scale)
+    dev = q.device
+    B, Hq, K, D = q.shape
+    _need(block_mask, "block_mask", torch.int64, (B, K), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = _workspace(orthrus_attn_workspace_size(desc), dev, workspace)
+    st = _lib.load().orthrus_block_attn_masked(
+        ctypes.byref(desc), q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), cache_len.data_ptr(), block_mask.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_block_attn_masked", st)
+    return out, lse
+
+
+def orthrus_topk_logprobs(logits, m: int, logp=None, idx=None, workspace=None, stream=None):
+    """Top-m logits per row and their log-probabilities.  logits fp32 [R, V].
+    Returns (logp fp32 [R, m], idx int32 [R, m])."""
+    R, V = logits.shape
+    dev = logits.device
+    _need(logits, "logits", torch.float32, (R, V))
+    logp = torch.empty((R, m), dtype=torch.float32, device=dev) if logp is None else logp
+    idx = torch.empty((R, m), dtype=torch.int32, device=dev) if idx is None else idx
+    _need(logp, "logp", torch.float32, (R, m), dev)
+    _need(idx, "idx", torch.int32, (R, m), dev)
+    ws = _workspace(int(_lib.load().orthrus_topk_workspace_size(R, V, m)), dev, workspace)
+    st = _lib.load().orthrus_topk_logprobs(R, V, m, logits.data_ptr(), logp.data_ptr(), idx.data_ptr(),
+                                           ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_topk_logprobs", st)
+    return logp, idx
+
+
+def orthrus_tree_build(logp, tok, anchor, n_nodes: int, parent=None, tokens=None, depth=None, stream=None):
+    """Best-first draft trees.  logp fp32 [B, Dd, m], tok int32 [B, Dd, m],
+    anchor int32 [B].  Returns (parent, tokens, depth) int32 [B, n_nodes]."""
+    B, Dd, m = logp.shape
+    dev = logp.device
+    _need(logp, "logp", torch.float32, (B, Dd, m))
+    _need(tok, "tok", torch.int32, (B, Dd, m), dev)
+    _need(anchor, "anchor", torch.int32, (B,), dev)
+    mk = lambda t: torch.empty((B, n_nodes), dtype=torch.int32, device=dev) if t is None else t
+    parent, tokens, depth = mk(parent), mk(tokens), mk(depth)
+    for t, nm in ((parent, "parent"), (tokens, "tokens"), (depth, "depth")):
+        _need(t, nm, torch.int32, (B, n_nodes), dev)
+    st = _lib.load().orthrus_tree_build(B, Dd, m, n_nodes, logp.data_ptr(), tok.data_ptr(), anchor.data_ptr(),
+                                        parent.data_ptr(), tokens.data_ptr(), depth.data_ptr(), _stream_ptr(stream))
+    _lib.check("orthrus_tree_build", st)
+    return parent, tokens, depth
+
+
+def orthrus_tree_masks(parent, mask=None, stream=None):
+    """Ancestor-or-self bitmasks (int64 [B, K]) of draft trees (parent int32 [B, K])."""
+    B, K = parent.shape
+    dev = parent.device
+    _need(parent, "parent", torch.int32, (B, K))
+    mask = torch.empty((B, K), dtype=torch.int64, device=dev) if mask is None else mask
+    _need(mask, "mask", torch.int64, (B, K), dev)
+    st = _lib.load().orthrus_tree_masks(B, K, parent.data_ptr(), mask.data_ptr(), _stream_ptr(stream))
+    _lib.check("orthrus_tree_masks", st)
+    return mask
+
+
+def orthrus_consensus_tree_greedy(logits, tokens, parent, accept_len=None, path=None, correction=None,
+                                  row_argmax=None, workspace=None, want_row_argmax: bool = False, stream=None):
+    """Greedy consensus along draft trees.  Returns (accept_len [B], path [B, K],
+    correction [B], row_argmax [B, K] or None), int32."""
+    B, K, V = logits.shape
+    dev = logits.device
+    _need(logits, "logits", torch.float32, (B, K, V))
+    _need(tokens, "tokens", torch.int32, (B, K), dev)
+    _need(parent, "parent", torch.int32, (B, K), dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    accept_len = torch.empty(B, **i32) if accept_len is None else accept_len
+    path = torch.empty((B, K), **i32) if path is None else path
+    correction = torch.empty(B, **i32) if correction is None else correction
+    if row_argmax is None and want_row_argmax:
+        row_argmax = torch.empty((B, K), **i32)
+    ws = _workspace(orthrus_consensus_workspace_size(B, K, V), dev, workspace)
+    st = _lib.load().orthrus_consensus_tree_greedy(
+        B, K, V, logits.data_ptr(), tokens.data_ptr(), parent.data_ptr(), accept_len.data_ptr(), path.data_ptr(),
+        correction.data_ptr(), row_argmax.data_ptr() if row_argmax is not None else None, ws.data_ptr(),
+        ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_consensus_tree_greedy", st)
+    return accept_len, path, correction, row_argmax
+
+
+def orthrus_cache_commit_path(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, path, node_tokens,
+                              correction, next_anchor=None, tokens=None, n_tokens=None, stream=None):
+    """Commit accepted tree paths (caches and cache_len updated in place).
+    Returns (next_anchor [B], tokens [B, K], n_tokens [B])."""
+    desc = _check_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, node_tokens)
+    B, K, dev = desc.batch, desc.block_k, k_cache.device
+    _need(path, "path", torch.int32, (B, K), dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    next_anchor = torch.empty(B, **i32) if next_anchor is None else next_anchor
+    tokens = torch.empty((B, K), **i32) if tokens is None else tokens
+    n_tokens = torch.empty(B, **i32) if n_tokens is None else n_tokens
+    st = _lib.load().orthrus_cache_commit_path(
+        ctypes.byref(desc), k_cache.data_ptr(), v_cache.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
+        cache_len.data_ptr(), accept_len.data_ptr(), path.data_ptr(), node_tokens.data_ptr(), correction.data_ptr(),
+        next_anchor.data_ptr(), tokens.data_ptr(), n_tokens.data_ptr(), _stream_ptr(stream))
+    _lib.check("orthrus_cache_commit_path", st)
+    return next_anchor, tokens, n_tokens

@@ -22,6 +22,7 @@ ORTHRUS_ERR_WORKSPACE_TOO_SMALL = 5
 ORTHRUS_ERR_HIP = 6
 ORTHRUS_MASK_DIFF_BIDIR = 0
 ORTHRUS_MASK_VERIFY_CAUSAL = 1
+ORTHRUS_MASK_EXPLICIT = 2
 ORTHRUS_DTYPE_F32 = 0
 ORTHRUS_DTYPE_BF16 = 1
 
@@ -32,7 +33,8 @@ EXPORTS = (
     "orthrus_block_attn_merge", "orthrus_consensus_workspace_size",
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_cache_commit",
     "orthrus_kl_workspace_size", "orthrus_forward_kl", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd",
-    "orthrus_status_string",
+    "orthrus_block_attn_masked", "orthrus_topk_workspace_size", "orthrus_topk_logprobs", "orthrus_tree_build",
+    "orthrus_tree_masks", "orthrus_consensus_tree_greedy", "orthrus_cache_commit_path", "orthrus_status_string",
 )
 
 
@@ -99,6 +101,13 @@ _SIGS = {
     "orthrus_forward_kl": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_float, _P, _SZ, _P]),
     "orthrus_train_attn_fwd": (_I32, [ctypes.POINTER(TrainAttnDesc)] + [_P] * 12),
     "orthrus_train_attn_bwd": (_I32, [ctypes.POINTER(TrainAttnDesc)] + [_P] * 13),
+    "orthrus_block_attn_masked": (_I32, [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "orthrus_topk_workspace_size": (_SZ, [_I32, _I32, _I32]),
+    "orthrus_topk_logprobs": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "orthrus_tree_build": (_I32, [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "orthrus_tree_masks": (_I32, [_I32, _I32, _P, _P, _P]),
+    "orthrus_consensus_tree_greedy": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "orthrus_cache_commit_path": (_I32, [ctypes.POINTER(CommitDesc)] + [_P] * 13),
     "orthrus_status_string": (ctypes.c_char_p, [_I32]),
 }
 

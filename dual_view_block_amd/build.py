@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liborthrus.so")
-SOURCES = ("api.hip", "attention.hip", "consensus.hip", "commit.hip", "kl.hip", "train_bwd.hip")
+SOURCES = ("api.hip", "attention.hip", "consensus.hip", "commit.hip", "kl.hip", "train_bwd.hip", "tree.hip")
 
 
 def hipcc() -> str:

@@ -35,7 +35,7 @@ orthrus_status check_desc(const orthrus_attn_desc* d) {
   if (d->n_q_heads % d->n_kv_heads != 0) return ORTHRUS_ERR_BAD_SHAPE;
   if (!(isfinite(d->softmax_scale) && d->softmax_scale >= 0.0f)) return ORTHRUS_ERR_BAD_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return ORTHRUS_ERR_UNSUPPORTED;
-  if (d->block_k > 32) return ORTHRUS_ERR_UNSUPPORTED;
+  if (d->block_k > 128) return ORTHRUS_ERR_UNSUPPORTED;
   // every element offset must fit comfortably in 63 bits and every grid dimension in range
   const long long rows = (long long)(d->n_q_heads / d->n_kv_heads) * d->block_k;
   if ((long long)d->batch * d->n_kv_heads > 65535LL || rows > (1LL << 20)) return ORTHRUS_ERR_BAD_SHAPE;
@@ -84,10 +84,16 @@ int device_cus() {
 orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q, const uint16_t* k_blk,
                         const uint16_t* v_blk, const uint16_t* k_cache, const uint16_t* v_cache,
                         const int32_t* cache_len, uint16_t* out, float* lse, void* workspace,
-                        size_t workspace_bytes, void* stream, int phases) {
+                        size_t workspace_bytes, void* stream, int phases, const uint64_t* block_mask = nullptr) {
   const orthrus_status st = check_desc(d);
   if (st != ORTHRUS_OK) return st;
-  if (mode != ORTHRUS_MASK_DIFF_BIDIR && mode != ORTHRUS_MASK_VERIFY_CAUSAL) return ORTHRUS_ERR_BAD_SHAPE;
+  if (mode != ORTHRUS_MASK_DIFF_BIDIR && mode != ORTHRUS_MASK_VERIFY_CAUSAL && mode != ORTHRUS_MASK_EXPLICIT)
+    return ORTHRUS_ERR_BAD_SHAPE;
+  if (mode == ORTHRUS_MASK_EXPLICIT) {
+    if (!block_mask && (phases & 1)) return ORTHRUS_ERR_NULL_PTR;
+    if ((phases & 1) && !aligned4(block_mask)) return ORTHRUS_ERR_MISALIGNED;
+    if (d->block_k > 64) return ORTHRUS_ERR_UNSUPPORTED;
+  }
   if (!workspace) return ORTHRUS_ERR_NULL_PTR;
   if ((phases & 1) && (!q || !k_blk || !v_blk || !k_cache || !v_cache || !cache_len))
     return ORTHRUS_ERR_NULL_PTR;
@@ -123,6 +129,7 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.max_len = d->max_len;
   a.causal = mode == ORTHRUS_MASK_VERIFY_CAUSAL ? 1 : 0;
   set_decode_strides(a);
+  a.blk_mask = mode == ORTHRUS_MASK_EXPLICIT ? block_mask : nullptr;
   a.splits = attn_launch_splits(plan, d->batch, d->n_kv_heads, d->max_len, cus);
   const int cap = env_int("ORTHRUS_MAX_SPLITS", a.splits);  // tuning: may only lower the split count
   if (cap < a.splits) a.splits = cap;
@@ -140,7 +147,7 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
 
 orthrus_status check_consensus_sizes(int32_t B, int32_t K, int32_t V) {
   if (B < 1 || K < 1 || V < 1) return ORTHRUS_ERR_BAD_SHAPE;
-  if (K > 32) return ORTHRUS_ERR_UNSUPPORTED;
+  if (K > 128) return ORTHRUS_ERR_UNSUPPORTED;
   if ((long long)B * K > 65535LL) return ORTHRUS_ERR_BAD_SHAPE;
   return ORTHRUS_OK;
 }
@@ -279,6 +286,14 @@ orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, orthrus_mask_mode 
                                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return run_attn(d, (int)mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
                   workspace_bytes, stream, 3);
+}
+
+orthrus_status orthrus_block_attn_masked(const orthrus_attn_desc* d, const uint16_t* q, const uint16_t* k_blk,
+                                         const uint16_t* v_blk, const uint16_t* k_cache, const uint16_t* v_cache,
+                                         const int32_t* cache_len, const uint64_t* block_mask, uint16_t* out,
+                                         float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attn(d, ORTHRUS_MASK_EXPLICIT, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
+                  workspace_bytes, stream, 3, block_mask);
 }
 
 orthrus_status orthrus_block_attn_partial(const orthrus_attn_desc* d, orthrus_mask_mode mode,
@@ -516,6 +531,97 @@ orthrus_status orthrus_train_attn_bwd(const orthrus_train_attn_desc* d, const ui
   a.scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   const hipError_t e = launch_train_bwd(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status orthrus_tree_masks(int32_t batch, int32_t block_k, const int32_t* parent, uint64_t* mask,
+                                  void* stream) {
+  if (batch < 1 || block_k < 1) return ORTHRUS_ERR_BAD_SHAPE;
+  if (block_k > 64) return ORTHRUS_ERR_UNSUPPORTED;
+  if ((long long)batch * block_k > 0x7fffffffLL) return ORTHRUS_ERR_BAD_SHAPE;
+  if (!parent || !mask) return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned4(parent) || (reinterpret_cast<uintptr_t>(mask) & 7u)) return ORTHRUS_ERR_MISALIGNED;
+  const hipError_t e = launch_tree_masks(batch, block_k, parent, mask, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status orthrus_consensus_tree_greedy(int32_t batch, int32_t block_k, int32_t vocab, const float* logits,
+                                             const int32_t* tokens, const int32_t* parent, int32_t* accept_len,
+                                             int32_t* path, int32_t* correction, int32_t* row_argmax,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  const orthrus_status st = check_consensus_sizes(batch, block_k, vocab);
+  if (st != ORTHRUS_OK) return st;
+  if (!logits || !tokens || !parent || !accept_len || !path || !correction || !workspace)
+    return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(logits) || !aligned4(tokens) || !aligned4(parent) || !aligned4(accept_len) || !aligned4(path) ||
+      !aligned4(correction) || (row_argmax && !aligned4(row_argmax)) || !aligned16(workspace))
+    return ORTHRUS_ERR_MISALIGNED;
+  const ConsensusPlan plan = make_consensus_plan(batch, block_k, vocab);
+  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+  const hipError_t e = launch_consensus_tree_greedy(batch, block_k, vocab, logits, tokens, parent, accept_len, path,
+                                                    correction, row_argmax, workspace, plan,
+                                                    reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status orthrus_cache_commit_path(const orthrus_commit_desc* d, uint16_t* k_cache, uint16_t* v_cache,
+                                         const uint16_t* k_blk, const uint16_t* v_blk, int32_t* cache_len,
+                                         const int32_t* accept_len, const int32_t* path, const int32_t* node_tokens,
+                                         const int32_t* correction, int32_t* next_anchor, int32_t* tokens,
+                                         int32_t* n_tokens, void* stream) {
+  const orthrus_status st = check_commit_desc(d);
+  if (st != ORTHRUS_OK) return st;
+  if (!k_cache || !v_cache || !k_blk || !v_blk || !cache_len || !accept_len || !path || !node_tokens ||
+      !correction || !next_anchor || !tokens || !n_tokens)
+    return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_blk) || !aligned16(v_blk) ||
+      !aligned4(cache_len) || !aligned4(accept_len) || !aligned4(path) || !aligned4(node_tokens) ||
+      !aligned4(correction) || !aligned4(next_anchor) || !aligned4(tokens) || !aligned4(n_tokens))
+    return ORTHRUS_ERR_MISALIGNED;
+  const size_t planes = (size_t)d->n_layers * d->batch * d->n_kv_heads;
+  const size_t cache_bytes = planes * d->max_len * d->head_dim * sizeof(uint16_t);
+  const size_t blk_bytes = planes * d->block_k * d->head_dim * sizeof(uint16_t);
+  if (overlaps(k_cache, cache_bytes, k_blk, blk_bytes) || overlaps(k_cache, cache_bytes, v_blk, blk_bytes) ||
+      overlaps(v_cache, cache_bytes, k_blk, blk_bytes) || overlaps(v_cache, cache_bytes, v_blk, blk_bytes) ||
+      overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
+    return ORTHRUS_ERR_BAD_SHAPE;
+  const hipError_t e = launch_cache_commit_path(d->n_layers, d->batch, d->n_kv_heads, d->head_dim, d->block_k,
+                                                d->max_len, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len,
+                                                path, node_tokens, correction, next_anchor, tokens, n_tokens,
+                                                reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+size_t orthrus_topk_workspace_size(int32_t rows, int32_t vocab, int32_t m) {
+  if (rows < 1 || vocab < 1 || m < 1 || m > 32 || m > vocab || rows > 65535) return 0;
+  const size_t chunks = (size_t)topk_chunks(vocab);
+  return round_up((size_t)rows * chunks * ((size_t)m * 8 + 8), kAlign);
+}
+
+orthrus_status orthrus_topk_logprobs(int32_t rows, int32_t vocab, int32_t m, const float* logits, float* logp,
+                                     int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 1 || vocab < 1 || m < 1 || m > vocab) return ORTHRUS_ERR_BAD_SHAPE;
+  if (m > 32 || rows > 65535) return ORTHRUS_ERR_UNSUPPORTED;
+  if (!logits || !logp || !idx || !workspace) return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned4(logits) || !aligned4(logp) || !aligned4(idx) || !aligned16(workspace))
+    return ORTHRUS_ERR_MISALIGNED;
+  if (workspace_bytes < orthrus_topk_workspace_size(rows, vocab, m)) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+  const hipError_t e = launch_topk_logprobs(rows, vocab, m, logits, logp, idx, workspace,
+                                            reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status orthrus_tree_build(int32_t batch, int32_t depth, int32_t m, int32_t n_nodes, const float* logp,
+                                  const int32_t* tok, const int32_t* anchor, int32_t* parent, int32_t* tokens,
+                                  int32_t* node_depth, void* stream) {
+  if (batch < 1 || depth < 0 || m < 1 || n_nodes < 1) return ORTHRUS_ERR_BAD_SHAPE;
+  if (n_nodes > 64 || m > 1024 || depth > 65535) return ORTHRUS_ERR_UNSUPPORTED;
+  if ((depth > 0 && (!logp || !tok)) || !anchor || !parent || !tokens || !node_depth) return ORTHRUS_ERR_NULL_PTR;
+  if ((logp && !aligned4(logp)) || (tok && !aligned4(tok)) || !aligned4(anchor) || !aligned4(parent) ||
+      !aligned4(tokens) || !aligned4(node_depth))
+    return ORTHRUS_ERR_MISALIGNED;
+  const hipError_t e = launch_tree_build(batch, depth, m, n_nodes, logp, tok, anchor, parent, tokens, node_depth,
+                                         reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 

@@ -57,7 +57,7 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 // Cache range of one split of sequence b: [kstart, kend).
 struct SplitRange {
-  int kstart, kend, ncache, has_block, ntiles;
+  int kstart, kend, ncache, has_block, ntiles;  // block tiles: ncache .. ntiles-1 when has_block
 };
 
 __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int split) {
@@ -71,7 +71,7 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int 
   r.kend = min(r.kstart + chunk, L);
   r.ncache = r.kstart < r.kend ? (r.kend - r.kstart + kTileKeys - 1) / kTileKeys : 0;
   r.has_block = split == S - 1 ? 1 : 0;
-  r.ntiles = r.ncache + r.has_block;
+  r.ntiles = r.ncache + (r.has_block ? (a.block_k + kTileKeys - 1) / kTileKeys : 0);
   return r;
 }
 
@@ -159,7 +159,9 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
   }
 }
 
-template <int D, int NQB>
+// EXPL: the block tile takes the explicit per-row masks of a.blk_mask (a
+// separate instantiation, so the mode-masked launches keep their registers).
+template <int D, int NQB, bool EXPL>
 __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, AttnPlan plan, int direct) {
   constexpr int DCH = D / 8;               // 16-byte chunks per row
   constexpr int ROWB = D * 2;              // bytes per row
@@ -230,12 +232,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   auto load_tile = [&](int t, Stage& r) __attribute__((always_inline)) {
     const bool whole = t < nfull;
     const bool real = t < sr.ntiles;
-    const bool blk = sr.has_block && t == sr.ncache;
+    const bool blk = sr.has_block && t >= sr.ncache;  // block tile t - ncache
+    const int bt = t - sr.ncache;
     const int last = whole ? kTileKeys - 1
-                           : (!real ? 0 : (blk ? K : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys))) - 1);
+                           : (!real ? 0 : (blk ? min(kTileKeys, K - bt * kTileKeys)
+                                               : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys))) - 1);
     const size_t toff = (size_t)t * TILEB;
-    const uint8_t* kp = (whole || (real && !blk)) ? kc0 + toff : kblk;
-    const uint8_t* vp = (whole || (real && !blk)) ? vc0 + toff : (real ? vblk : kblk);
+    const size_t boff = blk && real ? (size_t)bt * TILEB : 0;
+    const uint8_t* kp = (whole || (real && !blk)) ? kc0 + toff : kblk + boff;
+    const uint8_t* vp = (whole || (real && !blk)) ? vc0 + toff : (real ? vblk + boff : kblk);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const uint32_t off = (uint32_t)(min(crow[c], last) * ROWB) + cchunk[c];
@@ -272,7 +277,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
 
   // Keys of tile t: nvalid(t) of them are real; the block tile is the last.
   auto tile_valid = [&](int t) __attribute__((always_inline)) {
-    return (sr.has_block && t == sr.ncache) ? K : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys));
+    return (sr.has_block && t >= sr.ncache) ? min(kTileKeys, K - (t - sr.ncache) * kTileKeys)
+                                            : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys));
   };
 
   // K fragments of both 32-key halves of the tile in `stage`.  Logical chunk
@@ -327,17 +333,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
         }
   };
   // Padded keys and, in the verify view, block keys after the row: -inf.
-  auto mask_scores = [&](f32x16 (&s)[2], int nvalid, bool block_tile) __attribute__((always_inline)) {
+  // Explicit masks: the visible block keys of this lane's row, shifted so
+  // that register r of half h tests bit 32h + 8*(r/4) + r%4 of the word.
+
+  auto mask_scores = [&](f32x16 (&s)[2], int nvalid, bool block_tile, int key0) __attribute__((always_inline)) {
     int lim = nvalid;
-    if (block_tile && a.causal) lim = min(lim, qrow_i + 1);
+    if (block_tile && a.causal) lim = min(lim, qrow_i + 1 - key0);
     // register r of half h holds key 32h + 8*(r/4) + 4*half + r%4; compare the
     // constant part against an opaque per-lane bound
     int rel = lim - 4 * half;
     asm volatile("" : "+v"(rel));
+    if (EXPL && block_tile) {
+      // the row's mask word is read here, once, rather than kept live through the loop
+      const int mrow = min(rg * plan.rows_per_wg + wrow, R - 1) % K;
+      const uint64_t m = a.blk_mask[(size_t)b * K + mrow] >> (4 * half);
+      const uint32_t emask_lo = (uint32_t)m, emask_hi = (uint32_t)(m >> 32);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[h][r] = (32 * h + 8 * (r >> 2) + (r & 3)) < rel ? s[h][r] : kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 32 * h + 8 * (r >> 2) + (r & 3);
+          const uint32_t bit = (h ? emask_hi : emask_lo) & (1u << (kk & 31));
+          s[h][r] = (kk < rel && bit) ? s[h][r] : kNegInf;
+        }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[h][r] = (32 * h + 8 * (r >> 2) + (r & 3)) < rel ? s[h][r] : kNegInf;
+    }
   };
   bf16x8 qf[NDS];
   // O^T += V^T P^T over the 64 keys of a tile (k-step 2h + tt).
@@ -444,8 +468,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
     VFrag vf;
     load_v(vst, vf);
     if (masked) {
-      const bool blk = sr.has_block && t == sr.ncache;
-      if (blk || tile_valid(t) < kTileKeys) mask_scores(cur, tile_valid(t), blk);
+      const bool blk = sr.has_block && t >= sr.ncache;
+      if (blk || tile_valid(t) < kTileKeys) mask_scores(cur, tile_valid(t), blk, (t - sr.ncache) * kTileKeys);
     }
     update_ref(cur, pprev, vf);
     float lsum = 0.0f;
@@ -597,7 +621,10 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a, A
 template <int D, int NQB>
 hipError_t launch_stream(const AttnArgs& a, const AttnPlan& p, int direct, hipStream_t stream) {
   dim3 grid(a.splits, p.row_groups, a.batch * a.n_kv_heads);
-  hipLaunchKernelGGL((attn_stream_kernel<D, NQB>), grid, dim3(kThreads), 0, stream, a, p, direct);
+  if (a.blk_mask != nullptr)
+    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, true>), grid, dim3(kThreads), 0, stream, a, p, direct);
+  else
+    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, false>), grid, dim3(kThreads), 0, stream, a, p, direct);
   return hipGetLastError();
 }
 

@@ -91,7 +91,106 @@ __global__ __launch_bounds__(kCommitThreads) void commit_state_kernel(const Comm
   a.cache_len[b] = t + r;
 }
 
+// ---- commit of an accepted tree path: rows path[0..a] (root first) of the
+// verify block go to cache rows t..t+a; the correction is always emitted and
+// becomes the next anchor.  A commit is refused (nothing written, length
+// kept, n_tokens 0) if t < 0, a outside [0, K-1], t + a + 1 > max_len, or a
+// path node outside [0, K).
+struct PathArgs {
+  CommitArgs c;
+  const int32_t* path;
+  const int32_t* node_tokens;
+};
+
+__device__ __forceinline__ int path_rows(const PathArgs& p, int b) {
+  const int t = p.c.cache_len[b], a = p.c.accept_len[b], K = p.c.block_k;
+  if (t < 0 || a < 0 || a > K - 1 || t > p.c.max_len - (a + 1)) return -1;
+  const int32_t* pth = p.path + (size_t)b * K;
+  for (int i = 0; i <= a; ++i)
+    if (pth[i] < 0 || pth[i] >= K) return -1;
+  return a + 1;
+}
+
+// grid.x = planes, grid.y = 2 (keys, values)
+__global__ __launch_bounds__(kCommitThreads) void commit_path_rows_kernel(const PathArgs p) {
+  const CommitArgs& a = p.c;
+  const int plane = blockIdx.x;
+  const int b = (plane / a.n_kv_heads) % a.batch;
+  const int r = path_rows(p, b);
+  if (r <= 0) return;
+  const int t = a.cache_len[b];
+  const bool vals = blockIdx.y != 0;
+  const uint16_t* src = (vals ? a.v_blk : a.k_blk) + (size_t)plane * a.block_k * a.head_dim;
+  uint16_t* dst = (vals ? a.v_cache : a.k_cache) + ((size_t)plane * a.max_len + t) * a.head_dim;
+  const int32_t* pth = p.path + (size_t)b * a.block_k;
+  const int vpr = a.head_dim / 8;  // 16-byte vectors per row
+  for (int n = threadIdx.x; n < r * vpr; n += kCommitThreads) {
+    const int i = n / vpr, c = n % vpr;
+    reinterpret_cast<uint4*>(dst + (size_t)i * a.head_dim)[c] =
+        reinterpret_cast<const uint4*>(src + (size_t)pth[i] * a.head_dim)[c];
+  }
+}
+
+__global__ __launch_bounds__(kCommitThreads) void commit_path_state_kernel(const PathArgs p) {
+  const CommitArgs& a = p.c;
+  const int b = blockIdx.x * kCommitThreads + threadIdx.x;
+  if (b >= a.batch) return;
+  const int K = a.block_k;
+  const int r = path_rows(p, b);
+  int32_t* tok = a.tokens + (size_t)b * K;
+  if (r < 0) {
+    for (int i = 0; i < K; ++i) tok[i] = -1;
+    a.n_tokens[b] = 0;
+    a.next_anchor[b] = -1;
+    return;
+  }
+  const int32_t* pth = p.path + (size_t)b * K;
+  const int32_t* nt = p.node_tokens + (size_t)b * K;
+  const int acc = r - 1;
+  for (int i = 0; i < acc; ++i) tok[i] = nt[pth[i + 1]];
+  const int corr = a.correction[b];
+  tok[acc] = corr;
+  for (int i = acc + 1; i < K; ++i) tok[i] = -1;
+  a.n_tokens[b] = r;
+  a.next_anchor[b] = corr;
+  a.cache_len[b] = a.cache_len[b] + r;
+}
+
 }  // namespace
+
+hipError_t launch_cache_commit_path(int n_layers, int batch, int n_kv_heads, int head_dim, int block_k,
+                                    int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,
+                                    const uint16_t* v_blk, int32_t* cache_len, const int32_t* accept_len,
+                                    const int32_t* path, const int32_t* node_tokens, const int32_t* correction,
+                                    int32_t* next_anchor, int32_t* tokens, int32_t* n_tokens, hipStream_t stream) {
+  PathArgs p{};
+  CommitArgs& a = p.c;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.cache_len = cache_len;
+  a.accept_len = accept_len;
+  a.correction = correction;
+  a.cand = nullptr;
+  a.next_anchor = next_anchor;
+  a.tokens = tokens;
+  a.n_tokens = n_tokens;
+  a.planes = n_layers * batch * n_kv_heads;
+  a.batch = batch;
+  a.n_kv_heads = n_kv_heads;
+  a.head_dim = head_dim;
+  a.block_k = block_k;
+  a.max_len = max_len;
+  p.path = path;
+  p.node_tokens = node_tokens;
+  hipLaunchKernelGGL(commit_path_rows_kernel, dim3(a.planes, 2), dim3(kCommitThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(commit_path_state_kernel, dim3((batch + kCommitThreads - 1) / kCommitThreads),
+                     dim3(kCommitThreads), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head_dim, int block_k,
                                int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,

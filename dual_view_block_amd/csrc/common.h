@@ -55,6 +55,9 @@ struct AttnArgs {
   // > 0: sequence b attends to cache rows [0, b*len_step) and cache_len is
   // not read (causal rows processed in groups of block_k)
   int len_step;
+  // Explicit block masks (block_k <= 64): bit j of blk_mask[b*block_k + i]
+  // set = block key j visible to block row i; NULL = the mode's mask.
+  const uint64_t* blk_mask;
 };
 
 // Contiguous decode layouts: q/out [B,Hq,K,D], lse [B,Hq,K], blocks
@@ -70,6 +73,7 @@ inline void set_decode_strides(AttnArgs& a) {
   a.c_gs = (long long)a.max_len * D;
   a.c_bs = (long long)a.n_kv_heads * a.max_len * D;
   a.len_step = 0;
+  a.blk_mask = nullptr;
 }
 
 // Splits a launch uses on a device with `cus` compute units.
@@ -142,5 +146,31 @@ int kl_chunks(int vocab, int dtype_bytes, bool vec);
 hipError_t launch_forward_kl(int rows, int vocab, int dtype_bytes, bool vec, const void* target,
                              const void* draft, float* kl, void* grad, float scale, float* part, float* lse,
                              int groups, hipStream_t stream);
+
+// Commit of an accepted tree path (rows path[0..a]); the same two-launch shape.
+hipError_t launch_cache_commit_path(int n_layers, int batch, int n_kv_heads, int head_dim, int block_k,
+                                    int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,
+                                    const uint16_t* v_blk, int32_t* cache_len, const int32_t* accept_len,
+                                    const int32_t* path, const int32_t* node_tokens, const int32_t* correction,
+                                    int32_t* next_anchor, int32_t* tokens, int32_t* n_tokens, hipStream_t stream);
+
+// Greedy consensus along a draft tree (argmax partials, then one wave per
+// sequence walks the tree); the greedy workspace.
+hipError_t launch_consensus_tree_greedy(int batch, int block_k, int vocab, const float* logits,
+                                        const int32_t* tokens, const int32_t* parent, int32_t* accept_len,
+                                        int32_t* path, int32_t* correction, int32_t* row_argmax, void* workspace,
+                                        const ConsensusPlan& plan, hipStream_t stream);
+
+// ---------------------------------------------------------------- tree drafting
+// Ancestor-or-self masks (uint64 per node) of draft trees, K <= 64.
+hipError_t launch_tree_masks(int batch, int block_k, const int32_t* parent, uint64_t* mask, hipStream_t stream);
+// Top-m logits and their log-probabilities per row.
+int topk_chunks(int vocab);
+hipError_t launch_topk_logprobs(int rows, int vocab, int m, const float* logits, float* logp, int32_t* idx,
+                                void* workspace, hipStream_t stream);
+// Best-first draft trees (one wave per sequence), n_nodes <= 64.
+hipError_t launch_tree_build(int batch, int depth, int m, int n_nodes, const float* logp, const int32_t* tok,
+                             const int32_t* anchor, int32_t* parent, int32_t* tokens, int32_t* node_depth,
+                             hipStream_t stream);
 
 }  // namespace orthrus

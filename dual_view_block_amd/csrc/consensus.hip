@@ -19,38 +19,14 @@
 // target T = floor(m*S/2^24) (128-bit product) and scans inside it.  Integer
 // sums make the pick independent of reduction order.
 #include "common.h"
+#include "order_keys.h"
 
 namespace orthrus {
 namespace {
 
+using namespace keys;
+
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (x != x) return 0xFFFFFFFFu;  // NaN ranks above every number
-  if (x == 0.0f) u = 0u;           // -0 == +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ unsigned long long pack_key(float x, uint32_t idx) {
-  return ((unsigned long long)order_key(x) << 32) | (unsigned long long)(0xFFFFFFFFu - idx);
-}
-
-__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
-  return a > b ? a : b;
-}
-
-__device__ __forceinline__ unsigned long long wave_max64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = umax64(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ unsigned long long wave_sum64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
 
 // ---------------------------------------------------------------- greedy --
 __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* __restrict__ logits,
@@ -90,23 +66,77 @@ __global__ __launch_bounds__(64) void greedy_finalize_kernel(int block_k, int ch
                                                              const int32_t* cand, int32_t* accept_len,
                                                              int32_t* row_argmax, int32_t* correction) {
   const int b = blockIdx.x;
-  const int i = threadIdx.x;
-  int am = -1;
-  bool mismatch = false;
-  if (i < block_k) {
-    const unsigned long long* pp = part + ((size_t)b * block_k + i) * chunks;
-    unsigned long long m = 0;
-    for (int c = 0; c < chunks; ++c) m = umax64(m, pp[c]);
-    am = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
-    mismatch = cand[(size_t)b * block_k + i] != am;
-    if (row_argmax != nullptr) row_argmax[(size_t)b * block_k + i] = am;
+  // rows in groups of 64 (one per lane); the first group with a mismatch ends the scan
+  int a = block_k, am_a = -1;
+  for (int base = 0; base < block_k; base += 64) {
+    const int i = base + (int)threadIdx.x;
+    int am = -1;
+    bool mismatch = false;
+    if (i < block_k) {
+      const unsigned long long* pp = part + ((size_t)b * block_k + i) * chunks;
+      unsigned long long m = 0;
+      for (int c = 0; c < chunks; ++c) m = umax64(m, pp[c]);
+      am = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+      mismatch = cand[(size_t)b * block_k + i] != am;
+      if (row_argmax != nullptr) row_argmax[(size_t)b * block_k + i] = am;
+    }
+    const unsigned long long mm = __ballot(mismatch);
+    if (mm && a == block_k) {
+      const int lane = __builtin_ctzll(mm);
+      a = base + lane;
+      am_a = __shfl(am, lane);
+    }
   }
-  const unsigned long long mm = __ballot(mismatch);
-  const int a = mm ? __builtin_ctzll(mm) : block_k;
-  const int am_a = __shfl(am, a < block_k ? a : 0);
-  if (i == 0) {
+  if (threadIdx.x == 0) {
     accept_len[b] = a;
     correction[b] = a < block_k ? am_a : -1;
+  }
+}
+
+// ------------------------------------------------------------ tree greedy --
+// One wave per sequence: the argmax of every node's row (nodes lane and
+// lane + 64), then the walk from the root: at node cur the next node is the
+// lowest-index node c > cur with parent[c] == cur and token[c] equal to the
+// argmax of row cur (one ballot per step); the correction is the argmax of the
+// last node's row.
+__global__ __launch_bounds__(64) void tree_finalize_kernel(int K, int chunks, const unsigned long long* part,
+                                                           const int32_t* tokens, const int32_t* parent,
+                                                           int32_t* accept_len, int32_t* path, int32_t* correction,
+                                                           int32_t* row_argmax) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  int am[2] = {-1, -1}, par[2] = {-2, -2}, tok[2] = {-1, -1};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    if (i < K) {
+      const unsigned long long* pp = part + ((size_t)b * K + i) * chunks;
+      unsigned long long m = 0;
+      for (int c = 0; c < chunks; ++c) m = umax64(m, pp[c]);
+      am[h] = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+      par[h] = parent[(size_t)b * K + i];
+      tok[h] = tokens[(size_t)b * K + i];
+      if (row_argmax != nullptr) row_argmax[(size_t)b * K + i] = am[h];
+    }
+  }
+  int32_t* pth = path + (size_t)b * K;
+  if (lane == 0) pth[0] = 0;
+  int cur = 0, a = 0;
+  for (int step = 1; step < K; ++step) {
+    const int want = cur < 64 ? __shfl(am[0], cur) : __shfl(am[1], cur - 64);
+    const bool c0 = lane > cur && lane < K && par[0] == cur && tok[0] == want;
+    const bool c1 = lane + 64 > cur && lane + 64 < K && par[1] == cur && tok[1] == want;
+    const unsigned long long m0 = __ballot(c0), m1 = __ballot(c1);
+    if (!m0 && !m1) break;
+    cur = m0 ? __builtin_ctzll(m0) : 64 + __builtin_ctzll(m1);
+    ++a;
+    if (lane == 0) pth[a] = cur;
+  }
+  const int last_am = cur < 64 ? __shfl(am[0], cur) : __shfl(am[1], cur - 64);
+  for (int i = a + 1 + lane; i < K; i += 64) pth[i] = -1;
+  if (lane == 0) {
+    accept_len[b] = a;
+    correction[b] = last_am;
   }
 }
 
@@ -124,21 +154,24 @@ __global__ __launch_bounds__(64) void sample_accept_kernel(int block_k, int voca
                                                            int32_t* accept_len, int32_t* correction,
                                                            int32_t* ws_a) {
   const int b = blockIdx.x;
-  const int i = threadIdx.x;
-  bool reject = false;
-  if (i < block_k) {
-    const size_t row = (size_t)b * block_k + i;
-    const int c = cand[row];
-    const bool valid = c >= 0 && c < vocab;
-    const float pv = valid ? p[row * vocab + c] : 0.0f;
-    const float qv = valid ? q[row * vocab + c] : 0.0f;
-    const float u = uniforms[(size_t)b * (block_k + 1) + i];
-    const bool acc = valid && (__dmul_rn((double)u, (double)qv) < (double)pv);
-    reject = !acc;
+  int a = block_k;
+  for (int base = 0; base < block_k && a == block_k; base += 64) {  // groups of 64 rows
+    const int i = base + (int)threadIdx.x;
+    bool reject = false;
+    if (i < block_k) {
+      const size_t row = (size_t)b * block_k + i;
+      const int c = cand[row];
+      const bool valid = c >= 0 && c < vocab;
+      const float pv = valid ? p[row * vocab + c] : 0.0f;
+      const float qv = valid ? q[row * vocab + c] : 0.0f;
+      const float u = uniforms[(size_t)b * (block_k + 1) + i];
+      const bool acc = valid && (__dmul_rn((double)u, (double)qv) < (double)pv);
+      reject = !acc;
+    }
+    const unsigned long long mm = __ballot(reject);
+    if (mm) a = base + __builtin_ctzll(mm);
   }
-  const unsigned long long mm = __ballot(reject);
-  const int a = mm ? __builtin_ctzll(mm) : block_k;
-  if (i == 0) {
+  if (threadIdx.x == 0) {
     accept_len[b] = a;
     ws_a[b] = a;
     if (a >= block_k) correction[b] = -1;
@@ -295,6 +328,23 @@ hipError_t launch_consensus_greedy(int batch, int block_k, int vocab, const floa
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(greedy_finalize_kernel, dim3(batch), dim3(64), 0, stream, block_k, chunks, part,
                      cand, accept_len, row_argmax, correction);
+  return hipGetLastError();
+}
+
+hipError_t launch_consensus_tree_greedy(int batch, int block_k, int vocab, const float* logits,
+                                        const int32_t* tokens, const int32_t* parent, int32_t* accept_len,
+                                        int32_t* path, int32_t* correction, int32_t* row_argmax, void* workspace,
+                                        const ConsensusPlan& plan, hipStream_t stream) {
+  const int chunks = plan.greedy_chunks;
+  int chunk_len = (vocab + chunks - 1) / chunks;
+  chunk_len = (chunk_len + 3) & ~3;  // as for the greedy rule: whole 16-byte groups per chunk
+  auto* part = reinterpret_cast<unsigned long long*>(workspace);
+  hipLaunchKernelGGL(argmax_partial_kernel, dim3(chunks, batch * block_k), dim3(kThreads), 0, stream, logits,
+                     vocab, chunk_len, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tree_finalize_kernel, dim3(batch), dim3(64), 0, stream, block_k, chunks, part, tokens, parent,
+                     accept_len, path, correction, row_argmax);
   return hipGetLastError();
 }
 

@@ -48,11 +48,14 @@ typedef enum {
 /* Which block keys a block row may see (paper notes §3.2 and §4.1):
  * DIFF_BIDIR   -- diffusion view: every block row sees all K block keys
  *                 (anchor + K-1 mask positions attend to each other);
- * VERIFY_CAUSAL -- AR verify pass: block row i sees block keys j <= i.
- * In both modes every row sees all cached positions [0, cache_len[b]). */
+ * VERIFY_CAUSAL -- AR verify pass: block row i sees block keys j <= i;
+ * EXPLICIT     -- a given set per row (orthrus_block_attn_masked only): tree
+ *                 verification (ancestors and self) and ragged blocks.
+ * In every mode every row sees all cached positions [0, cache_len[b]). */
 typedef enum {
   ORTHRUS_MASK_DIFF_BIDIR = 0,
-  ORTHRUS_MASK_VERIFY_CAUSAL = 1
+  ORTHRUS_MASK_VERIFY_CAUSAL = 1,
+  ORTHRUS_MASK_EXPLICIT = 2
 } orthrus_mask_mode;
 
 typedef struct {
@@ -60,7 +63,7 @@ typedef struct {
   int32_t n_q_heads;     /* Hq >= 1, a multiple of n_kv_heads */
   int32_t n_kv_heads;    /* Hkv >= 1; q head h reads KV head h / (Hq / Hkv) */
   int32_t head_dim;      /* D, 64 or 128 (other values: ORTHRUS_ERR_UNSUPPORTED) */
-  int32_t block_k;       /* K, 1..32 block positions (anchor + K-1 masks) */
+  int32_t block_k;       /* K, 1..128 block positions (anchor + K-1 masks) */
   int32_t max_len;       /* cache capacity per sequence = row stride of the cache */
   float softmax_scale;   /* 0 -> 1/sqrt(D) */
 } orthrus_attn_desc;
@@ -125,6 +128,19 @@ orthrus_status orthrus_block_attn_verify(const orthrus_attn_desc* d, const uint1
                                          void* workspace, size_t workspace_bytes,
                                          void* stream);
 
+/* Block attention with an explicit per-row block mask (tree verification,
+ * paper notes §7.4-7.5; ragged blocks): block key j is visible to block row i
+ * of sequence b iff bit j of block_mask[b*K + i] is set (uint64 [B, K] on the
+ * device; K <= 64, else ORTHRUS_ERR_UNSUPPORTED).  Every row also sees the
+ * whole cache [0, cache_len[b]); a row that sees no key at all gets out = 0
+ * and lse = -inf.  Everything else is orthrus_block_attn. */
+orthrus_status orthrus_block_attn_masked(const orthrus_attn_desc* d, const uint16_t* q,
+                                         const uint16_t* k_blk, const uint16_t* v_blk,
+                                         const uint16_t* k_cache, const uint16_t* v_cache,
+                                         const int32_t* cache_len, const uint64_t* block_mask,
+                                         uint16_t* out, float* lse, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
 /* The two halves of orthrus_block_attn, for callers that schedule or time
  * them separately (or, later, combine partials from several cache shards).
  * orthrus_block_attn_partial streams the cache and the block and leaves one
@@ -154,7 +170,7 @@ size_t orthrus_consensus_workspace_size(int32_t batch, int32_t block_k, int32_t 
  *   correction int32 [B]       argmax of row a if a < K, else -1 (no bonus)
  * argmax: lowest index among equal maxima; NaN ranks above every number (first
  * NaN wins); -0 equals +0.  Results are bit-exact (comparisons only).
- * Sizes: 1 <= B, 1 <= K <= 32, 1 <= V < 2^31. */
+ * Sizes: 1 <= B, 1 <= K <= 128, 1 <= V < 2^31. */
 orthrus_status orthrus_consensus_greedy(int32_t batch, int32_t block_k, int32_t vocab,
                                         const float* logits, const int32_t* cand,
                                         int32_t* accept_len, int32_t* row_argmax,
@@ -327,6 +343,81 @@ orthrus_status orthrus_train_attn_bwd(const orthrus_train_attn_desc* d, const ui
                                       const float* lse_diff, const uint16_t* d_out_diff,
                                       uint16_t* dq_diff, uint16_t* dk_diff, uint16_t* dv_diff,
                                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * Tree verification (paper notes §7.4-7.5 and §9.6: verify a tree of
+ * candidate prefixes built from the K diffusion marginals, DDTree style; a
+ * dynamic block size is the same machinery with unused nodes).  A draft tree
+ * has K nodes: node 0 is the anchor, node i > 0 has parent[b*K + i] < i and a
+ * token; parent -1 marks an unused node.  Verify row i is the AR distribution
+ * after the path root..i, so the verify attention lets row i see the block
+ * keys of its ancestors and itself (orthrus_tree_masks +
+ * orthrus_block_attn_masked).
+ * ------------------------------------------------------------------------ */
+
+/* Top-m logits of every row and their log-probabilities (the per-position
+ * marginals a draft tree is built from): idx = the m largest logits (ties:
+ * lower index first), logp = logit - ln sum_v exp(logit_v), descending.
+ *   logits fp32 [rows, V];  logp fp32 [rows, m];  idx int32 [rows, m]
+ * 1 <= m <= min(32, V); rows <= 65535.  Workspace: orthrus_topk_workspace_size
+ * (0 if the sizes are invalid). */
+size_t orthrus_topk_workspace_size(int32_t rows, int32_t vocab, int32_t m);
+orthrus_status orthrus_topk_logprobs(int32_t rows, int32_t vocab, int32_t m, const float* logits,
+                                     float* logp, int32_t* idx, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Best-first draft trees of n_nodes (<= 64) nodes from per-depth marginals:
+ *   logp fp32 [B, depth, m] (descending per depth), tok int32 [B, depth, m]:
+ *   the top-m tokens of block positions 1..depth;  anchor int32 [B]
+ *   parent, tokens, node_depth int32 [B, n_nodes] (written)
+ * score(child of node p with rank r) = score(p) + logp[depth(p)][r] in fp32,
+ * score(root) = 0; the tree takes the best candidates one at a time (higher
+ * score, then lower parent index, then lower rank) -- the n_nodes-1
+ * highest-scoring prefixes.  Nodes that cannot be made (too few candidates)
+ * get parent -1 and token -1. */
+orthrus_status orthrus_tree_build(int32_t batch, int32_t depth, int32_t m, int32_t n_nodes,
+                                  const float* logp, const int32_t* tok, const int32_t* anchor,
+                                  int32_t* parent, int32_t* tokens, int32_t* node_depth, void* stream);
+
+/* Ancestor-or-self bitmask of every node (bit j of mask[b*K + i] set iff node
+ * j lies on the path root..i), the block_mask of the tree-verify attention.
+ * parent int32 [B, K], mask uint64 [B, K] (8-byte aligned); K <= 64. */
+orthrus_status orthrus_tree_masks(int32_t batch, int32_t block_k, const int32_t* parent,
+                                  uint64_t* mask, void* stream);
+
+/* Greedy consensus along a draft tree: from the root, move to the child
+ * (lowest node index first, children after their parent) whose token equals
+ * the AR argmax of the current node's row; stop when none does.
+ *   logits fp32 [B, K, V] (row i: AR logits after the path to node i)
+ *   tokens, parent int32 [B, K]
+ *   accept_len int32 [B]   a = accepted nodes after the root
+ *   path int32 [B, K]      root, n_1, .., n_a, then -1
+ *   correction int32 [B]   argmax of the last accepted node's row (always
+ *                          emitted: a cycle emits a + 1 tokens)
+ *   row_argmax int32 [B, K] (may be NULL)
+ * Argmax ties as orthrus_consensus_greedy.  K <= 128.  Workspace:
+ * orthrus_consensus_workspace_size. */
+orthrus_status orthrus_consensus_tree_greedy(int32_t batch, int32_t block_k, int32_t vocab,
+                                             const float* logits, const int32_t* tokens,
+                                             const int32_t* parent, int32_t* accept_len,
+                                             int32_t* path, int32_t* correction, int32_t* row_argmax,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Commit an accepted tree path: verify rows path[b, 0..a] (root first) of
+ * every layer and KV head go to cache rows t..t+a (t = cache_len[b]); the
+ * length grows by a + 1 in place; tokens[b] = the tokens of nodes
+ * path[1..a], then the correction (-1 after); n_tokens = a + 1; the
+ * correction becomes next_anchor.  Refused per sequence (nothing written,
+ * n_tokens 0, -1 outputs) if t < 0, a outside [0, K-1], t + a + 1 > max_len or
+ * a path node outside [0, K).  Layouts, aliasing rules and errors as
+ * orthrus_cache_commit. */
+orthrus_status orthrus_cache_commit_path(const orthrus_commit_desc* d, uint16_t* k_cache,
+                                         uint16_t* v_cache, const uint16_t* k_blk,
+                                         const uint16_t* v_blk, int32_t* cache_len,
+                                         const int32_t* accept_len, const int32_t* path,
+                                         const int32_t* node_tokens, const int32_t* correction,
+                                         int32_t* next_anchor, int32_t* tokens, int32_t* n_tokens,
+                                         void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* orthrus_status_string(orthrus_status s);

@@ -311,3 +311,69 @@ def train_attn_inputs(n_q_heads: int, n_kv_heads: int, seq_len: int, n_blocks: i
     out["anchors"] = torch.as_tensor(anchors, dtype=torch.int32).to(device)
     out["block_k"] = K
     return out
+
+
+def random_trees(batch: int, n_nodes: int, seed: int = 0, unused_frac: float = 0.0) -> torch.Tensor:
+    """int32 [B, n] draft-tree parents: node 0 is the root (-1); node i > 0
+    picks a uniform parent among the used nodes before it, or is unused (-1)
+    with probability ``unused_frac``."""
+    g = _gen(seed * 17 + 3, "cpu")
+    par = torch.full((batch, n_nodes), -1, dtype=torch.int32)
+    u = torch.rand((batch, n_nodes), generator=g)
+    pick = torch.rand((batch, n_nodes), generator=g)
+    for b in range(batch):
+        used = [0]
+        for i in range(1, n_nodes):
+            if float(u[b, i]) < unused_frac:
+                continue
+            par[b, i] = used[int(float(pick[b, i]) * len(used))]
+            used.append(i)
+    return par
+
+
+def tree_verify_logits(parent: torch.Tensor, tokens: torch.Tensor, vocab: int, accept_rate: float = 0.7,
+                       sigma: float = 3.0, seed: int = 0) -> torch.Tensor:
+    """fp32 [B, n, V] verify logits for draft trees with a planted top token
+    per node row: with probability ``accept_rate`` the token of one of the
+    node's children (uniform among them), else a uniform token.  Rows are
+    N(0, sigma) clamped to +-6 sigma with the planted token at 6 sigma + 1, so
+    each row's argmax is known by construction."""
+    g = _gen(seed * 29 + 11, "cpu")
+    B, n = parent.shape
+    s = float(sigma)
+    logits = (torch.randn((B, n, vocab), generator=g) * s).clamp_(-6 * s, 6 * s)
+    coin = torch.rand((B, n), generator=g)
+    pick = torch.rand((B, n), generator=g)
+    rand_tok = torch.randint(0, vocab, (B, n), generator=g)
+    for b in range(B):
+        kids = {i: [] for i in range(n)}
+        for i in range(1, n):
+            p = int(parent[b, i])
+            if 0 <= p < i:
+                kids[p].append(i)
+        for i in range(n):
+            if kids[i] and float(coin[b, i]) < accept_rate:
+                top = int(tokens[b, kids[i][int(float(pick[b, i]) * len(kids[i]))]])
+            else:
+                top = int(rand_tok[b, i])
+            logits[b, i, top] = 6 * s + 1
+    return logits
+
+
+def draft_marginals(batch: int, depth: int, m: int, vocab: int, seed: int = 0, ties: bool = False):
+    """Per-depth top-m marginals for tree building: logp fp32 [B, depth, m]
+    descending and <= 0 (the top entries of a uniformly drawn probability
+    vector over m + 4 outcomes, logged),
+    tok int32 [B, depth, m] distinct tokens per depth.  With ``ties`` some
+    log-probs repeat, exercising the tie rule."""
+    g = _gen(seed * 37 + 5, "cpu")
+    # a uniform random probability vector over m + 4 outcomes (normalised exponentials)
+    e = -torch.log(torch.rand((batch, depth, m + 4), generator=g, dtype=torch.float64).clamp_min(1e-300))
+    p = e / e.sum(dim=-1, keepdim=True)
+    top = torch.sort(p, dim=-1, descending=True).values[..., :m]
+    logp = torch.log(top).to(torch.float32)
+    if ties:
+        logp[:, :, 1::3] = logp[:, :, 0::3][:, :, :logp[:, :, 1::3].shape[2]]
+        logp = torch.sort(logp, dim=-1, descending=True).values
+    tok = torch.stack([torch.randperm(vocab, generator=g)[:m] for _ in range(batch * depth)]).reshape(batch, depth, m)
+    return logp, tok.to(torch.int32)

@@ -65,7 +65,8 @@ def test_workspace_query_depends_on_shapes_only():
     assert lib.orthrus_attn_workspace_size(ctypes.byref(_desc(head_dim=96))) == 0
     assert lib.orthrus_attn_num_splits(ctypes.byref(_desc(n_q_heads=30))) == -1
     assert lib.orthrus_consensus_workspace_size(1, 32, 151936) > 0
-    assert lib.orthrus_consensus_workspace_size(1, 33, 151936) == 0
+    assert lib.orthrus_consensus_workspace_size(1, 128, 151936) > 0
+    assert lib.orthrus_consensus_workspace_size(1, 129, 151936) == 0
 
 
 def _attn_call(desc, mode=0, ptrs=None, ws_bytes=1 << 30):
@@ -86,8 +87,9 @@ def _attn_call(desc, mode=0, ptrs=None, ws_bytes=1 << 30):
     (dict(desc=_desc(softmax_scale=float("nan"))), _lib.ORTHRUS_ERR_BAD_SHAPE),
     (dict(desc=_desc(softmax_scale=-1.0)), _lib.ORTHRUS_ERR_BAD_SHAPE),
     (dict(desc=_desc(head_dim=96)), _lib.ORTHRUS_ERR_UNSUPPORTED),
-    (dict(desc=_desc(block_k=33)), _lib.ORTHRUS_ERR_UNSUPPORTED),
-    (dict(desc=_desc(), mode=2), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(block_k=129)), _lib.ORTHRUS_ERR_UNSUPPORTED),
+    (dict(desc=_desc(), mode=3), _lib.ORTHRUS_ERR_BAD_SHAPE),
+    (dict(desc=_desc(), mode=2), _lib.ORTHRUS_ERR_NULL_PTR),   # explicit masks need orthrus_block_attn_masked
     (dict(desc=_desc(), ptrs=dict(kc=None)), _lib.ORTHRUS_ERR_NULL_PTR),
     (dict(desc=_desc(), ptrs=dict(lens=None)), _lib.ORTHRUS_ERR_NULL_PTR),
     (dict(desc=_desc(), ptrs=dict(q=4104)), _lib.ORTHRUS_ERR_MISALIGNED),
@@ -103,7 +105,7 @@ def test_consensus_argument_checks():
     lib = _lib.load()
     P = 4096
     assert lib.orthrus_consensus_greedy(0, 4, 10, P, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
-    assert lib.orthrus_consensus_greedy(1, 40, 10, P, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_consensus_greedy(1, 129, 10, P, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_UNSUPPORTED
     assert lib.orthrus_consensus_greedy(1, 4, 10, None, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_NULL_PTR
     assert lib.orthrus_consensus_greedy(1, 4, 10, P + 4, P, P, P, P, P, 1 << 20, None) == _lib.ORTHRUS_ERR_MISALIGNED
     assert lib.orthrus_consensus_greedy(1, 4, 10, P, P, P, P, P, P, 1, None) == _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL
@@ -167,6 +169,37 @@ def test_forward_kl_argument_checks():
     assert f(4, 10, BF, P + 2, Q, K, G, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_MISALIGNED
     assert f(4, 10, BF, P, Q, K, G + 8, 1.0, W, ok, None) == _lib.ORTHRUS_ERR_MISALIGNED
     assert f(8192, 151936, BF, P, Q, K, G, 1.0, W, ok - 1, None) == _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_tree_argument_checks():
+    lib = _lib.load()
+    P, W = 4096, 8192
+    desc = _lib.AttnDesc(1, 32, 8, 128, 65, 4096, 0.0)
+    assert lib.orthrus_block_attn_masked(ctypes.byref(desc), P, P, P, P, P, P, P, P, P, W, 1 << 30, None) == \
+        _lib.ORTHRUS_ERR_UNSUPPORTED                       # explicit masks: K <= 64
+    desc = _lib.AttnDesc(1, 32, 8, 128, 32, 4096, 0.0)
+    assert lib.orthrus_block_attn_masked(ctypes.byref(desc), P, P, P, P, P, P, None, P, P, W, 1 << 30, None) == \
+        _lib.ORTHRUS_ERR_NULL_PTR
+    assert lib.orthrus_tree_masks(1, 65, P, P, None) == _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_tree_masks(1, 8, P, P + 4, None) == _lib.ORTHRUS_ERR_MISALIGNED
+    assert lib.orthrus_tree_masks(0, 8, P, P, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert lib.orthrus_topk_workspace_size(4, 100, 33) == 0 and lib.orthrus_topk_workspace_size(4, 10, 11) == 0
+    assert lib.orthrus_topk_workspace_size(32, 151936, 8) > 0
+    assert lib.orthrus_topk_logprobs(4, 10, 11, P, P, P, W, 1 << 20, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert lib.orthrus_topk_logprobs(4, 100, 33, P, P, P, W, 1 << 20, None) == _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_topk_logprobs(4, 100, 8, P, P, P, W, 1, None) == _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL
+    assert lib.orthrus_tree_build(1, 4, 2, 65, P, P, P, P, P, P, None) == _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_tree_build(1, 4, 2, 0, P, P, P, P, P, P, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert lib.orthrus_tree_build(1, 4, 2, 8, None, P, P, P, P, P, None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert lib.orthrus_consensus_tree_greedy(1, 129, 10, P, P, P, P, P, P, P, W, 1 << 20, None) == \
+        _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_consensus_tree_greedy(1, 8, 10, P, P, None, P, P, P, P, W, 1 << 20, None) == \
+        _lib.ORTHRUS_ERR_NULL_PTR
+    c = _lib.CommitDesc(1, 1, 1, 64, 4, 256)
+    assert lib.orthrus_cache_commit_path(ctypes.byref(c), 1 << 40, 2 << 40, 3 << 40, 4 << 40, P, P, None, P, P, P,
+                                         P, P, None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert lib.orthrus_cache_commit_path(ctypes.byref(c), 1 << 40, 1 << 40, 3 << 40, 4 << 40, P, P, P, P, P, P,
+                                         P, P, None) == _lib.ORTHRUS_ERR_BAD_SHAPE
 
 
 def test_valid_call_without_gpu_reports_hip_error():
