@@ -42,7 +42,7 @@ def _parse():
     ap.add_argument("--cache-len", type=int, default=None)
     ap.add_argument("--block-k", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--k-sweep", default="1,4,8,16,32",
+    ap.add_argument("--k-sweep", default="1,4,8,16,32,64,128",
                     help="block sizes timed for the latency-vs-K line ('' to skip)")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -53,6 +53,10 @@ def _parse():
     ap.add_argument("--cycle-sets", type=int, default=32,
                     help="distinct input sets the cycles rotate through (one graph round); their "
                          "first-mismatch indices are the quantiles of the acceptance law")
+    ap.add_argument("--tree-cycles", type=int, default=32,
+                    help="synthetic tree-verification cycles timed (0 to skip): per cycle the diffusion "
+                         "attention of every layer, top-m marginals, a best-first draft tree, its masks, the "
+                         "tree-masked verify attention of every layer, tree consensus and the path commit")
     ap.add_argument("--kl-rows", type=int, default=8192,
                     help="rows of the forward-KL measurement (256 blocks x K = 32 diffusion positions "
                          "of one packed training sequence; 0 to skip)")
@@ -405,6 +409,79 @@ def time_forward_kl(device, rows: int, vocab: int, reps: int = 10):
     return out
 
 
+def _time_calls(fn, reps: int, stream) -> float:
+    """Average µs of `fn()` over `reps` back-to-back calls (HIP events on `stream`)."""
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def time_tree_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int = 4, m: int = 4):
+    """Tree-verification cycles through dual_view_block_amd.cycle.TreeDecodeCycles
+    (one round of `n_sets` cycles captured in a HIP graph and replayed), plus
+    the time of each tree-specific call.  Synthetic inputs: random N(0, 3)
+    diffusion and verify logits (the tokens accepted per cycle depend on the
+    model and are not reported as a figure of merit)."""
+    import torch
+
+    import dual_view_block_amd as dvb
+    from dual_view_block_amd.cycle import TreeDecodeCycles
+    from synth import cache_lengths, view_inputs
+
+    K, V = w.block_k, w.vocab
+    g = torch.Generator(device=device)
+    g.manual_seed(17)
+    sets = []
+    for si in range(n_sets):
+        ws = w.replace(seed=w.seed * 97 + si)
+        sets.append({"diff": [view_inputs(ws, l, "diff", device) for l in range(w.layers)],
+                     "verify": [view_inputs(ws, l, "verify", device) for l in range(w.layers)],
+                     "diff_logits": torch.randn((w.batch * (K - 1), V), generator=g, device=device) * 3,
+                     "verify_logits": torch.randn((w.batch, K, V), generator=g, device=device) * 3})
+    lens = cache_lengths(w, device)
+    anchor = torch.zeros(w.batch, dtype=torch.int32, device=device)
+    drv = TreeDecodeCycles(kc_all, vc_all, lens, anchor, sets, m=m)
+    drv.run(n_sets)
+    torch.cuda.synchronize()
+    drv.capture()
+    torch.cuda.synchronize()
+    rounds = max(1, n_cycles // n_sets)
+    stream = torch.cuda.current_stream()
+    l0 = lens.clone()
+    us = _time_calls(lambda: drv.replay(1), rounds, stream) / n_sets
+    tokens = int((lens - l0).sum().item())
+    # the tree-specific calls alone, back to back on the first set's data
+    s0 = sets[0]
+    sp = stream.cuda_stream
+    part = {
+        "topk_us": _time_calls(lambda: dvb.orthrus_topk_logprobs(s0["diff_logits"], m, logp=drv.logp, idx=drv.idx,
+                                                                 workspace=drv.topk_ws, stream=sp), 16, stream),
+        "tree_build_us": _time_calls(lambda: dvb.orthrus_tree_build(
+            drv.logp.view(w.batch, K - 1, m), drv.idx.view(w.batch, K - 1, m), drv.anchor, K, parent=drv.parent,
+            tokens=drv.tokens, depth=drv.depth, stream=sp), 16, stream),
+        "tree_masks_us": _time_calls(lambda: dvb.orthrus_tree_masks(drv.parent, mask=drv.mask, stream=sp), 16,
+                                     stream),
+        "tree_consensus_us": _time_calls(lambda: dvb.orthrus_consensus_tree_greedy(
+            s0["verify_logits"], drv.tokens, drv.parent, accept_len=drv.accept_len, path=drv.path,
+            correction=drv.correction, workspace=drv.cons_ws, stream=sp), 16, stream),
+    }
+    ver = drv._sets[0]["verify"]
+    part["masked_verify_call_us"] = _time_calls(lambda: [c(sp) for c in ver], 3, stream) / len(ver)
+    del drv
+    return {"cycles": rounds * n_sets, "input_sets": n_sets, "n_nodes": K, "top_m": m, "launch": "hip_graph",
+            "us_per_cycle": round(us, 2), "cycles_per_s": round(1e6 / us, 2),
+            "tokens_per_cycle_synthetic": round(tokens / (rounds * n_sets * w.batch), 3),
+            **{k: round(v, 2) for k, v in part.items()}}
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -562,7 +639,8 @@ def main():
         return
     # one layer-major cache for all layers, with room past L for the rows the
     # synthetic decode cycles commit (the step itself reads rows [0, L) only)
-    w = w.replace(max_len=max(w.capacity, w.cache_len + (args.cycles + 2 * args.cycle_sets) * w.block_k))
+    w = w.replace(max_len=max(w.capacity, w.cache_len + (args.cycles + 2 * args.cycle_sets) * w.block_k,
+                              w.cache_len + (args.tree_cycles + 8) * w.block_k))
     kc_all, vc_all = model_cache(w, device)
     caches = [(kc_all[layer], vc_all[layer]) for layer in range(w.layers)]
     torch.cuda.synchronize()
@@ -598,6 +676,13 @@ def main():
         cyc = time_cycles(w, kc_all, vc_all, device, args.cycles, args.cycle_sets, args.accept_rate)
         print(f"[bench] cycles: {cyc['us_per_cycle']:.1f} us/cycle, {cyc['tokens_per_cycle']:.2f} tokens/cycle, "
               f"commit {cyc['commit_us']:.2f} us", file=sys.stderr, flush=True)
+
+    tcy = None
+    if args.tree_cycles > 0:
+        tcy = time_tree_cycles(w, kc_all, vc_all, device, args.tree_cycles)
+        print(f"[bench] tree cycles: {tcy['us_per_cycle']:.1f} us/cycle; masked verify call "
+              f"{tcy['masked_verify_call_us']:.1f} us, topk {tcy['topk_us']:.1f} us, build {tcy['tree_build_us']:.1f} "
+              f"us, tree consensus {tcy['tree_consensus_us']:.1f} us", file=sys.stderr, flush=True)
 
     tra = None
     if args.train_attn:
@@ -657,6 +742,8 @@ def main():
         line["forward_kl"] = fkl
     if tra is not None:
         line["train_attention"] = tra
+    if tcy is not None:
+        line["tree_cycles"] = tcy
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, caches, device)
     print(json.dumps(line), flush=True)

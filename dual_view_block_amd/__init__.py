@@ -149,14 +149,16 @@ class PreparedAttention:
     """
 
     def __init__(self, mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
-                 softmax_scale: float = 0.0):
+                 softmax_scale: float = 0.0, block_mask=None):
         _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len)
         self.desc = attn_desc(q, k_cache, softmax_scale)
-        self._keep = (q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace)
+        self._keep = (q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace, block_mask)
         nbytes = orthrus_attn_workspace_size(self.desc)
         if workspace.numel() < nbytes:
             raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")
         lib = _lib.load()
+        if (mode == ORTHRUS_MASK_EXPLICIT) != (block_mask is not None):
+            raise ValueError("an explicit block mask goes with mode ORTHRUS_MASK_EXPLICIT, and only with it")
         self._fn = lib.orthrus_block_attn
         self._args = (ctypes.byref(self.desc), int(mode), q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
                       k_cache.data_ptr(), v_cache.data_ptr(), cache_len.data_ptr(), out.data_ptr(),
@@ -167,6 +169,12 @@ class PreparedAttention:
         self._partial_args = self._args[:8] + self._args[10:]
         self._merge = lib.orthrus_block_attn_merge
         self._merge_args = (self._args[0],) + self._args[8:]
+        if block_mask is not None:  # the whole call only (the halves take mode masks)
+            _need(block_mask, "block_mask", torch.int64, (q.shape[0], q.shape[2]), q.device)
+            self._fn = lib.orthrus_block_attn_masked
+            a = self._args
+            self._args = (a[0],) + a[2:8] + (block_mask.data_ptr(),) + a[8:]
+            self._partial = self._merge = None
 
     def __call__(self, stream_ptr: int) -> None:
         st = self._fn(*self._args, stream_ptr)

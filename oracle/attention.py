@@ -95,16 +95,14 @@ def _attend(qrows: np.ndarray, keys: np.ndarray, vals: np.ndarray,
     """
     s = scale * (qrows @ keys.T)
     s = np.where(mask, s, -np.inf)
-    out = np.zeros((qrows.shape[0], vals.shape[1]))
-    lse = np.full(qrows.shape[0], -np.inf)
-    for r in range(qrows.shape[0]):
-        if not mask[r].any():  # a row with no visible key: output 0, lse -inf (R22)
-            continue
-        smax = s[r].max()
-        e = np.exp(s[r] - smax)
-        denom = e.sum()
-        out[r] = (e / denom) @ vals
-        lse[r] = smax + np.log(denom)
+    seen = mask.any(axis=1)  # a row with no visible key: output 0, lse -inf (R22)
+    smax = np.where(seen, s.max(axis=1), 0.0)[:, None]
+    e = np.where(mask, np.exp(s - smax), 0.0)
+    denom = e.sum(axis=1, keepdims=True)
+    p = np.where(seen[:, None], e / np.where(denom > 0, denom, 1.0), 0.0)
+    out = p @ vals
+    with np.errstate(divide="ignore"):
+        lse = np.where(seen, smax[:, 0] + np.log(np.where(seen, denom[:, 0], 1.0)), -np.inf)
     return out, lse
 
 
