@@ -7,36 +7,43 @@
 // one softmax; block key j is visible to block row i always (diffusion view)
 // or iff j <= i (AR verify view).
 //
-// Work layout.  grid = (S splits, row groups, B * Hkv); one work-group of 4
-// waves (256 threads, one wave per SIMD) per CU.  A work-group owns one
+// Work layout.  grid = (S splits, row groups, B * Hkv); one work-group of 8
+// waves (512 threads, two waves per SIMD) per CU.  A work-group owns one
 // contiguous chunk of the (b, g) cache rows and up to 128 query rows (4
-// blocks of 32, one per wave); the last split also takes the K block keys as
-// one extra masked tile.
+// blocks of 32); split 0 also takes the K block keys as one extra masked
+// tile.  Work-groups are numbered so that the (b, g) groups interleave and
+// the block-carrying splits are dispatched first: the dispatcher starts the
+// work-groups over a couple of microseconds, and the heaviest ones should
+// not start last.
 //  * Streaming: the chunk is read in tiles of 64 keys (16 KiB of K and 16 KiB
 //    of V at D = 128).  Every thread issues coalesced 16-byte nontemporal
-//    loads into registers two tiles ahead of use, then writes them into a
-//    4-stage LDS ring (tiles t-1 .. t+2, 128 KiB) at the row's permuted chunk
-//    position; one barrier per tile orders writes and reads.  The 16-byte
-//    chunks of every K and V row are XOR-permuted per row so that both read
-//    patterns below hit distinct LDS banks.
-//  * Compute: each wave takes its query block against both 32-key halves of
-//    every tile.  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 query
+//    loads of the next tile into registers (32 KiB in flight per CU: more
+//    than that measured slower on MI355X), then writes them into a 2-stage
+//    LDS ring at the row's permuted chunk position; one barrier per tile
+//    orders writes and reads.  The 16-byte chunks of every K and V row are
+//    XOR-permuted per row so that both read patterns below hit distinct LDS
+//    banks.
+//  * Compute: wave w takes query block w >> 1 against key half w & 1 (32
+//    keys) of every tile, so each SIMD runs two waves whose matrix and vector
+//    work interleave (one wave per SIMD issues MFMAs at half the SIMD's
+//    rate).  S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (32 keys x 32 query
 //    rows; Q held in registers), so each lane owns one query row and its
 //    softmax statistics need one exchange with lane^32 (a permlane32 swap).
 //    O^T += V^T P^T on the same MFMA: P^T is the S^T accumulator converted to
 //    bf16 in place; V^T comes from the row-major V tile through
 //    ds_read_b64_tr_b16, the transposing LDS read, with the key order matched
-//    to the accumulator's register order.  The loop is software-pipelined
-//    with P V delayed by one tile: iteration t interleaves the S(t+1) MFMAs,
-//    the P(t-1) V(t-1) MFMAs and the exponentials of S(t).
+//    to the accumulator's register order.
 //  * Softmax: P = 2^(s*scale*log2(e) - m_ref) with a lazily raised reference
-//    m_ref (raised only when a shifted score exceeds it by more than 2^8; a
-//    raise first flushes the pending P V), so the accumulator rescale is
-//    rare; the sum cancels the reference exactly.
+//    m_ref (raised only when a shifted score exceeds it by more than 2^8), so
+//    the accumulator rescale is rare; the sum cancels the reference exactly.
+//    Each key half keeps its own reference, sum and accumulator; at the end
+//    the two waves of a query block combine theirs through LDS, each
+//    finishing half of head_dim.
 //  * Epilogue: with one split the work-group normalises and writes the rows
 //    itself.  Otherwise it stores a partial per row -- fp32 (m_ref, sum) and
 //    the bf16 value sum normalised by that sum, staged through LDS and written
-//    as whole coalesced rows -- and a second kernel merges the S partials:
+//    as whole coalesced rows with nontemporal stores -- and a second kernel
+//    merges the S partials:
 //    out = sum_s 2^(m_s-M) l_s o_s / sum_s 2^(m_s-M) l_s,
 //    lse = (M + log2 sum_s 2^(m_s-M) l_s) * ln 2, with one wave per row.
 #include "attn_frag.h"
@@ -49,8 +56,6 @@ namespace {
 
 using namespace frag;
 
-constexpr int kThreads = kAttnThreads;
-constexpr int kStages = 4;  // LDS ring stages: tiles t-1 .. t+2
 constexpr float kLazy = 8.0f;  // base-2 headroom before the softmax reference is raised
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994531f;
@@ -70,7 +75,7 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int 
   r.kstart = split * chunk;
   r.kend = min(r.kstart + chunk, L);
   r.ncache = r.kstart < r.kend ? (r.kend - r.kstart + kTileKeys - 1) / kTileKeys : 0;
-  r.has_block = split == S - 1 ? 1 : 0;
+  r.has_block = split == 0 ? 1 : 0;
   r.ntiles = r.ncache + (r.has_block ? (a.block_k + kTileKeys - 1) / kTileKeys : 0);
   return r;
 }
@@ -159,80 +164,85 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
   }
 }
 
-// EXPL: the block tile takes the explicit per-row masks of a.blk_mask (a
-// separate instantiation, so the mode-masked launches keep their registers).
+// The streaming kernel (see the top of the file).  Per wave and tile at D 128:
+// 8 S^T MFMAs, 16 exponentials per lane, 8 O^T MFMAs.
+constexpr int kStreamThreads = kAttnThreads;
+
 template <int D, int NQB, bool EXPL>
-__global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, AttnPlan plan, int direct) {
-  constexpr int DCH = D / 8;               // 16-byte chunks per row
-  constexpr int ROWB = D * 2;              // bytes per row
-  constexpr int TILEB = kTileKeys * ROWB;  // bytes of one K or V tile
-  constexpr int STAGEB = 2 * TILEB;        // one ring stage: a K tile and a V tile
-  constexpr int HALFB = 32 * ROWB;         // offset of a tile's second 32-key half
-  constexpr int NDS = D / 16;              // MFMA steps over head_dim for S^T
-  constexpr int NMB = D / 32;              // 32-wide head_dim blocks of O^T
-  constexpr int NWAVES = kThreads / 64;
-  constexpr int CPT = kTileKeys * DCH / kThreads;  // 16-byte chunks per thread per array per tile
-  static_assert(NWAVES == 4, "four waves, one 32-row query block each");
-  static_assert(CPT >= 1, "tile too small for the work-group");
-  static_assert(4 * NMB == 2 * NDS, "two PV MFMAs per S step");
+__global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a, AttnPlan plan, int direct) {
+  constexpr int DCH = D / 8;
+  constexpr int ROWB = D * 2;
+  constexpr int TILEB = kTileKeys * ROWB;
+  constexpr int STAGEB = 2 * TILEB;
+  constexpr int HALFB = 32 * ROWB;
+  constexpr int NDS = D / 16;
+  constexpr int NMB = D / 32;
+  constexpr int HMB = NMB / 2;  // head_dim blocks each wave of a pair finishes
+  constexpr int CPT = kTileKeys * DCH / kStreamThreads;
+  constexpr int RINGB = 2 * STAGEB;
+  constexpr int XCHB = 8 * HMB * 16 * 64 * 4;  // accumulator blocks handed to the partner wave
+  constexpr int REGION0 = RINGB > XCHB ? RINGB : XCHB;
+  constexpr int OPITCH = ROWB + 16;
+  static_assert(CPT >= 1 && HMB >= 1, "tile and head_dim fit the work-group");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * STAGEB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[REGION0 + 128 * OPITCH];
+  __shared__ float2 xstat[8][32];
 
-  const int split = blockIdx.x;
-  const int rg = blockIdx.y;
-  const int bg = blockIdx.z;
+  // dispatch order: (b, g) groups interleaved, split 0 (the block keys) first
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int bg = lin % (int)gridDim.z;
+  const int rg = (lin / (int)gridDim.z) % (int)gridDim.y;
+  const int split = lin / ((int)gridDim.z * (int)gridDim.y);
   const int grp = bg * plan.row_groups + rg;
   const int b = bg / a.n_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int qb = __builtin_amdgcn_readfirstlane(tid >> 6);  // this wave's query block
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb = w >> 1;  // query block
+  const int kh = w & 1;   // key half of every tile
   const int half = lane >> 5;
   const bool active = qb < NQB;
   const int R = plan.rows;
   const int K = a.block_k;
   const SplitRange sr = split_range(a, b, split);
   const int g = bg % a.n_kv_heads;
-  // q / out / lse element offset of row r (= head_in_group * K + i) of the (b, g) group
   const long long q_grp = b * a.q_bs + (long long)g * a.group * a.q_hs;
   const long long o_grp = b * a.o_bs + (long long)g * a.group * a.o_hs;
   const long long l_grp = b * a.l_bs + (long long)g * a.group * a.l_hs;
+  const int wrow = qb * 32 + (lane & 31);
+  const int qrow = rg * plan.rows_per_wg + wrow;
+  const int qrow_i = qrow % K;
 
-  // ---- this lane's query row (the N index of every MFMA it joins)
-  const int wrow = qb * 32 + (lane & 31);         // row inside the work-group block
-  const int qrow = rg * plan.rows_per_wg + wrow;  // row inside the (b, g) group
-  const int qrow_i = qrow % K;                    // its block position (row = head_in_group*K + i)
-
-  // ---- tile copies: thread tid moves 16-byte chunks n = tid + c*kThreads of
-  // the K tile and of the V tile (row n / DCH, chunk n % DCH, so consecutive
-  // lanes read consecutive 16 bytes of the head-major cache) with
-  // nontemporal loads into registers, two tiles ahead, and later writes them
-  // into the LDS ring at the row's permuted chunk position.  Rows past the
-  // valid count re-read the last valid row (finite data; their scores are
-  // masked to -inf, so P = 0 exactly).  Tiles past the end re-read the first
-  // block-key row (no HBM traffic to speak of) into a stage nobody reads.
+  // ---- tile copies: thread tid moves 16-byte chunks n = tid + c*512 of the K
+  // tile and of the V tile (row n / DCH, chunk n % DCH, so consecutive lanes
+  // read consecutive 16 bytes of the head-major cache) with nontemporal loads
+  // into registers, and writes them into the LDS ring at the row's permuted
+  // chunk position one iteration later.  Rows past the valid count re-read the
+  // last valid row (finite data; their scores are masked to -inf, so P = 0
+  // exactly).  A tile past the end re-reads the first block-key row into
+  // registers that are never stored.
   int crow[CPT];
   uint32_t cchunk[CPT], dk[CPT], dv[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int n = tid + c * kThreads;
+    const int n = tid + c * kStreamThreads;
     crow[c] = n / DCH;
     cchunk[c] = (uint32_t)(n % DCH) * 16;
     dk[c] = (uint32_t)(crow[c] * ROWB + swz_k<DCH>(crow[c], n % DCH) * 16);
     dv[c] = (uint32_t)(TILEB + crow[c] * ROWB + swz_v<DCH>(crow[c], n % DCH) * 16);
   }
-  // tiles [0, nfull) are whole cache tiles: no masking, no row clamping
   const int nfull = min((sr.kend - sr.kstart) / kTileKeys, sr.ncache);
   const long long split_off = b * a.c_bs + g * a.c_gs + (long long)sr.kstart * D;
-  const uint8_t* kc0 = reinterpret_cast<const uint8_t*>(a.k_cache + split_off);  // tile 0 of this split
+  const uint8_t* kc0 = reinterpret_cast<const uint8_t*>(a.k_cache + split_off);
   const uint8_t* vc0 = reinterpret_cast<const uint8_t*>(a.v_cache + split_off);
   const long long blk_off = b * a.blk_bs + g * a.blk_gs;
   const uint8_t* kblk = reinterpret_cast<const uint8_t*>(a.k_blk + blk_off);
   const uint8_t* vblk = reinterpret_cast<const uint8_t*>(a.v_blk + blk_off);
-  typedef u32x4 Stage[2 * CPT];  // K chunks, then V chunks
+  typedef u32x4 Stage[2 * CPT];
   auto load_tile = [&](int t, Stage& r) __attribute__((always_inline)) {
     const bool whole = t < nfull;
     const bool real = t < sr.ntiles;
-    const bool blk = sr.has_block && t >= sr.ncache;  // block tile t - ncache
+    const bool blk = sr.has_block && t >= sr.ncache;
     const int bt = t - sr.ncache;
     const int last = whole ? kTileKeys - 1
                            : (!real ? 0 : (blk ? min(kTileKeys, K - bt * kTileKeys)
@@ -256,14 +266,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
       *reinterpret_cast<u32x4*>(sb + dv[c]) = r[CPT + c];
     }
   };
+  auto tile_valid = [&](int t) __attribute__((always_inline)) {
+    return (sr.has_block && t >= sr.ncache) ? min(kTileKeys, K - (t - sr.ncache) * kTileKeys)
+                                            : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys));
+  };
 
-  // ---- running softmax state of this lane's row.  `mref` is a reference
-  // maximum in base-2 units (score * scale * log2 e): P = 2^(s*c2 - mref).  It
-  // is only raised when a score exceeds it by more than 2^kLazy, so P <= 2^8
-  // (exact in bf16 and fp32) and the accumulator rescale runs on a handful of
-  // tiles only; normalisation by the sum makes the reference cancel exactly.
+  // ---- running softmax state of this lane's row over this wave's key half
   float mref = kNegInf, neg_mref = 0.0f;
-  float l_run = 0.0f;  // this lane's half of the keys of each 8-key group
+  float l_run = 0.0f;
   f32x16 oacc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
@@ -273,44 +283,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
   const int grp16 = lane >> 4;
   const int jj = (lane & 15) >> 2;
   const int qq = lane & 3;
-  const int krow = lane & 31;  // key inside a 32-key half
+  const int krow = lane & 31;
 
-  // Keys of tile t: nvalid(t) of them are real; the block tile is the last.
-  auto tile_valid = [&](int t) __attribute__((always_inline)) {
-    return (sr.has_block && t >= sr.ncache) ? min(kTileKeys, K - (t - sr.ncache) * kTileKeys)
-                                            : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys));
-  };
-
-  // K fragments of both 32-key halves of the tile in `stage`.  Logical chunk
-  // 2*ds + half of row krow sits at byte 16 * (chunk ^ f(krow)) of the row,
-  // i.e. at (32*ds) ^ kswz with kswz = 16 * (half ^ f(krow)) < ROWB; f is the
-  // same for row krow + 32, so the second half is a constant offset away.
-  const uint32_t kswz = 16u * (uint32_t)swz_k<DCH>(krow, half);
-  auto load_k = [&](int stage, bf16x8 (&kf)[2][NDS]) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)(stage * STAGEB + krow * ROWB) + kswz;
+  // K fragments of this wave's 32-key half.  Logical chunk 2*ds + half of row
+  // krow sits at byte 16 * (chunk ^ f(krow)) of the row, i.e. at (32*ds) ^
+  // kswz with kswz = 16 * (half ^ f(krow)) < ROWB.
+  const uint32_t kbase = (uint32_t)(kh * HALFB + krow * ROWB) + 16u * (uint32_t)swz_k<DCH>(krow, half);
+  auto load_k = [&](int stage, bf16x8 (&kf)[NDS]) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(stage * STAGEB) + kbase;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const uint8_t* p = smem + (base ^ (32u * ds));
-      kf[0][ds] = *reinterpret_cast<const bf16x8*>(p);
-      kf[1][ds] = *reinterpret_cast<const bf16x8*>(p + HALFB);
-    }
+    for (int ds = 0; ds < NDS; ++ds) kf[ds] = *reinterpret_cast<const bf16x8*>(smem + (base ^ (32u * ds)));
   };
-  // V^T fragments of the tile in `stage`, in the key order of the S^T
-  // accumulator registers: key half h, MFMA k-step tt of 16 keys, head_dim
-  // block mb.  The lane reads keys 32h + 16tt + 4*half + jj and that + 8; all
-  // are congruent mod 4 and the V swizzle depends on the row mod 4 only, so
-  // one base per head_dim block plus constant offsets address them all.
+  // V^T fragments of the half in the key order of the S^T accumulator: k-step
+  // tt of 16 keys, head_dim block mb.  The lane reads keys 32*kh + 16*tt +
+  // 4*half + jj and that + 8; all are congruent mod 4 and the V swizzle
+  // depends on the row mod 4 only, so one base per head_dim block plus
+  // constant offsets address them all.  The per-tile bases are opaque to the
+  // optimiser so that those offsets fold into the LDS instructions, and the
+  // fragments are assembled with whole-vector bit casts (element-wise inserts
+  // of the i16 lanes into the bf16 operand were lowered incorrectly).
   uint32_t vbase[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int key0 = 4 * half + jj;
     const int d0 = 32 * mb + 16 * (grp16 & 1) + 4 * qq;
-    vbase[mb] = (uint32_t)(TILEB + key0 * ROWB + swz_v<DCH>(key0, d0 >> 3) * 16 + (d0 & 7) * 2);
+    vbase[mb] = (uint32_t)(TILEB + kh * HALFB + key0 * ROWB + swz_v<DCH>(key0, d0 >> 3) * 16 + (d0 & 7) * 2);
   }
-  typedef bf16x8 VFrag[2][2][NMB];
-  auto load_v = [&](int stage, VFrag& vf) __attribute__((always_inline)) {
-    // per-tile bases, opaque to the optimiser so that the constant offsets
-    // below fold into the LDS instructions
+  auto load_v = [&](int stage, bf16x8 (&vf)[2][NMB]) __attribute__((always_inline)) {
     uint32_t vb[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
@@ -318,288 +317,182 @@ __global__ __launch_bounds__(kThreads, 1) void attn_stream_kernel(AttnArgs a, At
       asm("" : "+v"(vb[mb]));
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const uint8_t* pa = smem + vb[mb] + h * HALFB + (16 * tt) * ROWB;
-          const uint8_t* pbp = pa + 8 * ROWB;
-          // whole-vector bit casts: element-wise inserts of the i16 lanes into
-          // the bf16 operand were lowered incorrectly by the compiler
-          const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa)));
-          const bf16x4 vb2 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pbp)));
-          vf[h][tt][mb] = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+      for (int mb = 0; mb < NMB; ++mb) {
+        const uint8_t* pa = smem + vb[mb] + (16 * tt) * ROWB;
+        const uint8_t* pbp = pa + 8 * ROWB;
+        const bf16x4 va = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa)));
+        const bf16x4 vb2 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pbp)));
+        vf[tt][mb] = __builtin_shufflevector(va, vb2, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
   };
-  // Padded keys and, in the verify view, block keys after the row: -inf.
-  // Explicit masks: the visible block keys of this lane's row, shifted so
-  // that register r of half h tests bit 32h + 8*(r/4) + r%4 of the word.
-
-  auto mask_scores = [&](f32x16 (&s)[2], int nvalid, bool block_tile, int key0) __attribute__((always_inline)) {
+  // register r holds key 32*kh + 8*(r/4) + 4*half + r%4 of the tile
+  auto mask_scores = [&](f32x16& s, int nvalid, bool block_tile, int key0) __attribute__((always_inline)) {
     int lim = nvalid;
     if (block_tile && a.causal) lim = min(lim, qrow_i + 1 - key0);
-    // register r of half h holds key 32h + 8*(r/4) + 4*half + r%4; compare the
-    // constant part against an opaque per-lane bound
-    int rel = lim - 4 * half;
+    int rel = lim - 4 * half - 32 * kh;
     asm volatile("" : "+v"(rel));
     if (EXPL && block_tile) {
-      // the row's mask word is read here, once, rather than kept live through the loop
-      const int mrow = min(rg * plan.rows_per_wg + wrow, R - 1) % K;
-      const uint64_t m = a.blk_mask[(size_t)b * K + mrow] >> (4 * half);
-      const uint32_t emask_lo = (uint32_t)m, emask_hi = (uint32_t)(m >> 32);
+      const int mrow = min(qrow, R - 1) % K;
+      const uint32_t em = (uint32_t)(a.blk_mask[(size_t)b * K + mrow] >> (4 * half + 32 * kh));
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 32 * h + 8 * (r >> 2) + (r & 3);
-          const uint32_t bit = (h ? emask_hi : emask_lo) & (1u << (kk & 31));
-          s[h][r] = (kk < rel && bit) ? s[h][r] : kNegInf;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + (r & 3);
+        s[r] = (kk < rel && (em & (1u << kk))) ? s[r] : kNegInf;
+      }
     } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[h][r] = (32 * h + 8 * (r >> 2) + (r & 3)) < rel ? s[h][r] : kNegInf;
+      for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) < rel ? s[r] : kNegInf;
     }
   };
-  bf16x8 qf[NDS];
-  // O^T += V^T P^T over the 64 keys of a tile (k-step 2h + tt).
-  auto pv = [&](const bf16x8 (&pb)[4], const VFrag& vf) __attribute__((always_inline)) {
+  // shifted base-2 exponents and the lazy reference raise (no pending P V here)
+  auto update_ref = [&](f32x16& s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c2, neg_mref);
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) oacc[mb] = mfma32(vf[ks >> 1][ks & 1][mb], pb[ks], oacc[mb]);
-  };
-  // Scores -> base-2 exponents relative to the reference, x = s*c2 - mref,
-  // in place; then the reference is raised (rare) if some x exceeds 2^kLazy
-  // or the row has none yet.  The raise first adds the previous tile's P V,
-  // still pending (it belongs to the old reference), then shifts x and
-  // rescales the accumulator and the running sum.  The maximum is taken over
-  // the x values (finite or -inf, never NaN) and across the lane pair that
-  // shares a row with one permlane32 swap.
-  auto update_ref = [&](f32x16 (&s)[2], bf16x8 (&pprev)[4], const VFrag& vprev) __attribute__((always_inline)) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[h][r] = fmaf(s[h][r], c2, neg_mref);
-    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[1][0], s[1][1]));
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
+    for (int r = 4; r < 16; r += 4) mx = fmaxf(mx, fmaxf(fmaxf(s[r], s[r + 1]), fmaxf(s[r + 2], s[r + 3])));
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
     mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     if (__ballot(mx > kLazy || mref == kNegInf)) {
-      pv(pprev, vprev);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) pprev[ks] = bf16x8{};
-      // raise by mx where that helps (mx is relative to the current frame)
       const bool raise = mx != kNegInf && (mx > kLazy || mref == kNegInf);
       const float shift = raise ? mx : 0.0f;
       const float alpha = (mref == kNegInf || !raise) ? (mref == kNegInf ? 0.0f : 1.0f) : fast_exp2(-mx);
       mref = raise ? (mref == kNegInf ? mx : mref + mx) : mref;
       neg_mref = (mref == kNegInf) ? 0.0f : -mref;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[h][r] -= shift;
+      for (int r = 0; r < 16; ++r) s[r] -= shift;
       l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) oacc[mb] *= alpha;
     }
   };
-  // exp2 of one score in the base-2 frame of the reference
-  auto expo = [&](float x) __attribute__((always_inline)) { return fast_exp2(x); };
-  auto next_stage = [](int s) __attribute__((always_inline)) { return s == kStages - 1 ? 0 : s + 1; };
-  auto prev_stage = [](int s) __attribute__((always_inline)) { return s == 0 ? kStages - 1 : s - 1; };
-
-  // ---- software pipeline.  LDS holds four tiles: t-1 (its V for the pending
-  // P(t-1) V(t-1)), t (V next), t+1 (K for S(t+1)) and t+2 (being written);
-  // registers hold the next two.  Iteration t issues three independent pieces
-  // of work on one wave: the S(t+1) MFMAs, the P(t-1) V(t-1) MFMAs and the
-  // exponentials of S(t), so the matrix core and the vector ALU overlap.  One
-  // barrier per tile: after it every wave is past iteration t-1, so the
-  // stage of tile t-2 can take tile t+2, and tile t+1 (written in iteration
-  // t-1) is visible.  Waves whose query block lies past the work-group's rows
-  // run the same code on zero queries and write nothing.
-  Stage stg0, stg1;  // at iteration t: tiles t+2 and t+3 (in flight or landed)
+  bf16x8 qf[NDS];
   {
-    const int row = min(rg * plan.rows_per_wg + wrow, R - 1);
+    const int row = min(qrow, R - 1);
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + q_grp + (row / K) * a.q_hs + (long long)(row % K) * D);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) qf[ds] = active ? qp[2 * ds + half] : bf16x8{};
   }
-  {
-    Stage t0, t1;
-    load_tile(0, t0);
-    load_tile(1, t1);
-    store_tile(0, t0);
-    load_tile(2, stg0);
-    store_tile(1, t1);
-    load_tile(3, stg1);
-  }
-  __syncthreads();
-  f32x16 sa[2], sb[2];
-  bf16x8 pprev[4];  // P(t-1) in bf16, the pending product's left operand
+  // One tile of this wave's half: S^T, mask, softmax, O^T += V^T P^T.
+  auto compute = [&](int st, int t) __attribute__((always_inline)) {
+    const int nval = tile_valid(t);
+    if (!active || nval <= 32 * kh) return;  // no real key in this half
+    bf16x8 kf[NDS];
+    load_k(st, kf);
+    f32x16 s;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) pprev[ks] = bf16x8{};
-  auto s_mfma = [&](const bf16x8 (&kf)[2][NDS], f32x16 (&s)[2]) __attribute__((always_inline)) {
+    for (int r = 0; r < 16; ++r) s[r] = 0.0f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[h][r] = 0.0f;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) s[h] = mfma32(kf[h][ds], qf[ds], s[h]);
-    }
-  };
-  if (sr.ntiles > 0) {
-    bf16x8 kf[2][NDS];
-    load_k(0, kf);
-    s_mfma(kf, sa);
-  }
-  const int nmain = nfull > 0 ? nfull - 1 : 0;  // iterations whose next tile is whole too
-
-  // One iteration: cur = S(t) -> P(t); pending P(t-1) V(t-1) is added;
-  // nxt = S(t+1) if there is a next tile.  Tile t sits in stage st, the
-  // pending V in stage vst; `refill` holds tile t+2 and takes tile t+4.
-  auto iteration = [&](int t, int st, int vst, f32x16 (&cur)[2], f32x16 (&nxt)[2], Stage& refill, bool masked,
-                       bool has_next) __attribute__((always_inline)) {
-    const int st1 = next_stage(st);   // tile t+1
-    const int st2 = next_stage(st1);  // tile t+2 (the stage tile t-2 used)
-    VFrag vf;
-    load_v(vst, vf);
-    if (masked) {
+    for (int ds = 0; ds < NDS; ++ds) s = mfma32(kf[ds], qf[ds], s);
+    bf16x8 vf[2][NMB];
+    load_v(st, vf);
+    if (t >= nfull) {
       const bool blk = sr.has_block && t >= sr.ncache;
-      if (blk || tile_valid(t) < kTileKeys) mask_scores(cur, tile_valid(t), blk, (t - sr.ncache) * kTileKeys);
+      mask_scores(s, nval, blk, (t - sr.ncache) * kTileKeys);
     }
-    update_ref(cur, pprev, vf);
+    update_ref(s);
     float lsum = 0.0f;
-    bf16x8 pnew[4];
-    if (has_next) {
-      __syncthreads();
-      store_tile(st2, refill);
-      load_tile(t + 4, refill);
-      bf16x8 kf[2][NDS];
-      load_k(st1, kf);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) nxt[h][r] = 0.0f;
-      // per S step: two S MFMAs, four exponentials, two pending PV MFMAs
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        nxt[0] = mfma32(kf[0][ds], qf[ds], nxt[0]);
-#pragma unroll
-        for (int e = 0; e < 32 / NDS; ++e) {
-          const int i = ds * (32 / NDS) + e;  // score i of the 32 this lane holds
-          const float p_ = expo(cur[i >> 4][i & 15]);
-          cur[i >> 4][i & 15] = p_;
-          lsum += p_;
-        }
-        nxt[1] = mfma32(kf[1][ds], qf[ds], nxt[1]);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = 2 * ds + u;  // pending PV MFMA j of 4 * NMB
-          const int ks = j / NMB, mb = j % NMB;
-          oacc[mb] = mfma32(vf[ks >> 1][ks & 1][mb], pprev[ks], oacc[mb]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float p_ = expo(cur[i >> 4][i & 15]);
-        cur[i >> 4][i & 15] = p_;
-        lsum += p_;
-      }
-      pv(pprev, vf);
+    for (int r = 0; r < 16; ++r) {
+      const float p_ = fast_exp2(s[r]);
+      s[r] = p_;
+      lsum += p_;
     }
     l_run += lsum;
+    bf16x8 pb[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pnew[ks][e] = (__bf16)cur[ks >> 1][8 * (ks & 1) + e];
+      for (int e = 0; e < 8; ++e) pb[tt][e] = (__bf16)s[8 * tt + e];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pprev[ks] = pnew[ks];
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) oacc[mb] = mfma32(vf[tt][mb], pb[tt], oacc[mb]);
   };
-  int t = 0, st = 0;
-  for (; t + 2 <= nmain; t += 2) {  // unrolled by two: scores and staging registers alternate
-    iteration(t, st, t == 0 ? st : prev_stage(st), sa, sb, stg0, false, true);
-    st = next_stage(st);
-    iteration(t + 1, st, prev_stage(st), sb, sa, stg1, false, true);
-    st = next_stage(st);
-  }
-  // ---- the remaining tiles (the last whole tile, a partial tile, the block
-  // tile; all of them if there are fewer than two whole tiles)
-  for (; t < sr.ntiles; ++t) {
-    const bool has_next = t + 1 < sr.ntiles;
-    iteration(t, st, t == 0 ? st : prev_stage(st), sa, sb, stg0, true, has_next);
-    if (has_next) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) sa[h] = sb[h];
-#pragma unroll
-      for (int c = 0; c < 2 * CPT; ++c) {  // keep "stg0 holds tile t+2"
-        const u32x4 x = stg0[c];
-        stg0[c] = stg1[c];
-        stg1[c] = x;
-      }
+
+  // ---- pipeline: at the top of iteration t, tile t sits in LDS stage t & 1
+  // and the registers hold tile t+1 (landed or landing).  After the barrier
+  // every wave is past iteration t-1, so stage (t+1) & 1 takes tile t+1 and
+  // the registers take tile t+2 while tile t is computed.
+  Stage stg;
+  load_tile(0, stg);
+  store_tile(0, stg);
+  load_tile(1, stg);
+  for (int t = 0; t < sr.ntiles; ++t) {
+    __syncthreads();
+    if (t + 1 < sr.ntiles) {
+      store_tile((t + 1) & 1, stg);
+      load_tile(t + 2, stg);
     }
-    st = has_next ? next_stage(st) : st;
-  }
-  if (sr.ntiles > 0) {  // the last tile's P V
-    VFrag vf;
-    load_v(st, vf);
-    pv(pprev, vf);
+    compute(t & 1, t);
   }
 
-  // ---- per-row totals: this lane holds half of the keys of every 8-key group
+  // ---- combine the two key halves of each query block through LDS: wave w
+  // hands the head_dim blocks its partner finishes (a raw register dump,
+  // lane-major) and its row statistics to the partner wave w ^ 1.
   const float l_row = l_run + __shfl_xor(l_run, 32);
-  const float m_out = mref;  // base-2 reference of acc and l
-
-  // ---- normalised rows in bf16 -> LDS (row pitch ROWB + 16 spreads the 32
-  // rows a store instruction touches over the banks) -> coalesced 16-byte
-  // global stores of whole rows.  The ring is free once every wave is past
-  // its last P V.
-  constexpr int OPITCH = ROWB + 16;
-  static_assert(128 * OPITCH <= kStages * STAGEB, "output rows fit the ring");
-  __syncthreads();
+  float* xch = reinterpret_cast<float*>(smem);
+  __syncthreads();  // every wave is past its last tile: the ring is free
   if (active) {
-    const float inv = l_row > 0.0f ? 1.0f / l_row : 0.0f;
-    uint8_t* orow = smem + wrow * OPITCH;
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
+    for (int j = 0; j < HMB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xch[((w * HMB + j) * 16 + r) * 64 + lane] = kh ? oacc[j][r] : oacc[HMB + j][r];
+    if (half == 0) xstat[w][lane] = make_float2(mref, l_row);
+  }
+  __syncthreads();
+  float m_out = kNegInf, l_out = 0.0f;
+  if (active) {
+    const int pw = w ^ 1;
+    const float2 po = xstat[pw][lane & 31];
+    m_out = fmaxf(mref, po.x);
+    const float a_s = mref == kNegInf ? 0.0f : fast_exp2(mref - m_out);
+    const float a_o = po.x == kNegInf ? 0.0f : fast_exp2(po.x - m_out);
+    l_out = a_s * l_row + a_o * po.y;
+    const float inv = l_out > 0.0f ? 1.0f / l_out : 0.0f;
+    const float ws = a_s * inv, wo = a_o * inv;
+    uint8_t* orow = smem + REGION0 + wrow * OPITCH;
+#pragma unroll
+    for (int j = 0; j < HMB; ++j) {
+      const int mb = kh * HMB + j;
+      const float* xp = xch + (size_t)((pw * HMB + j) * 16) * 64 + lane;
+      f32x16 own;  // register selects: a runtime index would put the accumulators in scratch
+#pragma unroll
+      for (int r = 0; r < 16; ++r) own[r] = kh ? oacc[HMB + j][r] : oacc[j][r];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         ushort4 o;
-        o.x = to_bf16_bits(oacc[mb][4 * q4 + 0] * inv);
-        o.y = to_bf16_bits(oacc[mb][4 * q4 + 1] * inv);
-        o.z = to_bf16_bits(oacc[mb][4 * q4 + 2] * inv);
-        o.w = to_bf16_bits(oacc[mb][4 * q4 + 3] * inv);
+        o.x = to_bf16_bits(own[4 * q4 + 0] * ws + xp[(4 * q4 + 0) * 64] * wo);
+        o.y = to_bf16_bits(own[4 * q4 + 1] * ws + xp[(4 * q4 + 1) * 64] * wo);
+        o.z = to_bf16_bits(own[4 * q4 + 2] * ws + xp[(4 * q4 + 2) * 64] * wo);
+        o.w = to_bf16_bits(own[4 * q4 + 3] * ws + xp[(4 * q4 + 3) * 64] * wo);
         *reinterpret_cast<ushort4*>(orow + 2 * (32 * mb + 8 * q4 + 4 * half)) = o;
       }
+    }
   }
   __syncthreads();
-  const int nrows = plan.rows_per_wg;  // the rows of the active query blocks
+  const int nrows = plan.rows_per_wg;
   const bool one_split = a.splits == 1 && direct;
-  // destination of row r: the output (one split) or this split's partial slot
   const size_t slot = (size_t)grp * a.splits + split;
-  for (int n = tid; n < nrows * DCH; n += kThreads) {
+  for (int n = tid; n < nrows * DCH; n += kStreamThreads) {
     const int r = n / DCH, ch = n % DCH;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * OPITCH + ch * 16);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + REGION0 + r * OPITCH + ch * 16);
     if (one_split) {
-      const int gr = rg * plan.rows_per_wg + r;  // row inside the (b, g) group
+      const int gr = rg * plan.rows_per_wg + r;
       if (gr < R)
         *reinterpret_cast<u32x4*>(a.out + o_grp + (gr / K) * a.o_hs + (long long)(gr % K) * D + ch * 8) = v;
     } else {
-      *reinterpret_cast<u32x4*>(a.ws_acc + (slot * plan.rows_per_wg + r) * D + ch * 8) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.ws_acc + (slot * plan.rows_per_wg + r) * D + ch * 8));
     }
   }
-  if (active && half == 0) {
+  if (active && kh == 0 && half == 0) {
     if (one_split) {
-      if (a.lse != nullptr && qrow < R) a.lse[l_grp + (qrow / K) * a.l_hs + qrow % K] = (m_out + log2f(l_row)) * kLn2;
+      if (a.lse != nullptr && qrow < R) a.lse[l_grp + (qrow / K) * a.l_hs + qrow % K] = (m_out + log2f(l_out)) * kLn2;
     } else {
-      float2 ml;
-      ml.x = m_out;
-      ml.y = l_row;
-      *reinterpret_cast<float2*>(a.ws_ml + (slot * plan.rows_per_wg + wrow) * 2) = ml;
+      __builtin_nontemporal_store(m_out, a.ws_ml + (slot * plan.rows_per_wg + wrow) * 2);
+      __builtin_nontemporal_store(l_out, a.ws_ml + (slot * plan.rows_per_wg + wrow) * 2 + 1);
     }
   }
 }
@@ -622,9 +515,9 @@ template <int D, int NQB>
 hipError_t launch_stream(const AttnArgs& a, const AttnPlan& p, int direct, hipStream_t stream) {
   dim3 grid(a.splits, p.row_groups, a.batch * a.n_kv_heads);
   if (a.blk_mask != nullptr)
-    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, true>), grid, dim3(kThreads), 0, stream, a, p, direct);
+    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, true>), grid, dim3(kStreamThreads), 0, stream, a, p, direct);
   else
-    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, false>), grid, dim3(kThreads), 0, stream, a, p, direct);
+    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, false>), grid, dim3(kStreamThreads), 0, stream, a, p, direct);
   return hipGetLastError();
 }
 

@@ -10,10 +10,10 @@ namespace orthrus {
 // Keys per LDS tile.  Every (sequence, KV head) range of cache rows is cut
 // into `splits` contiguous chunks that are whole multiples of this.
 constexpr int kTileKeys = 64;
-// The streaming kernel runs one 256-thread work-group (one wave per SIMD)
+// The streaming kernel runs one 512-thread work-group (two waves per SIMD)
 // per CU; with more than one split per (sequence, KV head) the launch never
 // exceeds the device's CU count.
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 512;
 // CU count the workspace is sized for (MI355X).  A device with fewer CUs runs
 // fewer splits inside the same workspace.
 constexpr int kPlanCUs = 256;
