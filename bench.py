@@ -63,6 +63,8 @@ def _parse():
     ap.add_argument("--train-attn", type=int, default=1,
                     help="time the training dual-pass attention (forward and diffusion-row backward) of "
                          "one packed 2048-token sequence at the workload's heads (0 to skip)")
+    ap.add_argument("--configs", type=int, default=1,
+                    help="also time the other configuration points (C2, C3, C4 at L=131072, C5); 0 skips")
     ap.add_argument("--accept-rate", type=float, default=0.912,
                     help="per-candidate match probability of the synthetic acceptance law "
                          "(0.912: 10.8 tokens per cycle at K = 32)")
@@ -424,6 +426,92 @@ def _time_calls(fn, reps: int, stream) -> float:
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
+# The other configuration points, timed as whole steps on their own caches:
+# (label, workload, overrides).  C4 at L = 131072 is timed at K = 32 and K = 1.
+CONFIG_POINTS = (
+    ("C2", "qwen3_1p7b_layer", {}),
+    ("C3", "qwen3_8b_8k", {}),
+    ("C4", "qwen3_8b_128k", {}),
+    ("C4", "qwen3_8b_128k", {"block_k": 1}),
+    ("C5", "ragged_b16", {}),
+)
+
+
+def step_bytes_lens(w, len_sum: int) -> int:
+    """Algorithmic bytes of one step when the sequences' cached lengths sum to
+    `len_sum`: every layer-view reads its cache rows, q and the block K/V and
+    writes its output; the greedy consensus reads the logits."""
+    bf = 2
+    cache = 2 * w.n_kv_heads * len_sum * w.head_dim * bf
+    q = w.batch * w.n_q_heads * w.block_k * w.head_dim * bf
+    blk = 2 * w.batch * w.n_kv_heads * w.block_k * w.head_dim * bf
+    return 2 * w.layers * (cache + 2 * q + blk) + greedy_bytes(w)
+
+
+class _SampleStep:
+    """A step whose consensus is the T>0 rejection sampler instead of greedy."""
+
+    def __init__(self, step, sample_call):
+        self.step, self.sample_call = step, sample_call
+
+    def run(self, stream_ptr: int) -> None:
+        for c in self.step.calls["diff"] + self.step.calls["verify"]:
+            c(stream_ptr)
+        self.sample_call(stream_ptr)
+
+
+def time_configs(device, steps: int, warmup: int):
+    """Step time of every other configuration point (eager launches, HIP events
+    on the launch stream, as for the headline step).  The ragged batch is also
+    timed with the T>0 sampler as its consensus, and the sampler alone."""
+    import torch
+
+    import dual_view_block_amd as dvb
+    from synth import WORKLOADS, model_cache, sample_inputs
+
+    out = {}
+    for label, name, kw in CONFIG_POINTS:
+        w = WORKLOADS[name].replace(**kw)
+        kc, vc = model_cache(w, device)
+        caches = [(kc[layer], vc[layer]) for layer in range(w.layers)]
+        st = Step(w, caches, device)
+        ms, _ = time_steps(st, steps, warmup, False)
+        len_sum = int(st.cache_len.sum().item())
+        nbytes = step_bytes_lens(w, len_sum)
+        rec = {"config": label, "workload": w.name, "layers": w.layers, "batch": w.batch,
+               "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+               "cache_len": (f"U{{{w.ragged_min}..{w.cache_len}}}" if w.ragged_min else w.cache_len),
+               "cache_len_sum": len_sum, "block_k": w.block_k, "consensus": "greedy",
+               "step_us": round(ms * 1e3, 2), "algorithmic_bytes_per_step": nbytes,
+               "achieved_tbs": round(nbytes / (ms * 1e-3) / 1e12, 4),
+               "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "tokens_verified_per_s": round(w.batch * w.block_k / (ms * 1e-3), 1)}
+        if label == "C5":
+            p, q, cand, u = sample_inputs(w, device=device)
+            B, K, V = p.shape
+            acc = torch.empty(B, dtype=torch.int32, device=device)
+            corr = torch.empty(B, dtype=torch.int32, device=device)
+            sws = torch.empty(dvb.orthrus_consensus_workspace_size(B, K, V), dtype=torch.uint8, device=device)
+
+            def sample(sp, p=p, q=q, cand=cand, u=u, acc=acc, corr=corr, sws=sws):
+                dvb.orthrus_consensus_sample(p, q, cand, u, acc, corr, sws, stream=sp)
+
+            stream = torch.cuda.current_stream()
+            rec["sample_consensus_us"] = round(_time_calls(lambda: sample(stream.cuda_stream), 20, stream), 2)
+            ms_s, _ = time_steps(_SampleStep(st, sample), steps, warmup, False)
+            rec["step_with_sample_consensus_us"] = round(ms_s * 1e3, 2)
+            rec["sample_accept_len"] = acc.cpu().tolist()
+            del p, q, cand, u, sws
+        out[f"{label}_{w.name}_k{w.block_k}"] = rec
+        print(f"[bench] {label} {w.name} K={w.block_k}: step {ms * 1e3:.1f} us "
+              f"({rec['achieved_tbs']:.2f} TB/s)"
+              + (f", sampler {rec['sample_consensus_us']:.1f} us" if label == "C5" else ""),
+              file=sys.stderr, flush=True)
+        del st, caches, kc, vc
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_tree_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int = 4, m: int = 4):
     """Tree-verification cycles through dual_view_block_amd.cycle.TreeDecodeCycles
     (one round of `n_sets` cycles captured in a HIP graph and replayed), plus
@@ -651,6 +739,7 @@ def main():
         profile_target(args, w, caches, device)
         return
     step = Step(w, caches, device)
+    splits = step.splits
     ms, wall_ms = time_steps(step, args.steps, args.warmup, args.graph)
     kern = time_kernels(step)
     print(f"[bench] step {ms * 1e3:.1f} us (host wall {wall_ms * 1e3:.1f} us), streaming kernel "
@@ -698,6 +787,12 @@ def main():
               f"({fkl['loss']['achieved_gbs']:.0f} GB/s), loss+grad {fkl['loss_and_grad']['us']:.1f} us "
               f"({fkl['loss_and_grad']['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
 
+    cfg = None
+    if args.configs:
+        del step
+        torch.cuda.empty_cache()
+        cfg = time_configs(device, args.steps, args.warmup)
+
     step_bytes = 2 * w.layers * attn_bytes(w) + greedy_bytes(w)
     value = step_bytes / (ms * 1e-3) / 1e12
     pbytes = stream_bytes(w)
@@ -720,7 +815,7 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "cache_len": w.cache_len,
                    "block_k": w.block_k, "vocab": w.vocab, "consensus": "greedy",
-                   "launch": "hip_graph" if args.graph else "eager", "splits": step.splits},
+                   "launch": "hip_graph" if args.graph else "eager", "splits": splits},
         "step_us": round(ms * 1e3, 2),
         "tokens_verified_per_s": round(w.batch * w.block_k / (ms * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
@@ -744,6 +839,8 @@ def main():
         line["train_attention"] = tra
     if tcy is not None:
         line["tree_cycles"] = tcy
+    if cfg is not None:
+        line["other_configs"] = cfg
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, caches, device)
     print(json.dumps(line), flush=True)
