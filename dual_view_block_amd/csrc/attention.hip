@@ -413,20 +413,24 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   };
 
   // ---- pipeline: at the top of iteration t, tile t sits in LDS stage t & 1
-  // and the registers hold tile t+1 (landed or landing).  After the barrier
-  // every wave is past iteration t-1, so stage (t+1) & 1 takes tile t+1 and
-  // the registers take tile t+2 while tile t is computed.
+  // (written before the last barrier) and the registers hold tile t+1 (landed
+  // or landing).  Each wave computes tile t, then writes tile t+1 into the
+  // other stage -- every wave finished reading it before the last barrier --
+  // and loads tile t+2 into the registers; the barrier then publishes tile
+  // t+1.  Computing first keeps the stage writes off the path of this wave's
+  // LDS reads.
   Stage stg;
   load_tile(0, stg);
   store_tile(0, stg);
   load_tile(1, stg);
+  __syncthreads();
   for (int t = 0; t < sr.ntiles; ++t) {
-    __syncthreads();
+    compute(t & 1, t);
     if (t + 1 < sr.ntiles) {
       store_tile((t + 1) & 1, stg);
       load_tile(t + 2, stg);
     }
-    compute(t & 1, t);
+    __syncthreads();
   }
 
   // ---- combine the two key halves of each query block through LDS: wave w
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   // lane-major) and its row statistics to the partner wave w ^ 1.
   const float l_row = l_run + __shfl_xor(l_run, 32);
   float* xch = reinterpret_cast<float*>(smem);
-  __syncthreads();  // every wave is past its last tile: the ring is free
+  // every wave is past its last tile (the loop ends on a barrier): the ring is free
   if (active) {
 #pragma unroll
     for (int j = 0; j < HMB; ++j)
