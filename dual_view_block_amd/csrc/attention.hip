@@ -70,8 +70,10 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int 
   int L = a.len_step > 0 ? b * a.len_step : a.cache_len[b];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int S = a.splits;
-  int chunk = (L + S - 1) / S;
-  chunk = (chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
+  // as even as the key count allows: a length that is not a multiple of S
+  // tiles leaves every split a short last tile rather than some splits a whole
+  // extra one (splits need not start on a tile boundary)
+  const int chunk = (L + S - 1) / S;
   r.kstart = split * chunk;
   r.kend = min(r.kstart + chunk, L);
   r.ncache = r.kstart < r.kend ? (r.kend - r.kstart + kTileKeys - 1) / kTileKeys : 0;

@@ -8,7 +8,8 @@ namespace orthrus {
 
 // ---------------------------------------------------------------- attention
 // Keys per LDS tile.  Every (sequence, KV head) range of cache rows is cut
-// into `splits` contiguous chunks that are whole multiples of this.
+// into `splits` contiguous chunks of ceil(L / splits) keys, each streamed in
+// tiles of this many keys (the last one of a chunk possibly short).
 constexpr int kTileKeys = 64;
 // The streaming kernel runs one 512-thread work-group (two waves per SIMD)
 // per CU; with more than one split per (sequence, KV head) the launch never
