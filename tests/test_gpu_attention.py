@@ -72,6 +72,15 @@ def test_long_context_32k_k_sweep(mode, K):
     _check(_inputs(w), mode, f"32k/K{K}")
 
 
+@pytest.mark.parametrize("L", [33000, 33918])
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_long_context_past_32k(mode, L):
+    """Lengths the decode cycles reach past 32768: 32 splits of ceil(L/32) keys,
+    each ending with a short tile (capacity 36864, as in the cycles)."""
+    w = WORKLOADS["qwen3_8b_32k"].replace(cache_len=L, max_len=36864)
+    _check(_inputs(w), mode, f"L{L}")
+
+
 @pytest.mark.parametrize("K", [1, 32])
 @pytest.mark.parametrize("mode", ["diff", "verify"])
 def test_long_context_128k(mode, K):
