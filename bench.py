@@ -71,7 +71,8 @@ def _parse():
     ap.add_argument("--traffic", default=TRAFFIC_JSON,
                     help="JSON record of rocprofv3-derived HBM bytes per streaming-kernel launch "
                          "(ignored if the code of attention.hip changed since it was taken)")
-    ap.add_argument("--profile-target", choices=["attn-stream", "copy", "forward-kl", "train-attn"], default=None,
+    ap.add_argument("--profile-target", choices=["attn-stream", "copy", "forward-kl", "train-attn", "consensus"],
+                    default=None,
                     help="run only the streaming kernel over every layer-view (or a plain copy "
                          "kernel of --copy-mib MiB, or the forward KL with its gradient at "
                          "--kl-rows x vocab) --steps times, for rocprofv3 counter runs")
@@ -641,6 +642,18 @@ def profile_target(args, w, caches, device) -> None:
     elif args.profile_target == "train-attn":
         for _ in range(args.steps):
             time_train_attn(w, device, reps=1)
+    elif args.profile_target == "consensus":
+        import dual_view_block_amd as dvb
+        from synth import WORKLOADS, greedy_inputs, sample_inputs
+
+        logits, cand, _ = greedy_inputs(w, device=device)  # [1, 32, 151936]
+        wr = WORKLOADS["ragged_b16"]
+        p, q, sc, u = sample_inputs(wr, device=device)     # [16, 32, 151936], drafts independent of targets
+        pc, qc, scc, uc = sample_inputs(wr, device=device, draft_noise=0.5)  # drafts close to their targets
+        for _ in range(args.steps):
+            dvb.orthrus_consensus_greedy(logits, cand)
+            dvb.orthrus_consensus_sample(p, q, sc, u)
+            dvb.orthrus_consensus_sample(pc, qc, scc, uc)
     elif args.profile_target == "forward-kl":
         import dual_view_block_amd as dvb
         from synth import kl_inputs
@@ -722,7 +735,7 @@ def main():
     if args.layers:
         w = w.replace(layers=args.layers)
     print(f"[bench] workload {w}", file=sys.stderr, flush=True)
-    if args.profile_target in ("copy", "forward-kl", "train-attn"):
+    if args.profile_target in ("copy", "forward-kl", "train-attn", "consensus"):
         profile_target(args, w, None, device)
         return
     # one layer-major cache for all layers, with room past L for the rows the
