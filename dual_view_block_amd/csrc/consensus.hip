@@ -238,6 +238,8 @@ __device__ unsigned long long block_scan64(unsigned long long v, unsigned long l
   return v + off;
 }
 
+constexpr int kSelectEpt = 16;  // consecutive elements per thread in the in-chunk scan
+
 __global__ __launch_bounds__(kThreads) void residual_select_kernel(int block_k, int vocab, int chunk_len,
                                                                    int chunks,
                                                                    const float* __restrict__ p,
@@ -280,31 +282,56 @@ __global__ __launch_bounds__(kThreads) void residual_select_kernel(int block_k, 
   if (c < chunks && mine > 0 && inc - mine <= T && T < inc) found = c;
   __syncthreads();
   const int cs = found;
-  unsigned long long run = 0;
-  for (int k = 0; k < cs; ++k) run += sums[((size_t)b * chunks + k) * 2 + (use_p ? 1 : 0)];
-  // ---- scan inside the chunk, kThreads elements at a time
+  // exclusive prefix of the chosen chunk, straight from the scan above
+  __shared__ unsigned long long run_sh;
+  if (c == cs) run_sh = inc - mine;
+  __syncthreads();
+  unsigned long long run = run_sh;
+  // ---- scan inside the chunk: each thread takes kSelectEpt consecutive
+  // elements (all their loads in flight at once), one block scan of the
+  // per-thread sums finds the thread whose elements hold T, and that thread
+  // walks its own elements; chunks longer than kThreads * kSelectEpt take
+  // several passes
   const size_t row = ((size_t)b * block_k + a) * vocab;
   const int begin = cs * chunk_len;
   const int end = min(vocab, begin + chunk_len);
   __shared__ int pick;
   if (threadIdx.x == 0) pick = -1;
   __syncthreads();
-  for (int base = begin; base < end; base += kThreads) {
-    const int v = base + threadIdx.x;
-    unsigned long long w = 0;
-    if (v < end) {
-      const unsigned long long fp = fixed_point(p[row + v]);
-      if (use_p) {
-        w = fp;
-      } else {
-        const unsigned long long fq = fixed_point(q[row + v]);
-        w = fp > fq ? fp - fq : 0ull;
+  for (int base = begin; base < end; base += kThreads * kSelectEpt) {
+    const int v0 = base + (int)threadIdx.x * kSelectEpt;
+    unsigned long long w[kSelectEpt];
+    unsigned long long tw = 0;
+#pragma unroll
+    for (int i = 0; i < kSelectEpt; ++i) {
+      const int v = v0 + i;
+      unsigned long long wi = 0;
+      if (v < end) {
+        const unsigned long long fp = fixed_point(p[row + v]);
+        if (use_p) {
+          wi = fp;
+        } else {
+          const unsigned long long fq = fixed_point(q[row + v]);
+          wi = fp > fq ? fp - fq : 0ull;
+        }
       }
+      w[i] = wi;
+      tw += wi;
     }
     unsigned long long tot;
-    const unsigned long long incl = block_scan64(w, &tot, scratch) + run;
-    const bool hit = v < end && incl > T && incl - w <= T;
-    if (hit) pick = v;  // exactly one element satisfies both bounds
+    const unsigned long long incl = block_scan64(tw, &tot, scratch) + run;
+    const unsigned long long excl = incl - tw;
+    if (tw > 0 && excl <= T && T < incl) {  // exactly one thread holds T
+      unsigned long long acc = excl;
+#pragma unroll
+      for (int i = 0; i < kSelectEpt; ++i) {
+        acc += w[i];
+        if (acc > T) {
+          pick = v0 + i;
+          break;
+        }
+      }
+    }
     __syncthreads();
     if (pick >= 0) break;
     run += tot;
