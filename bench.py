@@ -812,6 +812,8 @@ def main():
     achieved = pbytes / (kern["attn_stream_us"] * 1e-6) / 1e9
     traffic = load_traffic(args.traffic)
     flops = w.layers * (attn_flops(w, False) + attn_flops(w, True))
+    # the timed launches cover both views equally: their mean per launch
+    sflops = (attn_flops(w, False) + attn_flops(w, True)) // 2
     line = {
         "metric": METRIC,
         "value": round(value, 4),
@@ -834,6 +836,11 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "frac_hbm_peak_step": round(value * 1e3 / HBM_PEAK_GBS, 4),
         "mfma_tflops_step": round(flops / (ms * 1e-3) / 1e12, 2),
+        "frac_mfma_bf16_peak_step": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "stream_kernel_mfma": {"flops_per_launch": sflops,
+                               "tflops": round(sflops / (kern["attn_stream_us"] * 1e-6) / 1e12, 1),
+                               "frac_bf16_peak": round(sflops / (kern["attn_stream_us"] * 1e-6) / 1e12
+                                                       / MFMA_BF16_PEAK_TFLOPS, 4)},
         "step_us_vs_block_k": {str(k): round(v, 2) for k, v in sweep.items()},
         "k32_over_k1": round(sweep[32] / sweep[1], 4) if 32 in sweep and 1 in sweep else None,
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
