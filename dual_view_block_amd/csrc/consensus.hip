@@ -178,6 +178,8 @@ __global__ __launch_bounds__(64) void sample_accept_kernel(int block_k, int voca
   }
 }
 
+constexpr int kChunkEpt = 16;  // elements per thread and pass in the residual chunk sums
+
 __global__ __launch_bounds__(kThreads) void residual_chunks_kernel(int block_k, int vocab, int chunk_len,
                                                                    const float* __restrict__ p,
                                                                    const float* __restrict__ q,
@@ -191,11 +193,24 @@ __global__ __launch_bounds__(kThreads) void residual_chunks_kernel(int block_k, 
   const int begin = c * chunk_len;
   const int end = min(vocab, begin + chunk_len);
   unsigned long long sw = 0, sp = 0;
-  for (int v = begin + threadIdx.x; v < end; v += kThreads) {
-    const unsigned long long fp = fixed_point(p[row + v]);
-    const unsigned long long fq = fixed_point(q[row + v]);
-    sw += fp > fq ? fp - fq : 0ull;
-    sp += fp;
+  // Each pass issues all of a thread's loads (elements t + 256 i, coalesced
+  // across the wave) before any arithmetic: one memory round trip per pass.
+  // Integer sums, so the order does not matter.
+  for (int base = begin; base < end; base += kThreads * kChunkEpt) {
+    float pv[kChunkEpt], qv[kChunkEpt];
+#pragma unroll
+    for (int i = 0; i < kChunkEpt; ++i) {
+      const int v = base + (int)threadIdx.x + i * kThreads;
+      pv[i] = v < end ? p[row + v] : 0.0f;
+      qv[i] = v < end ? q[row + v] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kChunkEpt; ++i) {
+      const unsigned long long fp = fixed_point(pv[i]);
+      const unsigned long long fq = fixed_point(qv[i]);
+      sw += fp > fq ? fp - fq : 0ull;
+      sp += fp;
+    }
   }
   __shared__ unsigned long long red[2][kThreads / 64];
   sw = wave_sum64(sw);
