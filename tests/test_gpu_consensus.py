@@ -98,6 +98,17 @@ def test_sample_small_vocab(seed):
     _check_sample(p, q, cand, u, f"small seed={seed}")
 
 
+@pytest.mark.parametrize("seed,noise", [(77, None), (79, 1.0), (79, 2.0)])
+def test_sample_vocab_past_a_million(seed, noise):
+    """V = 1,200,000: the residual splits the row into 256 chunks of 4688
+    entries, longer than one pass of the chunk-sum and select loops (4096 per
+    pass), so both loops take a second pass.  The cases reject at row 0, at
+    row 1 or not at all."""
+    w = Workload("big_vocab", 1, 2, 1, 1, 1, 1, 2, 1_200_000, 3.0, seed)
+    p, q, cand, u = sample_inputs(w, draft_noise=noise)
+    _check_sample(p, q, cand, u, f"V=1.2M seed={seed} noise={noise}")
+
+
 def test_sample_degenerate_cases():
     B, K, V = 3, 4, 64
     g = torch.Generator().manual_seed(3)
