@@ -383,6 +383,9 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     if (!active || nval <= 32 * kh) return;  // no real key in this half
     bf16x8 kf[NDS];
     load_k(st, kf);
+    // all K fragment reads in flight before the first MFMA (left alone, the
+    // scheduler keeps two or three and each MFMA waits on its own read)
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.0f;

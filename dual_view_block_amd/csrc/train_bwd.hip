@@ -211,6 +211,9 @@ __global__ __launch_bounds__(kBwdThreads) void train_bwd_kernel(const TrainBwdAr
     {
       bf16x8 kf[NDS];
       load_rows(SLOT_KK, st, kf);
+      // all K fragment reads in flight before the first MFMA (doing the same
+      // for the V rows below costs spills)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.0f;
 #pragma unroll
