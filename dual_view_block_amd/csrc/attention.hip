@@ -34,8 +34,9 @@
 //    ds_read_b64_tr_b16, the transposing LDS read, with the key order matched
 //    to the accumulator's register order.
 //  * Softmax: P = 2^(s*scale*log2(e) - m_ref) with a lazily raised reference
-//    m_ref (raised only when a shifted score exceeds it by more than 2^8), so
-//    the accumulator rescale is rare; the sum cancels the reference exactly.
+//    m_ref (raised only when a shifted score exceeds it by more than 8, so
+//    P <= 2^8), so the accumulator rescale is rare; the sum cancels the
+//    reference exactly.
 //    Each key half keeps its own reference, sum and accumulator; at the end
 //    the two waves of a query block combine theirs through LDS, each
 //    finishing half of head_dim.
@@ -45,7 +46,9 @@
 //    as whole coalesced rows with nontemporal stores -- and a second kernel
 //    merges the S partials:
 //    out = sum_s 2^(m_s-M) l_s o_s / sum_s 2^(m_s-M) l_s,
-//    lse = (M + log2 sum_s 2^(m_s-M) l_s) * ln 2, with one wave per row.
+//    lse = (M + log2 sum_s 2^(m_s-M) l_s) * ln 2, with one wave per row and
+//    each XCD merging the rows whose partials its own streaming work-groups
+//    wrote.
 #include "attn_frag.h"
 #include "common.h"
 

@@ -11,8 +11,9 @@
 //   dV_blk = P_blk^T dO,  dK_blk = scale * dS_blk^T Q   (block keys; the sum
 //                                                          over rows covers all G heads)
 //
-// One work-group of 8 waves (512 threads, two per SIMD) per (block, KV head):
-// wave w owns rows 32*(w>>1) .. +31 (each lane one row, as in the streaming
+// One work-group of 8 waves (512 threads, two per SIMD) per (block, KV head),
+// numbered so that each XCD serves one KV head and its L2 keeps that head's
+// clean K/V, which every block of the head re-reads.  Wave w owns rows 32*(w>>1) .. +31 (each lane one row, as in the streaming
 // kernel) against key half w & 1 (32 keys) of every 64-key tile.  Per tile,
 // with the tile in LDS:
 //   S^T  = K Q^T      (A = K rows, B = Q fragments in registers)
