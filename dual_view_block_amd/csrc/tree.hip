@@ -23,6 +23,7 @@ namespace {
 using namespace keys;
 
 constexpr int kTreeThreads = 256;
+constexpr int kTreeMaxNodes = 64;  // nodes per tree (one wave holds them all)
 constexpr int kTopkPerThread = 16;
 constexpr int kTopkChunk = kTopkPerThread * kTreeThreads;
 constexpr float kLog2eT = 1.4426950408889634f;
@@ -152,6 +153,43 @@ __device__ __forceinline__ unsigned long long cand_key(float score, int parent, 
          (unsigned long long)(0xFFFF - rank);
 }
 
+// Maximum of a 64-bit key over the wave, in every lane, without LDS: at each
+// level a lane takes the larger of its key and a partner's, the partners
+// being lane ^ 1 and lane ^ 2 (quad permutes), the mirrored quad of its
+// 8-lane half and the mirrored half of its 16-lane row (DPP), then lane ^ 16
+// and lane ^ 32 (permlane swaps).  After the six levels every lane holds the
+// maximum of all 64.
+__device__ __forceinline__ unsigned long long pick_max(unsigned long long v, uint32_t ohi, uint32_t olo) {
+  const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_step(unsigned long long v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, 0xF, 0xF, false);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, 0xF, 0xF, false);
+  return pick_max(v, ohi, olo);
+}
+__device__ __forceinline__ unsigned long long wave_max64_regs(unsigned long long v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+  v = dpp_max_step<0x4E>(v);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+  v = dpp_max_step<0x141>(v);  // row_half_mirror: the other quad of the 8-lane half
+  v = dpp_max_step<0x140>(v);  // row_mirror: the other half of the 16-lane row
+  {
+    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    v = pick_max(pick_max(v, sh[0], sl[0]), sh[1], sl[1]);  // lane ^ 16
+  }
+  {
+    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+    const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    v = pick_max(pick_max(v, sh[0], sl[0]), sh[1], sl[1]);  // lane ^ 32
+  }
+  return v;
+}
+
 // one wave per sequence; n <= 64 nodes, so every live candidate has a lane
 __global__ __launch_bounds__(64) void tree_build_kernel(int Dd, int m, int n, const float* __restrict__ logp,
                                                         const int32_t* __restrict__ tok,
@@ -169,6 +207,20 @@ __global__ __launch_bounds__(64) void tree_build_kernel(int Dd, int m, int n, co
     to[lane] = lane == 0 ? anchor[b] : -1;
     dout[lane] = 0;
   }
+  // The reachable part of this sequence's marginals, staged in LDS once: a
+  // tree of n <= 64 nodes reaches depth n - 1 <= 63 at most, and a parent's
+  // rank r at most n - 2, so depths < 64 and ranks < 64 cover every step.
+  // Each step then reads LDS instead of waiting on a global load.
+  __shared__ float slp[kTreeMaxNodes * kTreeMaxNodes];
+  __shared__ int32_t stk[kTreeMaxNodes * kTreeMaxNodes];
+  const int dd = Dd < kTreeMaxNodes ? Dd : kTreeMaxNodes;
+  const int mm = m < kTreeMaxNodes ? m : kTreeMaxNodes;
+  for (int e = lane; e < dd * mm; e += 64) {
+    const int d = e / mm, r = e % mm;
+    slp[e] = lp[(size_t)d * m + r];
+    stk[e] = tk[(size_t)d * m + r];
+  }
+  __syncthreads();
   float nscore = 0.0f;  // lane j: score of node j
   int ndep = 0;         // lane j: depth of node j
   bool cv = false;      // this lane's candidate slot
@@ -176,29 +228,31 @@ __global__ __launch_bounds__(64) void tree_build_kernel(int Dd, int m, int n, co
   int cp = 0, cr = 0;
   if (lane == 0 && Dd > 0 && m > 0) {
     cv = true;
-    cs = 0.0f + lp[0];
+    cs = 0.0f + slp[0];
   }
   for (int made = 1; made < n; ++made) {
     const unsigned long long key = cv ? cand_key(cs, cp, cr) : 0ull;
-    const unsigned long long best = wave_max64(key);
+    const unsigned long long best = wave_max64_regs(key);
     if (best == 0ull) break;
+    // winner and p are the same in every lane: read the values straight from
+    // their lanes (readlane) rather than through an LDS shuffle
     const int winner = __builtin_ctzll(__ballot(key == best));
-    const int p = __shfl(cp, winner), r = __shfl(cr, winner);
-    const float s = __shfl(cs, winner);
-    const int d = __shfl(ndep, p);
-    const float ps = __shfl(nscore, p);
+    const int p = __builtin_amdgcn_readlane(cp, winner), r = __builtin_amdgcn_readlane(cr, winner);
+    const float s = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(cs), winner));
+    const int d = __builtin_amdgcn_readlane(ndep, p);
+    const float ps = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(nscore), p));
     if (lane == made) {
       nscore = s;
       ndep = d + 1;
     }
     if (lane == 0) {
       po[made] = p;
-      to[made] = tk[d * m + r];
+      to[made] = stk[d * mm + r];
       dout[made] = d + 1;
     }
     if (lane == winner) {  // the parent's next-ranked child takes the slot
       if (r + 1 < m) {
-        cs = ps + lp[d * m + r + 1];
+        cs = ps + slp[d * mm + r + 1];
         cr = r + 1;
       } else {
         cv = false;
@@ -208,7 +262,7 @@ __global__ __launch_bounds__(64) void tree_build_kernel(int Dd, int m, int n, co
       const int slot = __builtin_ctzll(__ballot(!cv));
       if (lane == slot) {
         cv = true;
-        cs = s + lp[(d + 1) * m];
+        cs = s + slp[(d + 1) * mm];
         cp = made;
         cr = 0;
       }
