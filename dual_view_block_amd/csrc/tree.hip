@@ -46,24 +46,79 @@ __global__ __launch_bounds__(kTreeThreads) void tree_mask_kernel(int batch, int 
   mask[n] = m;
 }
 
+// Wave reductions in registers, the result in every lane, without LDS: the
+// partners at the six levels are lane ^ 1 and lane ^ 2 (quad permutes), the
+// mirrored quad of the 8-lane half and the mirrored half of the 16-lane row
+// (DPP), then lane ^ 16 and lane ^ 32 (permlane swaps).  Each lane combines
+// its value with its partner's, so after six levels every lane holds the
+// result; for sums both lanes of a pair add the same two values, so every
+// lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_partner(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t partner16(uint32_t x) {  // lane ^ 16
+  const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return ((threadIdx.x >> 4) & 1) ? sw[0] : sw[1];
+}
+__device__ __forceinline__ uint32_t partner32(uint32_t x) {  // lane ^ 32
+  const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return ((threadIdx.x >> 5) & 1) ? sw[0] : sw[1];
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce32(uint32_t v, Op op) {
+  v = op(v, dpp_partner<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_partner<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_partner<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_partner<0x140>(v));  // row_mirror
+  v = op(v, partner16(v));
+  v = op(v, partner32(v));
+  return v;
+}
+__device__ __forceinline__ float wave_max_f_regs(float v) {
+  return __uint_as_float(wave_reduce32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_sum_f_regs(float v) {
+  return __uint_as_float(wave_reduce32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+__device__ __forceinline__ unsigned long long pick_max(unsigned long long v, uint32_t ohi, uint32_t olo) {
+  const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_step(unsigned long long v) {
+  return pick_max(v, dpp_partner<CTRL>((uint32_t)(v >> 32)), dpp_partner<CTRL>((uint32_t)v));
+}
+__device__ __forceinline__ unsigned long long wave_max64_regs(unsigned long long v) {
+  v = dpp_max_step<0xB1>(v);
+  v = dpp_max_step<0x4E>(v);
+  v = dpp_max_step<0x141>(v);
+  v = dpp_max_step<0x140>(v);
+  v = pick_max(v, partner16((uint32_t)(v >> 32)), partner16((uint32_t)v));
+  v = pick_max(v, partner32((uint32_t)(v >> 32)), partner32((uint32_t)v));
+  return v;
+}
+
 __device__ __forceinline__ float block_max_f(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = wave_max_f_regs(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 __device__ __forceinline__ float block_sum_f(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  v = wave_sum_f_regs(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 __device__ __forceinline__ unsigned long long block_max_k(unsigned long long v, unsigned long long* red) {
-  v = wave_max64(v);
+  v = wave_max64_regs(v);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -124,12 +179,10 @@ __global__ __launch_bounds__(kTreeThreads) void topk_finalize_kernel(int rows, i
   const float* ml = part_ml + (size_t)row * chunks * 2;
   float M = -__builtin_inff();
   for (int c = lane; c < chunks; c += 64) M = fmaxf(M, ml[2 * c]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  M = wave_max_f_regs(M);
   float S = 0.0f;
   for (int c = lane; c < chunks; c += 64) S = fmaf(ml[2 * c + 1], __builtin_amdgcn_exp2f((ml[2 * c] - M) * kLog2eT), S);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) S += __shfl_xor(S, o);
+  S = wave_sum_f_regs(S);
   const float lse = M + logf(S);
   const unsigned long long* ks = part_keys + (size_t)row * chunks * m;
   unsigned long long last = ~0ull;
@@ -140,7 +193,7 @@ __global__ __launch_bounds__(kTreeThreads) void topk_finalize_kernel(int rows, i
         const unsigned long long k = ks[(size_t)c * m + j];
         best = umax64(best, k < last ? k : 0ull);
       }
-    last = wave_max64(best);
+    last = wave_max64_regs(best);
     if (lane == 0) {
       logp[(size_t)row * m + r] = key_value((uint32_t)(last >> 32)) - lse;
       idx[(size_t)row * m + r] = (int32_t)(0xFFFFFFFFu - (uint32_t)(last & 0xFFFFFFFFull));
@@ -151,43 +204,6 @@ __global__ __launch_bounds__(kTreeThreads) void topk_finalize_kernel(int rows, i
 __device__ __forceinline__ unsigned long long cand_key(float score, int parent, int rank) {
   return ((unsigned long long)order_key(score) << 32) | ((unsigned long long)(0xFFFF - parent) << 16) |
          (unsigned long long)(0xFFFF - rank);
-}
-
-// Maximum of a 64-bit key over the wave, in every lane, without LDS: at each
-// level a lane takes the larger of its key and a partner's, the partners
-// being lane ^ 1 and lane ^ 2 (quad permutes), the mirrored quad of its
-// 8-lane half and the mirrored half of its 16-lane row (DPP), then lane ^ 16
-// and lane ^ 32 (permlane swaps).  After the six levels every lane holds the
-// maximum of all 64.
-__device__ __forceinline__ unsigned long long pick_max(unsigned long long v, uint32_t ohi, uint32_t olo) {
-  const unsigned long long o = ((unsigned long long)ohi << 32) | olo;
-  return o > v ? o : v;
-}
-template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_max_step(unsigned long long v) {
-  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
-  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, 0xF, 0xF, false);
-  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, 0xF, 0xF, false);
-  return pick_max(v, ohi, olo);
-}
-__device__ __forceinline__ unsigned long long wave_max64_regs(unsigned long long v) {
-  v = dpp_max_step<0xB1>(v);   // quad_perm [1, 0, 3, 2]: lane ^ 1
-  v = dpp_max_step<0x4E>(v);   // quad_perm [2, 3, 0, 1]: lane ^ 2
-  v = dpp_max_step<0x141>(v);  // row_half_mirror: the other quad of the 8-lane half
-  v = dpp_max_step<0x140>(v);  // row_mirror: the other half of the 16-lane row
-  {
-    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
-    const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    v = pick_max(pick_max(v, sh[0], sl[0]), sh[1], sl[1]);  // lane ^ 16
-  }
-  {
-    const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
-    const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    v = pick_max(pick_max(v, sh[0], sl[0]), sh[1], sl[1]);  // lane ^ 32
-  }
-  return v;
 }
 
 // one wave per sequence; n <= 64 nodes, so every live candidate has a lane
