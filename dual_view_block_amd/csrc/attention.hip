@@ -96,6 +96,35 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int 
 // S-1 and get weight 0.  Every sum runs in a fixed order, so all callers get
 // identical bits.  `row` is inside the work-group row block; rows at or past
 // `row_end` are read (clamped) but not written.
+// Reductions over the LPR lanes of a merge row, in registers (no LDS): the
+// partners at each level are lane ^ 1 and lane ^ 2 (quad permutes), the
+// mirrored quad of the 8-lane half and the mirrored half of the 16-lane row
+// (DPP), lane ^ 16 and, for 64-lane rows, lane ^ 32 (permlane swaps).  Both
+// lanes of a pair combine the same two values, so every lane of the row ends
+// with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float partner16_f(float x) {  // lane ^ 16
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((threadIdx.x >> 4) & 1) ? sw[0] : sw[1]);
+}
+__device__ __forceinline__ float partner32_f(float x) {  // lane ^ 32
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(((threadIdx.x >> 5) & 1) ? sw[0] : sw[1]);
+}
+template <int LPR, typename Op>
+__device__ __forceinline__ float row_reduce(float v, Op op) {
+  v = op(v, dpp_partner_f<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_partner_f<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_partner_f<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_partner_f<0x140>(v));  // row_mirror
+  v = op(v, partner16_f(v));
+  if constexpr (LPR == 64) v = op(v, partner32_f(v));
+  return v;
+}
+
 template <int D, int SMAX>
 __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p, int grp, int row, int row_end) {
   constexpr int LPR = D / 2;                  // lanes per row
@@ -127,8 +156,7 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
   float M = m[0];
 #pragma unroll
   for (int c = 1; c < NW; ++c) M = fmaxf(M, m[c]);
-#pragma unroll
-  for (int o = 1; o < LPR; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+  M = row_reduce<LPR>(M, [](float a, float b) { return fmaxf(a, b); });
   float wt[NW];
   float L = 0.0f;
 #pragma unroll
@@ -136,8 +164,7 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
     wt[c] = (m[c] == kNegInf) ? 0.0f : fast_exp2(m[c] - M) * l[c];
     L += wt[c];
   }
-#pragma unroll
-  for (int o = 1; o < LPR; o <<= 1) L += __shfl_xor(L, o);
+  L = row_reduce<LPR>(L, [](float a, float b) { return a + b; });
   // out = sum_s w_s o_s in split order; w_s is read from the lane holding it
   float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
