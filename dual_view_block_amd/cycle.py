@@ -1,9 +1,10 @@
 """Synthetic multi-cycle decode driver over the C ABI.
 
-One Orthrus decode cycle (paper notes §4.1) is, per layer, the diffusion-view
-block attention and the AR verify block attention over the shared cache, then
-one consensus over the verify distributions, then the commit that writes the
-verified rows into the cache and advances the lengths.  This driver issues
+One Orthrus decode cycle (paper notes §4.1) is the diffusion-view block
+attention of every layer, then the AR verify block attention of every layer
+(both over the shared cache), then one consensus over the verify
+distributions, then the commit that writes the verified rows into the cache
+and advances the lengths.  This driver issues
 exactly those calls, cycle after cycle, on one HIP stream: lengths live on the
 device and every call reads them there, so the host never waits for a cycle to
 finish before issuing the next one.  There is no model between the calls: each
@@ -67,11 +68,15 @@ class DecodeCycles:
             acc, corr = torch.empty(B, **i32), torch.empty(B, **i32)
             anchor, toks, ntok = torch.empty(B, **i32), torch.empty((B, K), **i32), torch.empty(B, **i32)
             _need(s["cand"], "cand", torch.int32, (B, K), dev)
+            # the whole diffusion forward (every layer), then the whole verify
+            # forward: the verify pass needs the candidates the diffusion pass
+            # produces, so a real cycle cannot interleave the two per layer
             calls = []
             for l in range(self.n_layers):
                 q, k_blk, v_blk = s["diff"][l]
                 calls.append(PreparedAttention(ORTHRUS_MASK_DIFF_BIDIR, q, k_blk, v_blk, k_cache[l], v_cache[l],
                                                cache_len, d_out[l], None, self.attn_ws, softmax_scale))
+            for l in range(self.n_layers):
                 calls.append(PreparedAttention(ORTHRUS_MASK_VERIFY_CAUSAL, s["verify"][l][0], kb[l], vb[l],
                                                k_cache[l], v_cache[l], cache_len, v_out[l], None, self.attn_ws,
                                                softmax_scale))

@@ -34,6 +34,8 @@ Readings of points the pages leave open:
   the correction is token 0.
 * R11 -- uniforms are [B, K+1] float32 on the 2**-24 grid in [0, 1):
   u[0..K-1] for the accept tests, u[K] for the residual draw.
+* R28 -- a candidate outside [0, V) is not a token of the vocabulary: the
+  target gives it probability 0, so it is rejected like any p = 0 token.
 
 Inputs must be finite probability rows for the sampler (each row sums to at
 most 8, which keeps every 64-bit prefix sum exact); outside that contract
@@ -179,12 +181,16 @@ def sample_consensus(p_target, q_draft, cand, uniforms):
     Q = _np(q_draft, np.float32)
     cd = _np(cand, np.int64)
     U = _np(uniforms, np.float32)
-    B, K, _ = P.shape
+    B, K, V = P.shape
     acc = np.zeros(B, dtype=np.int64)
     corr = np.zeros(B, dtype=np.int64)
     for b in range(B):
-        pc = np.array([P[b, i, cd[b, i]] for i in range(K)])
-        qc = np.array([Q[b, i, cd[b, i]] for i in range(K)])
+        # R28: a candidate outside the vocabulary [0, V) is a token the target
+        # gives probability 0, so the strict accept test rejects it (R8); its
+        # draft probability is then irrelevant and is taken as 0.
+        inside = [0 <= cd[b, i] < V for i in range(K)]
+        pc = np.array([P[b, i, cd[b, i]] if inside[i] else 0.0 for i in range(K)], dtype=np.float32)
+        qc = np.array([Q[b, i, cd[b, i]] if inside[i] else 0.0 for i in range(K)], dtype=np.float32)
         a = accept_prefix(pc, qc, U[b, :K])
         acc[b] = a
         if a == K:

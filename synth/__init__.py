@@ -179,6 +179,51 @@ def greedy_inputs(w: Workload, device="cpu", first_mismatch=None, ties: bool = F
     return logits.to(device), cand.to(torch.int32).to(device), j_star
 
 
+# Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+# easy as 1, 2, 3", SC 2011): a counter-based generator.  Each 128-bit counter
+# (four 32-bit words) and 64-bit key give four independent 32-bit outputs;
+# ten rounds, each two 32x32->64 multiplications whose halves are mixed with
+# the other words and the key, the key bumped by the Weyl constants between
+# rounds.
+_PHILOX_M = (0xD2511F53, 0xCD9E8D57)
+_PHILOX_W = (0x9E3779B9, 0xBB67AE85)
+_U32 = 0xFFFFFFFF
+
+
+def philox4x32(counters, key):
+    """Philox4x32-10 of uint64 arrays holding 32-bit words.
+
+    counters: int array [..., 4]; key: (k0, k1).  Returns uint64 [..., 4]."""
+    import numpy as np
+
+    c = np.asarray(counters, dtype=np.uint64) & np.uint64(_U32)
+    c0, c1, c2, c3 = (c[..., i].copy() for i in range(4))
+    k0, k1 = np.uint64(key[0] & _U32), np.uint64(key[1] & _U32)
+    m0, m1 = np.uint64(_PHILOX_M[0]), np.uint64(_PHILOX_M[1])
+    lo = np.uint64(_U32)
+    for r in range(10):
+        p0, p1 = m0 * c0, m1 * c2            # exact: both factors < 2^32
+        c0, c1, c2, c3 = ((p1 >> np.uint64(32)) ^ c1 ^ k0, p1 & lo,
+                          (p0 >> np.uint64(32)) ^ c3 ^ k1, p0 & lo)
+        if r < 9:
+            k0 = (k0 + np.uint64(_PHILOX_W[0])) & lo
+            k1 = (k1 + np.uint64(_PHILOX_W[1])) & lo
+    return np.stack([c0, c1, c2, c3], axis=-1)
+
+
+def philox_uniforms(n: int, seed: int) -> torch.Tensor:
+    """float64 [n] uniforms on the 2**-24 grid in [0, 1): output word j of
+    the Philox4x32-10 block with counter (j // 4, 0, 0, 0) and key (seed mod
+    2^32, seed >> 32), top 24 bits."""
+    import numpy as np
+
+    blocks = (n + 3) // 4
+    ctr = np.zeros((blocks, 4), dtype=np.uint64)
+    ctr[:, 0] = np.arange(blocks, dtype=np.uint64)
+    words = philox4x32(ctr, (int(seed) & _U32, (int(seed) >> 32) & _U32)).reshape(-1)[:n]
+    return torch.from_numpy((words >> np.uint64(8)).astype(np.float64) / 16777216.0)
+
+
 def quantise_uniforms(u: torch.Tensor) -> torch.Tensor:
     """Put float uniforms on the 2**-24 grid in [0, 1) (exact in float32)."""
     return (torch.floor(u.double() * 16777216.0).clamp(0, 16777215) / 16777216.0).float()
@@ -191,8 +236,9 @@ def sample_inputs(w: Workload, device="cpu", draft_noise: Optional[float] = None
     z_p ~ N(0, sigma); z_q ~ N(0, sigma) independent, or z_q = z_p + N(0,
     draft_noise) when ``draft_noise`` is set (a draft close to the target, so
     acceptance runs long).  p, q = softmax in float64 rounded to float32.
-    cand[b, i] ~ q[b, i] (seeded multinomial); uniforms [B, K+1] on the 2**-24
-    grid.  Returns (p, q, cand int32, uniforms float32).
+    cand[b, i] ~ q[b, i] by inverse CDF of a Philox4x32-10 uniform; uniforms
+    [B, K+1] on the 2**-24 grid from a second Philox stream.  Returns (p, q,
+    cand int32, uniforms float32).
     """
     g = _gen(w.seed * 131 + 5 + seed_offset, "cpu")
     B, K, V, s = w.batch, w.block_k, w.vocab, float(w.logit_sigma)
@@ -204,10 +250,12 @@ def sample_inputs(w: Workload, device="cpu", draft_noise: Optional[float] = None
     p64 = torch.softmax(zp, dim=-1)
     q64 = torch.softmax(zq, dim=-1)
     del zp, zq
-    gc = _gen(w.seed * 131 + 6 + seed_offset, "cpu")
-    cand = torch.multinomial(q64.reshape(B * K, V), 1, generator=gc).reshape(B, K)
-    gu = _gen(w.seed * 131 + 7 + seed_offset, "cpu")
-    u = quantise_uniforms(torch.rand((B, K + 1), generator=gu, dtype=torch.float64))
+    # cand ~ q by inverse CDF of one Philox uniform per row; the accept and
+    # residual uniforms from a second Philox stream
+    uc = philox_uniforms(B * K, w.seed * 131 + 6 + seed_offset).reshape(B * K, 1)
+    cdf = torch.cumsum(q64.reshape(B * K, V), dim=-1)
+    cand = torch.searchsorted(cdf, uc * cdf[:, -1:], right=True).clamp_(max=V - 1).reshape(B, K)
+    u = quantise_uniforms(philox_uniforms(B * (K + 1), w.seed * 131 + 7 + seed_offset).reshape(B, K + 1))
     return (p64.float().to(device), q64.float().to(device),
             cand.to(torch.int32).to(device), u.to(device))
 

@@ -81,11 +81,21 @@ def test_long_context_past_32k(mode, L):
     _check(_inputs(w), mode, f"L{L}")
 
 
-@pytest.mark.parametrize("K", [1, 32])
+@pytest.mark.parametrize("K", [1, 4, 8, 16, 32])
 @pytest.mark.parametrize("mode", ["diff", "verify"])
 def test_long_context_128k(mode, K):
+    """L=131072 at every block size of the K sweep."""
     w = WORKLOADS["qwen3_8b_128k"].replace(block_k=K)
     _check(_inputs(w), mode, f"128k/K{K}")
+
+
+@pytest.mark.parametrize("K", [64, 128])
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_large_blocks_32k(mode, K):
+    """K = 64 and 128 at L=32768, Qwen3-8B heads: 256 and 512 query rows per
+    KV head, the shapes the block-size sweep times past K = 32."""
+    w = WORKLOADS["qwen3_8b_32k"].replace(block_k=K)
+    _check(_inputs(w), mode, f"32k/K{K}")
 
 
 @pytest.mark.parametrize("mode", ["diff", "verify"])

@@ -1,0 +1,112 @@
+"""GPU parity when the running softmax maximum moves during the stream.
+
+With N(0, 1) inputs and the 1/sqrt(D) scale no key after the first tiles
+tops the early maximum by much, so the online softmax never has to rescale
+its accumulator after it started.  These cases make it do so, and compare
+with the fp64 oracle at the usual bar (max-abs 2e-2, rel-L2 5e-3, lse 1e-3):
+
+* softmax scale 1.0: scores spread over ~16 base-2 units per standard
+  deviation, so the maximum keeps rising as more keys are seen;
+* planted keys: cache rows equal to twice a query row, placed in late tiles
+  of several splits, in the block keys, and at position 0 (an attention
+  sink), at the default scale;
+* the same spread scores through an explicit block mask and through the
+  training forward.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dual_view_block_amd as dvb
+import oracle
+from synth import WORKLOADS, Workload, attention_inputs, random_trees, train_attn_inputs
+from tests._parity import assert_attn_close, assert_lse_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+MODES = {"diff": oracle.MASK_DIFF_BIDIR, "verify": oracle.MASK_VERIFY_CAUSAL}
+
+
+def _check(x, mode, what, scale=None):
+    fn = dvb.orthrus_block_attn_diff if mode == "diff" else dvb.orthrus_block_attn_verify
+    kw = {"softmax_scale": scale} if scale else {}
+    out, lse = fn(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"], x["cache_len"], **kw)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.block_attention(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"],
+                                          x["cache_len"], MODES[mode], scale=scale)
+    e = assert_attn_close(out, ref, what)
+    assert_lse_close(lse, ref_lse, what)
+    print(f"{what}: max_abs={e[0]:.2e} rel_l2={e[1]:.2e}", flush=True)
+
+
+def _plant(x, positions, gain=2.0):
+    """Cache row `pos` of every (b, g) := gain * q row (head g*G + pos % G,
+    block row pos % K): a key whose score for that query row is far above
+    every ordinary score."""
+    q, kc = x["q"], x["k_cache"]
+    B, Hq, K, D = q.shape
+    Hkv = kc.shape[1]
+    G = Hq // Hkv
+    for pos in positions:
+        for g in range(Hkv):
+            kc[:, g, pos] = (gain * q[:, g * G + pos % G, pos % K].float()).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_spread_scores_32k(mode):
+    """L=32768, K=32, softmax scale 1.0."""
+    _check(attention_inputs(WORKLOADS["qwen3_8b_32k"], device=DEV), mode, f"spread32k/{mode}", scale=1.0)
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_planted_late_keys_block_and_sink_32k(mode):
+    """L=32768, K=32, default scale: planted keys near the end of chunks 3,
+    17 and 31 of the 32-way split, mid-way through chunk 9, at position 0,
+    and a block key equal to twice a query row."""
+    x = attention_inputs(WORKLOADS["qwen3_8b_32k"], device=DEV)
+    _plant(x, [0, 3 * 1024 + 1000, 9 * 1024 + 500, 17 * 1024 + 1020, 31 * 1024 + 1023])
+    x["k_blk"][:, :, 20] = (2.0 * x["q"][:, 1, 3].float()).to(torch.bfloat16).unsqueeze(1)
+    _check(x, mode, f"planted32k/{mode}")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_spread_scores_ragged_batch(mode):
+    """The ragged batch of 16 (L_b ~ U{1024..16384}) at softmax scale 1.0."""
+    _check(attention_inputs(WORKLOADS["ragged_b16"], device=DEV), mode, f"spread-ragged/{mode}", scale=1.0)
+
+
+def test_spread_scores_explicit_masks():
+    """Tree (ancestor) block masks at softmax scale 1.0, L 4000 / 1500 / 0."""
+    K = 32
+    w = Workload("tree-spread", 1, 3, 32, 8, 128, 4000, K, 100, 3.0, 71, max_len=4000)
+    x = attention_inputs(w, device=DEV)
+    x["cache_len"] = torch.tensor([4000, 1500, 0], dtype=torch.int32, device=DEV)
+    masks = oracle.ancestor_masks(random_trees(3, K, seed=71, unused_frac=0.1))
+    bits = torch.from_numpy(oracle.masks_to_bits(masks).view(np.int64)).to(DEV)
+    out, lse = dvb.orthrus_block_attn_masked(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"],
+                                             x["cache_len"], bits, softmax_scale=1.0)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.block_attention(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"],
+                                          x["cache_len"], oracle.MASK_EXPLICIT, scale=1.0, block_masks=masks)
+    e = assert_attn_close(out, ref, "explicit-spread")
+    assert_lse_close(lse, ref_lse, "explicit-spread")
+    print(f"explicit-spread: max_abs={e[0]:.2e} rel_l2={e[1]:.2e}", flush=True)
+
+
+def test_spread_scores_training_forward():
+    """Training dual-pass forward (L 512, 16 blocks of 32, 8 / 2 heads) at
+    softmax scale 1.0, every head."""
+    x = train_attn_inputs(8, 2, 512, 16, 32, 128, seed=91, device=DEV)
+    out_ar, lse_ar, out_d, lse_d = dvb.orthrus_train_attn_fwd(x["q_ar"], x["k_ar"], x["v_ar"], x["q_diff"],
+                                                              x["k_diff"], x["v_diff"], x["anchors"], 32,
+                                                              softmax_scale=1.0)
+    torch.cuda.synchronize()
+    r_ar, rl_ar, r_d, rl_d = oracle.dual_pass_forward(x["q_ar"].cpu(), x["k_ar"].cpu(), x["v_ar"].cpu(),
+                                                      x["q_diff"].cpu(), x["k_diff"].cpu(), x["v_diff"].cpu(),
+                                                      x["anchors"].cpu(), 32, scale=1.0)
+    e1 = assert_attn_close(out_ar, r_ar, "train-spread/ar")
+    e2 = assert_attn_close(out_d, r_d, "train-spread/diff")
+    for got, ref, nm in ((lse_ar, rl_ar, "ar"), (lse_d, rl_d, "diff")):
+        err = float(np.abs(got.cpu().double().numpy() - ref).max())
+        assert err <= 1e-3, f"train-spread/{nm} lse err {err:.3e}"
+    print(f"train-spread: ar {e1}, diff {e2}", flush=True)

@@ -209,3 +209,24 @@ def test_sample_consensus_composes_the_steps():
                 assert corr[b] == _brute_pick(wts.tolist(), int(uniform_to_grid_int(u[b, 6])))
                 assert wts[corr[b]] > 0
         assert oracle.tokens_committed(acc, 6).min() >= 1
+
+
+@pytest.mark.parametrize("bad", [-1, -7, 37, 1 << 30])
+def test_out_of_vocabulary_candidate_is_a_zero_probability_token(bad):
+    """R28: a candidate outside [0, V) behaves exactly like an extra vocabulary
+    entry V that the target gives probability 0 (and the draft 0 too, so no
+    residual weight lands on it): the same accepted length and correction."""
+    w = Workload("oov", 1, 4, 1, 1, 1, 1, 6, 37, 1.5, 61)
+    p, q, cand, u = sample_inputs(w, draft_noise=0.3)
+    B, K, V = p.shape
+    for i in (0, 2, K - 1):
+        c = cand.clone()
+        c[:, i] = bad
+        acc, corr = oracle.sample_consensus(p, q, c, u)
+        pe = torch.cat([p, torch.zeros(B, K, 1)], dim=-1)
+        qe = torch.cat([q, torch.zeros(B, K, 1)], dim=-1)
+        ce = cand.clone()
+        ce[:, i] = V
+        racc, rcorr = oracle.sample_consensus(pe, qe, ce, u)
+        assert np.array_equal(acc, racc) and np.array_equal(corr, rcorr), (i, acc, racc, corr, rcorr)
+        assert (acc <= i).all()
