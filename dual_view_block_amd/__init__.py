@@ -31,7 +31,7 @@ __all__ = [
     "PreparedCommit", "orthrus_kl_workspace_size", "orthrus_forward_kl", "PreparedForwardKL",
     "TrainAttnDesc", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd", "orthrus_block_attn_masked",
     "orthrus_topk_logprobs", "orthrus_tree_build", "orthrus_tree_masks", "orthrus_consensus_tree_greedy",
-    "orthrus_cache_commit_path",
+    "orthrus_cache_commit_path", "orthrus_block_attn_noalloc",
 ]
 
 
@@ -126,6 +126,23 @@ def orthrus_block_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len, mode: int, 
         k_cache.data_ptr(), v_cache.data_ptr(), cache_len.data_ptr(), out.data_ptr(),
         lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel(), _stream_ptr(stream))
     _lib.check("orthrus_block_attn", st)
+    return out, lse
+
+
+def orthrus_block_attn_noalloc(q, k_blk, v_blk, k_cache, v_cache, cache_len, mode: int, out, lse=None,
+                               softmax_scale: float = 0.0, stream=None):
+    """orthrus_block_attn on the library's own device scratch: the C call
+    allocates nothing (the caller passes `out`, and `lse` or None)."""
+    _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len)
+    desc = attn_desc(q, k_cache, softmax_scale)
+    _need(out, "out", torch.bfloat16, tuple(q.shape), q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, tuple(q.shape[:3]), q.device)
+    st = _lib.load().orthrus_block_attn_noalloc(
+        ctypes.byref(desc), int(mode), q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), cache_len.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else None,
+        _stream_ptr(stream))
+    _lib.check("orthrus_block_attn_noalloc", st)
     return out, lse
 
 

@@ -6,9 +6,16 @@
 
 #include <math.h>
 #include <atomic>
+#include <mutex>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+
+// Scratch of orthrus_block_attn_noalloc: the workspace of every such call on a
+// device (each device holds its own copy from library load to process end).
+// Host code never passes this name to a kernel -- on the host it is only a
+// stand-in for the symbol -- but the device address looked up below.
+static __device__ __align__(256) uint8_t scratch[ORTHRUS_NOALLOC_SCRATCH_BYTES];
 
 namespace orthrus {
 namespace {
@@ -257,6 +264,36 @@ orthrus_status run_train_part(const orthrus_train_attn_desc* d, int batch, int b
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 
+// Host-side pointer checks of a block-attention call (every one that
+// run_attn makes before its first HIP call, for the entry points that must
+// finish them before looking anything up on the device).
+orthrus_status check_attn_ptrs(const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
+                               const uint16_t* k_cache, const uint16_t* v_cache, const int32_t* cache_len,
+                               const uint16_t* out, const float* lse) {
+  if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !cache_len || !out) return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(cache_len) || !aligned16(out) || (lse && !aligned4(lse)))
+    return ORTHRUS_ERR_MISALIGNED;
+  return ORTHRUS_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; NULL if the lookup failed.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
 // true if the byte ranges [p, p+n) and [q, q+m) overlap
 bool overlaps(const void* p, size_t n, const void* q, size_t m) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
@@ -326,6 +363,22 @@ orthrus_status orthrus_block_attn_verify(const orthrus_attn_desc* d, const uint1
                                          void* workspace, size_t workspace_bytes, void* stream) {
   return run_attn(d, ORTHRUS_MASK_VERIFY_CAUSAL, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse,
                   workspace, workspace_bytes, stream, 3);
+}
+
+orthrus_status orthrus_block_attn_noalloc(const orthrus_attn_desc* d, orthrus_mask_mode mode, const uint16_t* q,
+                                          const uint16_t* k_blk, const uint16_t* v_blk, const uint16_t* k_cache,
+                                          const uint16_t* v_cache, const int32_t* cache_len, uint16_t* out,
+                                          float* lse, void* stream) {
+  const orthrus_status st = check_desc(d);
+  if (st != ORTHRUS_OK) return st;
+  if (mode != ORTHRUS_MASK_DIFF_BIDIR && mode != ORTHRUS_MASK_VERIFY_CAUSAL) return ORTHRUS_ERR_BAD_SHAPE;
+  if (make_plan(d).ws_bytes > ORTHRUS_NOALLOC_SCRATCH_BYTES) return ORTHRUS_ERR_UNSUPPORTED;
+  const orthrus_status pst = check_attn_ptrs(q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse);
+  if (pst != ORTHRUS_OK) return pst;
+  void* ws = scratch_address();
+  if (ws == nullptr) return ORTHRUS_ERR_HIP;
+  return run_attn(d, (int)mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, ws,
+                  ORTHRUS_NOALLOC_SCRATCH_BYTES, stream, 3);
 }
 
 size_t orthrus_consensus_workspace_size(int32_t batch, int32_t block_k, int32_t vocab) {

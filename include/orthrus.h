@@ -141,6 +141,29 @@ orthrus_status orthrus_block_attn_masked(const orthrus_attn_desc* d, const uint1
                                          uint16_t* out, float* lse, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/* Bytes of the device scratch behind orthrus_block_attn_noalloc (16 MiB per
+ * device, held from library load until the process ends). */
+#define ORTHRUS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* orthrus_block_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the call allocates nothing and uses a
+ * scratch array the library keeps in device memory, one per device, of
+ * ORTHRUS_NOALLOC_SCRATCH_BYTES.  The caller still passes every input and
+ * output.  mode is ORTHRUS_MASK_DIFF_BIDIR or ORTHRUS_MASK_VERIFY_CAUSAL.
+ * Results are those of orthrus_block_attn with the same arguments, bit for
+ * bit.  A descriptor whose orthrus_attn_workspace_size exceeds the scratch
+ * returns ORTHRUS_ERR_UNSUPPORTED (nothing enqueued); other errors as
+ * orthrus_block_attn.  Every call on one device shares that device's scratch,
+ * which keeps the last call's contents: calls that overlap in time on one
+ * device (several streams, several host threads) race and give wrong
+ * results; calls in one stream's order are safe. */
+orthrus_status orthrus_block_attn_noalloc(const orthrus_attn_desc* d, orthrus_mask_mode mode,
+                                          const uint16_t* q, const uint16_t* k_blk,
+                                          const uint16_t* v_blk, const uint16_t* k_cache,
+                                          const uint16_t* v_cache, const int32_t* cache_len,
+                                          uint16_t* out, float* lse, void* stream);
+
 /* The two halves of orthrus_block_attn, for callers that schedule or time
  * them separately (or, later, combine partials from several cache shards).
  * orthrus_block_attn_partial streams the cache and the block and leaves one

@@ -229,3 +229,26 @@ def test_product_path_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in src.lower(), f
+
+
+def test_noalloc_entry_point_rejects_before_any_hip_call():
+    """orthrus_block_attn_noalloc: a descriptor whose workspace exceeds the
+    16 MiB scratch is refused with ORTHRUS_ERR_UNSUPPORTED, and bad pointers,
+    alignment and modes are refused as in orthrus_block_attn -- all on the host."""
+    lib = _lib.load()
+
+    def call(desc, mode=0, **ptrs):
+        p = dict(q=4096, kb=4096, vb=4096, kc=4096, vc=4096, lens=4096, out=4096, lse=4096)
+        p.update(ptrs)
+        return lib.orthrus_block_attn_noalloc(ctypes.byref(desc), mode, p["q"], p["kb"], p["vb"], p["kc"],
+                                              p["vc"], p["lens"], p["out"], p["lse"], None)
+
+    big = _desc(batch=256)  # 2048 groups of 128 rows: ~69 MB of split partials
+    assert lib.orthrus_attn_workspace_size(ctypes.byref(big)) > _lib.ORTHRUS_NOALLOC_SCRATCH_BYTES
+    assert call(big) == _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_attn_workspace_size(ctypes.byref(_desc())) <= _lib.ORTHRUS_NOALLOC_SCRATCH_BYTES
+    assert call(_desc(), mode=_lib.ORTHRUS_MASK_EXPLICIT) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert call(_desc(), q=None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert call(_desc(), out=None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert call(_desc(), kc=4104) == _lib.ORTHRUS_ERR_MISALIGNED
+    assert call(_desc(head_dim=96)) == _lib.ORTHRUS_ERR_UNSUPPORTED
