@@ -11,10 +11,11 @@
 // waves (512 threads, two waves per SIMD) per CU.  A work-group owns one
 // contiguous chunk of the (b, g) cache rows and up to 128 query rows (4
 // blocks of 32); split 0 also takes the K block keys as one extra masked
-// tile.  Work-groups are numbered so that the (b, g) groups interleave and
-// the block-carrying splits are dispatched first: the dispatcher starts the
-// work-groups over a couple of microseconds, and the heaviest ones should
-// not start last.
+// tile, before its cache tiles, so that the block is computed while the first
+// cache tile is on its way from HBM.  Work-groups are numbered so that the
+// (b, g) groups interleave and the block-carrying splits are dispatched
+// first: the dispatcher starts the work-groups over a couple of
+// microseconds, and the heaviest ones should not start last.
 //  * Streaming: the chunk is read in tiles of 64 keys (16 KiB of K and 16 KiB
 //    of V at D = 128).  Every thread issues coalesced 16-byte nontemporal
 //    loads of the next tile into registers (32 KiB in flight per CU: more
@@ -65,7 +66,7 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 // Cache range of one split of sequence b: [kstart, kend).
 struct SplitRange {
-  int kstart, kend, ncache, has_block, ntiles;  // block tiles: ncache .. ntiles-1 when has_block
+  int kstart, kend, ncache, nblk, ntiles;  // tiles 0 .. nblk-1: the block keys; then ncache cache tiles
 };
 
 __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int split) {
@@ -80,8 +81,10 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int 
   r.kstart = split * chunk;
   r.kend = min(r.kstart + chunk, L);
   r.ncache = r.kstart < r.kend ? (r.kend - r.kstart + kTileKeys - 1) / kTileKeys : 0;
-  r.has_block = split == 0 ? 1 : 0;
-  r.ntiles = r.ncache + (r.has_block ? (a.block_k + kTileKeys - 1) / kTileKeys : 0);
+  // split 0 streams the block keys first: their tile is computed while the
+  // first cache tile is still on its way from HBM
+  r.nblk = split == 0 ? (a.block_k + kTileKeys - 1) / kTileKeys : 0;
+  r.ntiles = r.nblk + r.ncache;
   return r;
 }
 
@@ -272,17 +275,18 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   const uint8_t* vblk = reinterpret_cast<const uint8_t*>(a.v_blk + blk_off);
   typedef u32x4 Stage[2 * CPT];
   auto load_tile = [&](int t, Stage& r) __attribute__((always_inline)) {
-    const bool whole = t < nfull;
     const bool real = t < sr.ntiles;
-    const bool blk = sr.has_block && t >= sr.ncache;
-    const int bt = t - sr.ncache;
+    const bool blk = real && t < sr.nblk;
+    const int ct = t - sr.nblk;  // cache tile index
+    const bool cache = real && !blk;
+    const bool whole = cache && ct < nfull;
     const int last = whole ? kTileKeys - 1
-                           : (!real ? 0 : (blk ? min(kTileKeys, K - bt * kTileKeys)
-                                               : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys))) - 1);
-    const size_t toff = (size_t)t * TILEB;
-    const size_t boff = blk && real ? (size_t)bt * TILEB : 0;
-    const uint8_t* kp = (whole || (real && !blk)) ? kc0 + toff : kblk + boff;
-    const uint8_t* vp = (whole || (real && !blk)) ? vc0 + toff : (real ? vblk + boff : kblk);
+                           : (!real ? 0 : (blk ? min(kTileKeys, K - t * kTileKeys)
+                                               : min(kTileKeys, sr.kend - (sr.kstart + ct * kTileKeys))) - 1);
+    const size_t toff = (size_t)ct * TILEB;
+    const size_t boff = blk ? (size_t)t * TILEB : 0;
+    const uint8_t* kp = cache ? kc0 + toff : kblk + boff;
+    const uint8_t* vp = cache ? vc0 + toff : (real ? vblk + boff : kblk);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const uint32_t off = (uint32_t)(min(crow[c], last) * ROWB) + cchunk[c];
@@ -299,8 +303,8 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     }
   };
   auto tile_valid = [&](int t) __attribute__((always_inline)) {
-    return (sr.has_block && t >= sr.ncache) ? min(kTileKeys, K - (t - sr.ncache) * kTileKeys)
-                                            : min(kTileKeys, sr.kend - (sr.kstart + t * kTileKeys));
+    return t < sr.nblk ? min(kTileKeys, K - t * kTileKeys)
+                       : min(kTileKeys, sr.kend - (sr.kstart + (t - sr.nblk) * kTileKeys));
   };
 
   // ---- running softmax state of this lane's row over this wave's key half
@@ -423,9 +427,9 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     for (int ds = 0; ds < NDS; ++ds) s = mfma32(kf[ds], qf[ds], s);
     bf16x8 vf[2][NMB];
     load_v(st, vf);
-    if (t >= nfull) {
-      const bool blk = sr.has_block && t >= sr.ncache;
-      mask_scores(s, nval, blk, (t - sr.ncache) * kTileKeys);
+    if (t < sr.nblk || t - sr.nblk >= nfull) {
+      const bool blk = t < sr.nblk;
+      mask_scores(s, nval, blk, t * kTileKeys);
     }
     update_ref(s);
     float lsum = 0.0f;
@@ -454,10 +458,12 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   // and loads tile t+2 into the registers; the barrier then publishes tile
   // t+1.  Computing first keeps the stage writes off the path of this wave's
   // LDS reads.
-  Stage stg;
-  load_tile(0, stg);
-  store_tile(0, stg);
+  // The first two tiles are requested together: the first one's latency is
+  // the longest of the launch, and the second one's hides under it.
+  Stage stg, stg0;
+  load_tile(0, stg0);
   load_tile(1, stg);
+  store_tile(0, stg0);
   __syncthreads();
   for (int t = 0; t < sr.ntiles; ++t) {
     compute(t & 1, t);
