@@ -66,7 +66,8 @@ AttnPlan make_plan(const orthrus_attn_desc* d) {
   const size_t slots = (size_t)groups * p.splits * p.rows_per_wg;
   p.ml_bytes = round_up(slots * 2 * sizeof(float), kAlign);
   p.acc_bytes = round_up(slots * d->head_dim * sizeof(uint16_t), kAlign);
-  p.ws_bytes = p.ml_bytes + p.acc_bytes;
+  p.tab_bytes = round_up((size_t)d->batch * 2 * sizeof(int32_t), kAlign);
+  p.ws_bytes = p.ml_bytes + p.acc_bytes + p.tab_bytes;
   return p;
 }
 
@@ -127,6 +128,7 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   a.ws_ml = reinterpret_cast<float*>(ws);
   a.ws_acc = reinterpret_cast<uint16_t*>(ws + plan.ml_bytes);
+  a.ws_tab = reinterpret_cast<int2*>(ws + plan.ml_bytes + plan.acc_bytes);
   a.batch = d->batch;
   a.n_q_heads = d->n_q_heads;
   a.n_kv_heads = d->n_kv_heads;
@@ -140,13 +142,17 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.splits = attn_launch_splits(plan, d->batch, d->n_kv_heads, d->max_len, cus);
   const int cap = env_int("ORTHRUS_MAX_SPLITS", a.splits);  // tuning: may only lower the split count
   if (cap < a.splits) a.splits = cap;
+  // several sequences: share the launch's work-groups out by cache length
+  a.ragged = (d->batch > 1 && d->batch <= kRaggedMaxSeqs && a.splits > 1 &&
+              env_int("ORTHRUS_EVEN_SPLITS", 0) == 0) ? 1 : 0;
+  a.nwg = d->batch * d->n_kv_heads * plan.row_groups * a.splits;
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   if ((phases & 1) && getenv("ORTHRUS_DEBUG") != nullptr)
     fprintf(stderr, "[orthrus] attn mode=%d B=%d Hq=%d Hkv=%d D=%d K=%d max_len=%d rows=%d qblocks=%d "
-            "row_groups=%d splits=%d ws=%zu\n", mode, d->batch, d->n_q_heads, d->n_kv_heads,
+            "row_groups=%d splits=%d ragged=%d ws=%zu\n", mode, d->batch, d->n_q_heads, d->n_kv_heads,
             d->head_dim, d->block_k, d->max_len, plan.rows, plan.qblocks, plan.row_groups,
-            a.splits, plan.ws_bytes);
+            a.splits, a.ragged, plan.ws_bytes);
   // tuning switch: merge the splits inside the streaming kernel (one launch)
   const hipError_t e = launch_block_attention(a, plan, phases, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;

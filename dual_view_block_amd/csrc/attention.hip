@@ -69,11 +69,14 @@ struct SplitRange {
   int kstart, kend, ncache, nblk, ntiles;  // tiles 0 .. nblk-1: the block keys; then ncache cache tiles
 };
 
-__device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int split) {
+__device__ __forceinline__ int seq_len(const AttnArgs& a, int b) {
+  const int L = a.len_step > 0 ? b * a.len_step : a.cache_len[b];
+  return L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+}
+
+__device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int split, int S) {
   SplitRange r;
-  int L = a.len_step > 0 ? b * a.len_step : a.cache_len[b];
-  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
-  const int S = a.splits;
+  const int L = seq_len(a, b);
   // as even as the key count allows: a length that is not a multiple of S
   // tiles leaves every split a short last tile rather than some splits a whole
   // extra one (splits need not start on a tile boundary)
@@ -86,6 +89,104 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int 
   r.nblk = split == 0 ? (a.block_k + kTileKeys - 1) / kTileKeys : 0;
   r.ntiles = r.nblk + r.ncache;
   return r;
+}
+
+// ---- length-aware placement for batches of several sequences
+//
+// With several sequences the launch's N work-groups are shared out by cache
+// length rather than evenly: sequence b (nt_b = max(1, ceil(L_b / 64)) cache
+// tiles) gets s_b = ceil(nt_b / c) splits for each of its H = Hkv * row_groups
+// groups, where c is the smallest tile count per split with
+// H * sum_b s_b <= N.  Every work-group then streams at most c tiles, so a
+// long sequence no longer sets the time of the whole call.  The lengths are
+// read on the device by every streaming work-group (no host sync); each
+// sequence's first work-group leaves (first work-group, splits) in the
+// workspace for the merge.
+// Sequence b's work-groups are N_b = H * sum_{b' < b} s_b' .. + H * s_b - 1,
+// split-major (work-group N_b + split * H + h); its partials use the slot of
+// the work-group's index.  Work-groups past the last sequence have no work.
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int seq_tiles(const AttnArgs& a, int b) {
+  return max(1, (seq_len(a, b) + kTileKeys - 1) / kTileKeys);
+}
+
+// Up to kRaggedMaxSeqs sequences: lane l of a wave holds the tile counts of
+// sequences l, l + 64, ... in registers, read once.
+constexpr int kRaggedSlots = kRaggedMaxSeqs / 64;
+
+struct RaggedTiles {
+  int nt[kRaggedSlots];  // tile count of sequence lane + 64*k (0 past the batch)
+};
+
+__device__ __forceinline__ RaggedTiles ragged_tiles(const AttnArgs& a) {
+  const int lane = threadIdx.x & 63;
+  RaggedTiles r;
+#pragma unroll
+  for (int k = 0; k < kRaggedSlots; ++k) r.nt[k] = lane + 64 * k < a.batch ? seq_tiles(a, lane + 64 * k) : 0;
+  return r;
+}
+
+// The smallest tiles-per-split bound c with H * sum_b ceil(nt_b / c) <= N
+// (called by a whole wave; every lane gets c).  c lies between H*T/N and
+// H*T/(N - H*B), T = sum_b nt_b (N > H*B whenever the plan is used).
+__device__ int ragged_chunk_tiles(const AttnArgs& a, const RaggedTiles& rt, int H, int N) {
+  int t = 0;
+#pragma unroll
+  for (int k = 0; k < kRaggedSlots; ++k) t += rt.nt[k];
+  const long long T = wave_sum(t);
+  const long long HT = (long long)H * T;
+  int lo = (int)max(1LL, (HT + N - 1) / N);
+  const long long room = (long long)N - (long long)H * a.batch;
+  int hi = (int)max((long long)lo, room > 0 ? (HT + room - 1) / room : HT);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    int tot = 0;
+#pragma unroll
+    for (int k = 0; k < kRaggedSlots; ++k) tot += (rt.nt[k] + mid - 1) / mid;
+    if ((long long)wave_sum(tot) * H <= N) hi = mid; else lo = mid + 1;
+  }
+  return lo;
+}
+
+struct RaggedSeq {
+  int b;      // sequence (-1: past the last one)
+  int first;  // its first work-group
+  int nsplit; // its splits per group
+};
+
+// The sequence whose work-groups contain work-group `lin` (a whole wave calls it).
+__device__ RaggedSeq ragged_seq(const AttnArgs& a, const RaggedTiles& rt, int H, int c, int lin) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+#pragma unroll
+  for (int k = 0; k < kRaggedSlots; ++k) {
+    const int bb = 64 * k + lane;
+    const int sb = bb < a.batch ? (rt.nt[k] + c - 1) / c : 0;
+    int incl = sb * H;  // inclusive scan of the work-group counts
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int excl = incl - sb * H;
+    const unsigned long long m = __ballot(bb < a.batch && lin >= base + excl && lin < base + incl);
+    if (m) {
+      const int src = __builtin_ctzll(m);
+      return {64 * k + src, base + __shfl(excl, src), __shfl(sb, src)};
+    }
+    base += __shfl(incl, 63);
+  }
+  return {-1, base, 0};
 }
 
 // Merge of the S split partials of one output row: with per-split reference
@@ -199,6 +300,71 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
   }
 }
 
+// Merge of one output row (two at D = 64, one per half-wave) from S partials
+// at slots slot0 + s * stride, for any S: batches of 16 splits, each batch one
+// memory round trip, combined online (the running maximum, sum and value sum
+// are rescaled when a batch raises the maximum).  Lane j < 16 of a row holds
+// the statistics of split s0 + j of batch s0.  Fixed summation order.
+template <int D>
+__device__ __forceinline__ void merge_wave_dyn(const AttnArgs& a, const AttnPlan& p, int grp, size_t slot0,
+                                               int stride, int S, int row, int row_end) {
+  constexpr int LPR = D / 2;
+  constexpr int NB = 16;
+  const int lane = threadIdx.x & 63;
+  const int j = lane & (LPR - 1);
+  const int hw = LPR == 32 ? (lane >> 5) : 0;
+  const int myrow = row + hw;
+  const int rrow = min(myrow, p.rows_per_wg - 1);
+  float M = kNegInf, L = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    uint32_t v[NB];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const size_t idx = (slot0 + (size_t)min(s0 + t, S - 1) * stride) * p.rows_per_wg + rrow;
+      v[t] = *reinterpret_cast<const uint32_t*>(a.ws_acc + idx * D + 2 * j);
+    }
+    const bool real = j < NB && s0 + j < S;
+    const size_t sidx = (slot0 + (size_t)min(s0 + min(j, NB - 1), S - 1) * stride) * p.rows_per_wg + rrow;
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + sidx * 2);
+    const float m = real ? ml.x : kNegInf;
+    const float l = real ? ml.y : 0.0f;
+    const float Mn = fmaxf(M, row_reduce<LPR>(m, [](float x, float y) { return fmaxf(x, y); }));
+    const float sc = M == kNegInf ? 0.0f : fast_exp2(M - Mn);
+    L *= sc;
+    acc0 *= sc;
+    acc1 *= sc;
+    const float wt = m == kNegInf ? 0.0f : fast_exp2(m - Mn) * l;
+    L += row_reduce<LPR>(wt, [](float x, float y) { return x + y; });
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      float ws;
+      if constexpr (LPR == 64) {
+        ws = readlane_f(wt, t);
+      } else {
+        const float w0 = readlane_f(wt, t);
+        const float w1 = readlane_f(wt, t + 32);
+        ws = hw ? w1 : w0;
+      }
+      ws = s0 + t < S ? ws : 0.0f;
+      acc0 = fmaf(ws, __uint_as_float(v[t] << 16), acc0);
+      acc1 = fmaf(ws, __uint_as_float(v[t] & 0xFFFF0000u), acc1);
+    }
+    M = Mn;
+  }
+  if (myrow < row_end) {
+    const int rg = grp % p.row_groups;
+    const int r = rg * p.rows_per_wg + myrow;
+    if (r < p.rows) {
+      const int bg = grp / p.row_groups;
+      const int b = bg / a.n_kv_heads, h = (bg % a.n_kv_heads) * a.group + r / a.block_k, i = r % a.block_k;
+      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+      const uint32_t o = (uint32_t)to_bf16_bits(acc0 * inv) | ((uint32_t)to_bf16_bits(acc1 * inv) << 16);
+      *reinterpret_cast<uint32_t*>(a.out + b * a.o_bs + h * a.o_hs + (long long)i * D + 2 * j) = o;
+      if (a.lse != nullptr && j == 0) a.lse[b * a.l_bs + h * a.l_hs + i] = (M + log2f(L)) * kLn2;
+    }
+  }
+}
+
 // The streaming kernel (see the top of the file).  Per wave and tile at D 128:
 // 8 S^T MFMAs, 16 exponentials per lane, 8 O^T MFMAs.
 constexpr int kStreamThreads = kAttnThreads;
@@ -223,11 +389,32 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   __shared__ __attribute__((aligned(16))) uint8_t smem[REGION0 + 128 * OPITCH];
   __shared__ float2 xstat[8][32];
 
-  // dispatch order: (b, g) groups interleaved, split 0 (the block keys) first
+  // dispatch order: (b, g) groups interleaved, split 0 (the block keys) first;
+  // with several sequences, work-groups go to sequences by cache length
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int bg = lin % (int)gridDim.z;
-  const int rg = (lin / (int)gridDim.z) % (int)gridDim.y;
-  const int split = lin / ((int)gridDim.z * (int)gridDim.y);
+  int bg, rg, split, nsplit;
+  size_t slot;
+  if (a.ragged) {
+    const int H = a.n_kv_heads * plan.row_groups;
+    const RaggedTiles rt = ragged_tiles(a);
+    const RaggedSeq sq = ragged_seq(a, rt, H, ragged_chunk_tiles(a, rt, H, a.nwg), lin);
+    if (sq.b < 0) return;  // no work left for this work-group (uniform: every wave finds the same)
+    const int local = lin - sq.first;
+    // the sequence's first work-group records where its splits are, for the merge
+    if (local == 0 && threadIdx.x == 0) a.ws_tab[sq.b] = make_int2(sq.first, sq.nsplit);
+    const int h = local % H;
+    split = local / H;
+    rg = h % plan.row_groups;
+    bg = sq.b * a.n_kv_heads + h / plan.row_groups;
+    nsplit = sq.nsplit;
+    slot = (size_t)lin;
+  } else {
+    bg = lin % (int)gridDim.z;
+    rg = (lin / (int)gridDim.z) % (int)gridDim.y;
+    split = lin / ((int)gridDim.z * (int)gridDim.y);
+    nsplit = a.splits;
+    slot = (size_t)(bg * plan.row_groups + rg) * a.splits + split;
+  }
   const int grp = bg * plan.row_groups + rg;
   const int b = bg / a.n_kv_heads;
   const int tid = threadIdx.x;
@@ -239,7 +426,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   const bool active = qb < NQB;
   const int R = plan.rows;
   const int K = a.block_k;
-  const SplitRange sr = split_range(a, b, split);
+  const SplitRange sr = split_range(a, b, split, nsplit);
   const int g = bg % a.n_kv_heads;
   const long long q_grp = b * a.q_bs + (long long)g * a.group * a.q_hs;
   const long long o_grp = b * a.o_bs + (long long)g * a.group * a.o_hs;
@@ -519,8 +706,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   }
   __syncthreads();
   const int nrows = plan.rows_per_wg;
-  const bool one_split = a.splits == 1 && direct;
-  const size_t slot = (size_t)grp * a.splits + split;
+  const bool one_split = !a.ragged && a.splits == 1 && direct;
   for (int n = tid; n < nrows * DCH; n += kStreamThreads) {
     const int r = n / DCH, ch = n % DCH;
     const u32x4 v = *reinterpret_cast<const u32x4*>(smem + REGION0 + r * OPITCH + ch * 16);
@@ -564,6 +750,21 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a, A
   merge_wave<D, SMAX>(a, plan, grp, first % plan.rows_per_wg, plan.rows_per_wg);
 }
 
+// Merge after a length-aware streaming launch: one wave per row (two at
+// D 64); the group's splits and their slots come from the table the
+// streaming launch left in the workspace.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_ragged_kernel(AttnArgs a, AttnPlan plan, int total_rows) {
+  constexpr int RPW = 128 / D;
+  const int gw = (int)blockIdx.x * (kMergeThreads / 64) + (int)(threadIdx.x >> 6);
+  const int first = gw * RPW;
+  if (first >= total_rows) return;
+  const int grp = first / plan.rows_per_wg;
+  const int H = a.n_kv_heads * plan.row_groups;
+  const int2 sq = a.ws_tab[grp / H];  // (first work-group, splits) of the group's sequence
+  merge_wave_dyn<D>(a, plan, grp, (size_t)sq.x + grp % H, H, sq.y, first % plan.rows_per_wg, plan.rows_per_wg);
+}
+
 template <int D, int NQB>
 hipError_t launch_stream(const AttnArgs& a, const AttnPlan& p, int direct, hipStream_t stream) {
   dim3 grid(a.splits, p.row_groups, a.batch * a.n_kv_heads);
@@ -585,6 +786,13 @@ hipError_t launch_merge_s(const AttnArgs& a, const AttnPlan& p, hipStream_t stre
 
 template <int D>
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
+  if (a.ragged) {
+    constexpr int rows_per_block = (kMergeThreads / 64) * (128 / D);
+    const int total = a.batch * a.n_kv_heads * p.row_groups * p.rows_per_wg;
+    dim3 grid((total + rows_per_block - 1) / rows_per_block);
+    hipLaunchKernelGGL((attn_merge_ragged_kernel<D>), grid, dim3(kMergeThreads), 0, stream, a, p, total);
+    return hipGetLastError();
+  }
   if (a.splits <= 8) return launch_merge_s<D, 8>(a, p, stream);
   if (a.splits <= 16) return launch_merge_s<D, 16>(a, p, stream);
   if (a.splits <= 32) return launch_merge_s<D, 32>(a, p, stream);
@@ -608,7 +816,7 @@ template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, int phases, hipStream_t stream) {
   if (phases == 1) return launch_stream_any<D>(a, p, 0, stream);
   if (phases == 2) return launch_merge<D>(a, p, stream);
-  if (a.splits == 1) return launch_stream_any<D>(a, p, 1, stream);
+  if (a.splits == 1 && !a.ragged) return launch_stream_any<D>(a, p, 1, stream);
   const hipError_t e = launch_stream_any<D>(a, p, 0, stream);
   if (e != hipSuccess) return e;
   return launch_merge<D>(a, p, stream);

@@ -19,6 +19,8 @@ constexpr int kAttnThreads = 512;
 // fewer splits inside the same workspace.
 constexpr int kPlanCUs = 256;
 constexpr int kMaxSplits = 64;
+// Largest batch whose work-groups are shared out by cache length.
+constexpr int kRaggedMaxSeqs = 256;
 
 struct AttnPlan {
   int rows;          // R = G * K query rows per (sequence, KV head)
@@ -28,6 +30,7 @@ struct AttnPlan {
   int splits;        // most splits per (sequence, KV head, row group) the workspace holds
   size_t ml_bytes;       // fp32 (max, sum) per row and split
   size_t acc_bytes;      // bf16 normalised partial outputs per row and split
+  size_t tab_bytes;      // int2 per sequence: first work-group and splits (length-aware launches)
   size_t ws_bytes;       // total workspace
 };
 
@@ -42,9 +45,12 @@ struct AttnArgs {
   float* lse;
   float* ws_ml;       // fp32 (reference max, sum) per row and split
   uint16_t* ws_acc;   // bf16 normalised partial output per row and split
+  int2* ws_tab;       // per sequence: first work-group and splits (length-aware launches)
   int batch, n_q_heads, n_kv_heads, group, block_k, head_dim, max_len;
   int causal;
   int splits;        // splits of this launch (<= plan.splits)
+  int ragged;        // 1: several sequences, work-groups shared out by cache length
+  int nwg;           // work-groups of the streaming launch (ragged placement)
   float scale_log2;  // softmax scale * log2(e)
   // Element strides.  Block row i of q head h in sequence b is at
   // q + b*q_bs + h*q_hs + i*head_dim (out likewise with o_*, lse with l_*, in

@@ -255,3 +255,19 @@ def test_single_split_direct_output(mode, monkeypatch):
     output itself (no merge launch); it must meet the same oracle bar."""
     monkeypatch.setenv("ORTHRUS_MAX_SPLITS", "1")
     _check(_inputs(WORKLOADS["qwen3_1p7b_layer"]), mode, "one_split")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+@pytest.mark.parametrize("lens", [
+    [16384, 1024, 1024, 1024],          # one long sequence takes most of the work-groups
+    [0, 5000, 64, 16383],               # an empty cache, a one-tile cache, ragged tails
+    [3000, 3000, 3000, 3000, 3000, 3000],
+])
+def test_ragged_batches_shared_by_length(mode, lens):
+    """Several sequences: the launch's work-groups are shared out by cache
+    length on the device (a long sequence gets more splits per KV head)."""
+    B = len(lens)
+    w = Workload("rag", 1, B, 32, 8, 128, max(lens), 32, 10, 1.0, 41 + B, max_len=16384)
+    x = _inputs(w)
+    x["cache_len"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    _check(x, mode, f"ragged{lens}")
