@@ -201,24 +201,20 @@ orthrus_status check_kl_sizes(int32_t rows, int32_t vocab, int dtype) {
   return ORTHRUS_OK;
 }
 
-// work-groups per CU of the persistent partial pass of the forward KL
-constexpr int kKlWgPerCu = 8;
-
 struct KlPlan {
   int esize;
   bool vec;
-  int chunks;
-  size_t part_bytes, lse_bytes, ws_bytes;
+  size_t ws_bytes;
 };
 
 KlPlan make_kl_plan(int32_t rows, int32_t vocab, int dtype) {
+  (void)rows;
   KlPlan p{};
   p.esize = dtype == ORTHRUS_DTYPE_F32 ? 4 : 2;
   p.vec = ((size_t)vocab * p.esize) % 16 == 0;
-  p.chunks = kl_chunks(vocab, p.esize, p.vec);
-  p.part_bytes = round_up((size_t)rows * p.chunks * 8 * sizeof(float), kAlign);
-  p.lse_bytes = round_up((size_t)rows * 2 * sizeof(float), kAlign);
-  p.ws_bytes = p.part_bytes + p.lse_bytes;
+  // the row-wise kernel keeps its statistics in registers; the workspace
+  // argument stays in the interface, one alignment unit of it reserved
+  p.ws_bytes = kAlign;
   return p;
 }
 
@@ -477,11 +473,8 @@ orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, orthrus_dtype dty
   if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
   const int cus = device_cus();
   if (cus < 1) return ORTHRUS_ERR_HIP;
-  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   const hipError_t e = launch_forward_kl(rows, vocab, plan.esize, plan.vec, target_logits, draft_logits, kl, grad,
-                                         grad_scale, reinterpret_cast<float*>(ws),
-                                         reinterpret_cast<float*>(ws + plan.part_bytes), kKlWgPerCu * cus,
-                                         reinterpret_cast<hipStream_t>(stream));
+                                         grad_scale, cus, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 

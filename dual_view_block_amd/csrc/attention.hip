@@ -415,7 +415,6 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     nsplit = a.splits;
     slot = (size_t)(bg * plan.row_groups + rg) * a.splits + split;
   }
-  const int grp = bg * plan.row_groups + rg;
   const int b = bg / a.n_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;

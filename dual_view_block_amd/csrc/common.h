@@ -144,15 +144,11 @@ hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head
                                int32_t* tokens, int32_t* n_tokens, hipStream_t stream);
 
 // ---------------------------------------------------------------- forward KL
-// Vocabulary chunks per row (one work-group each) for a logits element size
-// and load form (16-byte vectors when every row starts 16-byte aligned).
-int kl_chunks(int vocab, int dtype_bytes, bool vec);
-// Partials (a persistent grid of `groups` work-groups), finalize, and (if
-// grad != NULL) the gradient pass, on `stream`.  part: rows * chunks * 8
-// floats; lse: rows * 2 floats.
+// Forward KL (and, if grad != NULL, its gradient) of `rows` logit rows: one
+// row-wise launch on `stream` sized from the device's CU count.  vec: every
+// row starts 16-byte aligned (16-byte loads).
 hipError_t launch_forward_kl(int rows, int vocab, int dtype_bytes, bool vec, const void* target,
-                             const void* draft, float* kl, void* grad, float scale, float* part, float* lse,
-                             int groups, hipStream_t stream);
+                             const void* draft, float* kl, void* grad, float scale, int cus, hipStream_t stream);
 
 // Commit of an accepted tree path (rows path[0..a]); the same two-launch shape.
 hipError_t launch_cache_commit_path(int n_layers, int batch, int n_kv_heads, int head_dim, int block_k,

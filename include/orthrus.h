@@ -294,9 +294,9 @@ size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, orthrus_dtype dtyp
  *   grad  [rows, V] (dtype) (written; may be NULL) grad_scale * (q_v - p_v),
  *                           the derivative of kl[n] * grad_scale with respect to
  *                           draft_logits[n, v]; the AR side is frozen
- *   workspace  device scratch of at least orthrus_kl_workspace_size bytes,
- *              owned by the caller; no initialisation needed; calls sharing it
- *              must not overlap in time.
+ *   workspace  device scratch of at least orthrus_kl_workspace_size bytes
+ *              (one 256-byte unit: the kernel keeps its row statistics in
+ *              registers), owned by the caller; no initialisation needed.
  * Logits must be finite; no temperature is applied (the caller scales the
  * logits for one).  Sums run in fp32 in a fixed order, so results are
  * deterministic.  Rows are contiguous with stride V; rows up to 65535
