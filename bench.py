@@ -80,6 +80,9 @@ def _parse():
     ap.add_argument("--summarize-trace", metavar="RESULTS_DB",
                     help="print per-kernel durations (markdown) from a rocprofv3 --kernel-trace "
                          "results database and exit")
+    ap.add_argument("--trace-phases", default=None,
+                    help="with --summarize-trace: streaming-kernel dispatch ranges to summarise separately "
+                         "(label=a:b,...; bench.py prints them for its own run)")
     ap.add_argument("--make-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
                                                         "COPY_WRITE_CSV"),
                     help="turn four rocprofv3 --pmc counter_collection.csv files into the traffic "
@@ -160,10 +163,12 @@ def load_traffic(path: str):
     return rec.get("bytes_per_launch")
 
 
-def summarize_trace(db_path: str) -> None:
+def summarize_trace(db_path: str, phases: str = None) -> None:
     """Per-kernel duration statistics of a rocprofv3 kernel-trace database
     (every dispatch of the library's kernels it holds), as a markdown table,
-    plus the median idle gap between consecutive dispatches."""
+    plus the median idle gap between consecutive dispatches.  `phases`
+    ("label=a:b,label=a:b", as bench.py prints them) adds the statistics of
+    the streaming kernel's dispatches a..b-1 (in launch order) of each phase."""
     import re
     import sqlite3
 
@@ -181,6 +186,23 @@ def summarize_trace(db_path: str) -> None:
         v = sorted(v)
         print(f"| {nm} | {gx} × {gy} × {gz} | {wg} | {len(v)} | {statistics.mean(v):.2f} | "
               f"{statistics.median(v):.2f} | {v[0]:.2f} | {v[int(0.9 * (len(v) - 1))]:.2f} |")
+    if phases:
+        # the streaming kernel's most frequent (grid, work-group) launch shape
+        key = max((k for k in groups if "attn_stream_kernel" in k[0]), key=lambda k: len(groups[k]))
+        durs = groups[key]  # in launch order (rows are sorted by start)
+        print()
+        print(f"Phases of {key[0]} ({key[1]} × {key[2]} × {key[3]}), dispatch index ranges in launch order:")
+        print()
+        print("| phase | dispatches | mean µs | median µs | min µs |")
+        print("|---|---|---|---|---|")
+        for item in phases.split(","):
+            label, rng = item.split("=")
+            a, b = (int(x) for x in rng.split(":"))
+            v = durs[a:b]
+            if not v:
+                continue
+            sv = sorted(v)
+            print(f"| {label} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | {sv[0]:.2f} |")
     gaps = {}
     for a, b in zip(rows, rows[1:]):
         key = tuple(re.sub(r"[<(].*", "", x[0].replace("(anonymous namespace)::", "")).split("::")[-1]
@@ -755,7 +777,7 @@ def cpu_baseline(w, caches, device, budget_s: float = 10.0):
 def main():
     args = _parse()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.trace_phases)
         return
     if args.make_traffic:
         make_traffic(args.make_traffic, args.traffic, args.copy_mib)
@@ -800,6 +822,14 @@ def main():
     splits = step.splits
     ms, wall_ms = time_steps(step, args.steps, args.warmup, args.graph)
     kern = time_kernels(step)
+    # where this run's streaming-kernel dispatches fall, in launch order, for
+    # reading a kernel trace of the same command (bench.py --summarize-trace)
+    n_l = len(step.calls["diff"]) + len(step.calls["verify"])
+    pre = (1 if args.graph else 0) + args.warmup
+    t0 = (pre + args.steps) * n_l
+    phases = {"timed_steps": (pre * n_l, t0), "back_to_back": (t0, t0 + 3 * n_l)}
+    phase_arg = ",".join(f"{k}={a}:{b}" for k, (a, b) in phases.items())
+    print(f"[bench] streaming-kernel dispatch phases: {phase_arg}", file=sys.stderr, flush=True)
     print(f"[bench] step {ms * 1e3:.1f} us (host wall {wall_ms * 1e3:.1f} us), streaming kernel "
           f"{kern['attn_stream_us']:.2f} us, merge {kern['attn_merge_us']:.2f} us, call "
           f"{kern['attn_call_us']:.2f} us", file=sys.stderr, flush=True)
@@ -894,6 +924,9 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attn_stream_kernel<128,4> (one launch per orthrus_block_attn_* call)",
                      "algorithmic_bytes_per_launch": pbytes,
+                     "duration_us": round(kern["attn_stream_us"], 3),
+                     "duration_from": "HIP events around 3 runs of back-to-back streaming launches, median",
+                     "trace_phases": phase_arg,
                      "call_achieved_gbs": round(attn_bytes(w) / (kern["attn_call_us"] * 1e-6) / 1e9, 1)},
     }
     if cyc is not None:
