@@ -11,7 +11,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liborthrus.so")
+# ORTHRUS_LIBRARY names another build of the same library (for instance the
+# host-sanitised one that dual_view_block_amd.build makes for the CPU tests)
+LIB_PATH = os.environ.get("ORTHRUS_LIBRARY") or os.path.join(HERE, "liborthrus.so")
 
 ORTHRUS_OK = 0
 ORTHRUS_ERR_NULL_PTR = 1

@@ -319,7 +319,7 @@ int32_t orthrus_attn_num_splits(const orthrus_attn_desc* d) {
   return make_plan(d).splits;
 }
 
-orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, orthrus_mask_mode mode, const uint16_t* q,
+orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, int32_t mode, const uint16_t* q,
                                   const uint16_t* k_blk, const uint16_t* v_blk, const uint16_t* k_cache,
                                   const uint16_t* v_cache, const int32_t* cache_len, uint16_t* out,
                                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
@@ -335,7 +335,7 @@ orthrus_status orthrus_block_attn_masked(const orthrus_attn_desc* d, const uint1
                   workspace_bytes, stream, 3, block_mask);
 }
 
-orthrus_status orthrus_block_attn_partial(const orthrus_attn_desc* d, orthrus_mask_mode mode,
+orthrus_status orthrus_block_attn_partial(const orthrus_attn_desc* d, int32_t mode,
                                           const uint16_t* q, const uint16_t* k_blk, const uint16_t* v_blk,
                                           const uint16_t* k_cache, const uint16_t* v_cache,
                                           const int32_t* cache_len, void* workspace, size_t workspace_bytes,
@@ -367,7 +367,7 @@ orthrus_status orthrus_block_attn_verify(const orthrus_attn_desc* d, const uint1
                   workspace, workspace_bytes, stream, 3);
 }
 
-orthrus_status orthrus_block_attn_noalloc(const orthrus_attn_desc* d, orthrus_mask_mode mode, const uint16_t* q,
+orthrus_status orthrus_block_attn_noalloc(const orthrus_attn_desc* d, int32_t mode, const uint16_t* q,
                                           const uint16_t* k_blk, const uint16_t* v_blk, const uint16_t* k_cache,
                                           const uint16_t* v_cache, const int32_t* cache_len, uint16_t* out,
                                           float* lse, void* stream) {
@@ -454,22 +454,22 @@ orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_ca
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 
-size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, orthrus_dtype dtype) {
-  if (check_kl_sizes(rows, vocab, (int)dtype) != ORTHRUS_OK) return 0;
-  return make_kl_plan(rows, vocab, (int)dtype).ws_bytes;
+size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, int32_t dtype) {
+  if (check_kl_sizes(rows, vocab, dtype) != ORTHRUS_OK) return 0;
+  return make_kl_plan(rows, vocab, dtype).ws_bytes;
 }
 
-orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, orthrus_dtype dtype, const void* target_logits,
+orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, int32_t dtype, const void* target_logits,
                                   const void* draft_logits, float* kl, void* grad, float grad_scale,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  const orthrus_status st = check_kl_sizes(rows, vocab, (int)dtype);
+  const orthrus_status st = check_kl_sizes(rows, vocab, dtype);
   if (st != ORTHRUS_OK) return st;
   if (!target_logits || !draft_logits || !kl || !workspace) return ORTHRUS_ERR_NULL_PTR;
   if (!isfinite(grad_scale)) return ORTHRUS_ERR_BAD_SHAPE;
   if (!aligned16(target_logits) || !aligned16(draft_logits) || !aligned4(kl) || (grad && !aligned16(grad)) ||
       !aligned16(workspace))
     return ORTHRUS_ERR_MISALIGNED;
-  const KlPlan plan = make_kl_plan(rows, vocab, (int)dtype);
+  const KlPlan plan = make_kl_plan(rows, vocab, dtype);
   if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
   const int cus = device_cus();
   if (cus < 1) return ORTHRUS_ERR_HIP;
@@ -677,8 +677,8 @@ orthrus_status orthrus_tree_build(int32_t batch, int32_t depth, int32_t m, int32
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 
-const char* orthrus_status_string(orthrus_status s) {
-  switch (s) {
+const char* orthrus_status_string(int32_t status) {
+  switch (status) {
     case ORTHRUS_OK: return "ORTHRUS_OK";
     case ORTHRUS_ERR_NULL_PTR: return "ORTHRUS_ERR_NULL_PTR: a required pointer is NULL";
     case ORTHRUS_ERR_BAD_SHAPE: return "ORTHRUS_ERR_BAD_SHAPE: a size is out of range or inconsistent";

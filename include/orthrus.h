@@ -103,7 +103,7 @@ int32_t orthrus_attn_num_splits(const orthrus_attn_desc* d);
  *              workspace must not overlap in time (use one workspace per
  *              stream).
  * Neither k_blk/v_blk nor anything else is ever written into the cache. */
-orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, orthrus_mask_mode mode,
+orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, int32_t mode,
                                   const uint16_t* q, const uint16_t* k_blk,
                                   const uint16_t* v_blk, const uint16_t* k_cache,
                                   const uint16_t* v_cache, const int32_t* cache_len,
@@ -158,7 +158,7 @@ orthrus_status orthrus_block_attn_masked(const orthrus_attn_desc* d, const uint1
  * which keeps the last call's contents: calls that overlap in time on one
  * device (several streams, several host threads) race and give wrong
  * results; calls in one stream's order are safe. */
-orthrus_status orthrus_block_attn_noalloc(const orthrus_attn_desc* d, orthrus_mask_mode mode,
+orthrus_status orthrus_block_attn_noalloc(const orthrus_attn_desc* d, int32_t mode,
                                           const uint16_t* q, const uint16_t* k_blk,
                                           const uint16_t* v_blk, const uint16_t* k_cache,
                                           const uint16_t* v_cache, const int32_t* cache_len,
@@ -173,7 +173,7 @@ orthrus_status orthrus_block_attn_noalloc(const orthrus_attn_desc* d, orthrus_ma
  * orthrus_block_attn does (the pair gives bit-identical results).  Both calls
  * must get the same descriptor and workspace, in this order on one stream;
  * arguments, layouts and errors are those of orthrus_block_attn. */
-orthrus_status orthrus_block_attn_partial(const orthrus_attn_desc* d, orthrus_mask_mode mode,
+orthrus_status orthrus_block_attn_partial(const orthrus_attn_desc* d, int32_t mode,
                                           const uint16_t* q, const uint16_t* k_blk,
                                           const uint16_t* v_blk, const uint16_t* k_cache,
                                           const uint16_t* v_cache, const int32_t* cache_len,
@@ -282,7 +282,7 @@ typedef enum {
 } orthrus_dtype;
 
 /* Workspace bytes orthrus_forward_kl needs (0 if the sizes are invalid). */
-size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, orthrus_dtype dtype);
+size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, int32_t dtype);
 
 /* Forward KL of the diffusion view against the frozen AR model over the whole
  * vocabulary -- the distillation loss of paper notes §3.1 and §3.3,
@@ -301,7 +301,7 @@ size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, orthrus_dtype dtyp
  * logits for one).  Sums run in fp32 in a fixed order, so results are
  * deterministic.  Rows are contiguous with stride V; rows up to 65535
  * (more: ORTHRUS_ERR_UNSUPPORTED).  grad may alias neither input. */
-orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, orthrus_dtype dtype,
+orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, int32_t dtype,
                                   const void* target_logits, const void* draft_logits, float* kl,
                                   void* grad, float grad_scale, void* workspace,
                                   size_t workspace_bytes, void* stream);
@@ -442,8 +442,10 @@ orthrus_status orthrus_cache_commit_path(const orthrus_commit_desc* d, uint16_t*
                                          int32_t* next_anchor, int32_t* tokens, int32_t* n_tokens,
                                          void* stream);
 
-/* Static, human-readable name of a status code. */
-const char* orthrus_status_string(orthrus_status s);
+/* Static, human-readable name of a status code (any value: unknown codes
+ * give "ORTHRUS_ERR_UNKNOWN").  Enumerations travel as int32_t across this
+ * interface, so out-of-range values are well defined and are rejected. */
+const char* orthrus_status_string(int32_t status);
 
 #ifdef __cplusplus
 }
