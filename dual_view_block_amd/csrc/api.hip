@@ -63,10 +63,12 @@ AttnPlan make_plan(const orthrus_attn_desc* d) {
   if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   p.splits = (int)s;
-  const size_t slots = (size_t)groups * p.splits * p.rows_per_wg;
+  // several sequences: a balanced launch writes up to one partial per
+  // work-group plus one per group boundary inside a work-group's range
+  const size_t slots = ((size_t)groups * p.splits + (d->batch > 1 ? (size_t)groups : 0)) * p.rows_per_wg;
   p.ml_bytes = round_up(slots * 2 * sizeof(float), kAlign);
   p.acc_bytes = round_up(slots * d->head_dim * sizeof(uint16_t), kAlign);
-  p.tab_bytes = round_up((size_t)d->batch * 2 * sizeof(int32_t), kAlign);
+  p.tab_bytes = round_up((size_t)groups * 2 * sizeof(int32_t), kAlign);  // first and last slot per group
   p.ws_bytes = p.ml_bytes + p.acc_bytes + p.tab_bytes;
   return p;
 }
@@ -142,7 +144,7 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.splits = attn_launch_splits(plan, d->batch, d->n_kv_heads, d->max_len, cus);
   const int cap = env_int("ORTHRUS_MAX_SPLITS", a.splits);  // tuning: may only lower the split count
   if (cap < a.splits) a.splits = cap;
-  // several sequences: share the launch's work-groups out by cache length
+  // several sequences: the launch's work-groups share one list of tiles
   a.ragged = (d->batch > 1 && d->batch <= kRaggedMaxSeqs && a.splits > 1 &&
               env_int("ORTHRUS_EVEN_SPLITS", 0) == 0) ? 1 : 0;
   a.nwg = d->batch * d->n_kv_heads * plan.row_groups * a.splits;
@@ -153,7 +155,6 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
             "row_groups=%d splits=%d ragged=%d ws=%zu\n", mode, d->batch, d->n_q_heads, d->n_kv_heads,
             d->head_dim, d->block_k, d->max_len, plan.rows, plan.qblocks, plan.row_groups,
             a.splits, a.ragged, plan.ws_bytes);
-  // tuning switch: merge the splits inside the streaming kernel (one launch)
   const hipError_t e = launch_block_attention(a, plan, phases, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }

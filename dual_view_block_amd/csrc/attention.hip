@@ -66,7 +66,8 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 // Cache range of one split of sequence b: [kstart, kend).
 struct SplitRange {
-  int kstart, kend, ncache, nblk, ntiles;  // tiles 0 .. nblk-1: the block keys; then ncache cache tiles
+  // tiles 0 .. nblk-1: block-key tiles blk0 .. blk0+nblk-1; then ncache cache tiles
+  int kstart, kend, ncache, nblk, ntiles, blk0;
 };
 
 __device__ __forceinline__ int seq_len(const AttnArgs& a, int b) {
@@ -88,105 +89,111 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int 
   // first cache tile is still on its way from HBM
   r.nblk = split == 0 ? (a.block_k + kTileKeys - 1) / kTileKeys : 0;
   r.ntiles = r.nblk + r.ncache;
+  r.blk0 = 0;
   return r;
 }
 
-// ---- length-aware placement for batches of several sequences
+// ---- balanced placement for batches of several sequences
 //
-// With several sequences the launch's N work-groups are shared out by cache
-// length rather than evenly: sequence b (nt_b = max(1, ceil(L_b / 64)) cache
-// tiles) gets s_b = ceil(nt_b / c) splits for each of its H = Hkv * row_groups
-// groups, where c is the smallest tile count per split with
-// H * sum_b s_b <= N.  Every work-group then streams at most c tiles, so a
-// long sequence no longer sets the time of the whole call.  The lengths are
-// read on the device by every streaming work-group (no host sync); each
-// sequence's first work-group leaves (first work-group, splits) in the
-// workspace for the merge.
-// Sequence b's work-groups are N_b = H * sum_{b' < b} s_b' .. + H * s_b - 1,
-// split-major (work-group N_b + split * H + h); its partials use the slot of
-// the work-group's index.  Work-groups past the last sequence have no work.
+// With several sequences of different lengths the launch's N work-groups
+// share one list of work: for every sequence b and every one of its
+// H = Hkv * row_groups groups h (b-major), a segment of kPieceCost cost units
+// followed by S_b tiles -- the nblk = ceil(K / 64) block-key tiles, then the
+// ceil(L_b / 64) cache tiles.  With W units in all and n = min(N, W),
+// work-group w < n takes units [w W / n, (w+1) W / n): every work-group gets
+// the same amount of work (to within one unit), whatever the lengths.  A
+// work-group's range can cross segments; it computes one partial per segment
+// whose tiles it touches, in slot w + seg (seg = b H + h): the pieces of one
+// segment come from consecutive work-groups, so their slots are consecutive,
+// and no two pieces share a slot (slots stay below N + B H).  The work-group
+// holding a segment's first tile records the first slot, the one holding its
+// last tile the last slot, for the merge.  The lengths are read on the device
+// (no host sync).
 
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-__device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return x;
+// Tiles of one segment of sequence b: block-key tiles, then cache tiles.
+__device__ __forceinline__ int seg_tiles(const AttnArgs& a, int b) {
+  return (a.block_k + kTileKeys - 1) / kTileKeys + (seq_len(a, b) + kTileKeys - 1) / kTileKeys;
 }
-__device__ __forceinline__ int seq_tiles(const AttnArgs& a, int b) {
-  return max(1, (seq_len(a, b) + kTileKeys - 1) / kTileKeys);
-}
+// The fixed cost of one piece (its q and first tiles' latency, the closing
+// combine and partial write: about 5.4 us against 1.37 us per tile), counted
+// as this many tiles of work at the head of every segment when the list is
+// divided, so that work-groups whose ranges cross many short segments get
+// fewer tiles.
+constexpr int kPieceCost = 4;
 
-// Up to kRaggedMaxSeqs sequences: lane l of a wave holds the tile counts of
-// sequences l, l + 64, ... in registers, read once.
+// Up to kRaggedMaxSeqs sequences: lane l of a wave holds the segment tile
+// counts of sequences l, l + 64, ... in registers, read once.
 constexpr int kRaggedSlots = kRaggedMaxSeqs / 64;
 
 struct RaggedTiles {
-  int nt[kRaggedSlots];  // tile count of sequence lane + 64*k (0 past the batch)
+  int st[kRaggedSlots];  // segment units of sequence lane + 64*k: kPieceCost + tiles (0 past the batch)
 };
 
 __device__ __forceinline__ RaggedTiles ragged_tiles(const AttnArgs& a) {
   const int lane = threadIdx.x & 63;
   RaggedTiles r;
 #pragma unroll
-  for (int k = 0; k < kRaggedSlots; ++k) r.nt[k] = lane + 64 * k < a.batch ? seq_tiles(a, lane + 64 * k) : 0;
+  for (int k = 0; k < kRaggedSlots; ++k)
+    r.st[k] = lane + 64 * k < a.batch ? kPieceCost + seg_tiles(a, lane + 64 * k) : 0;
   return r;
 }
 
-// The smallest tiles-per-split bound c with H * sum_b ceil(nt_b / c) <= N
-// (called by a whole wave; every lane gets c).  c lies between H*T/N and
-// H*T/(N - H*B), T = sum_b nt_b (N > H*B whenever the plan is used).
-__device__ int ragged_chunk_tiles(const AttnArgs& a, const RaggedTiles& rt, int H, int N) {
+__device__ __forceinline__ long long ragged_total(const RaggedTiles& rt) {
   int t = 0;
 #pragma unroll
-  for (int k = 0; k < kRaggedSlots; ++k) t += rt.nt[k];
-  const long long T = wave_sum(t);
-  const long long HT = (long long)H * T;
-  int lo = (int)max(1LL, (HT + N - 1) / N);
-  const long long room = (long long)N - (long long)H * a.batch;
-  int hi = (int)max((long long)lo, room > 0 ? (HT + room - 1) / room : HT);
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    int tot = 0;
-#pragma unroll
-    for (int k = 0; k < kRaggedSlots; ++k) tot += (rt.nt[k] + mid - 1) / mid;
-    if ((long long)wave_sum(tot) * H <= N) hi = mid; else lo = mid + 1;
-  }
-  return lo;
+  for (int k = 0; k < kRaggedSlots; ++k) t += rt.st[k];
+  return (long long)wave_sum(t);
 }
 
-struct RaggedSeq {
-  int b;      // sequence (-1: past the last one)
-  int first;  // its first work-group
-  int nsplit; // its splits per group
+struct SeqAt {
+  int b;           // the sequence
+  int stiles;      // its segment units kPieceCost + S_b
+  long long base;  // index of its first unit (segment h = 0) in the list
 };
 
-// The sequence whose work-groups contain work-group `lin` (a whole wave calls it).
-__device__ RaggedSeq ragged_seq(const AttnArgs& a, const RaggedTiles& rt, int H, int c, int lin) {
+// The sequence whose segments hold list unit T < W (a whole wave calls it).
+__device__ SeqAt seq_at(const AttnArgs& a, const RaggedTiles& rt, int H, long long T) {
   const int lane = threadIdx.x & 63;
-  int base = 0;
+  long long base = 0;
 #pragma unroll
   for (int k = 0; k < kRaggedSlots; ++k) {
     const int bb = 64 * k + lane;
-    const int sb = bb < a.batch ? (rt.nt[k] + c - 1) / c : 0;
-    int incl = sb * H;  // inclusive scan of the work-group counts
+    const long long sz = (long long)rt.st[k] * H;  // this lane's sequence: all H segments
+    long long incl = sz;                          // inclusive scan over the lanes
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
+      const long long y = __shfl_up(incl, o);
       if (lane >= o) incl += y;
     }
-    const int excl = incl - sb * H;
-    const unsigned long long m = __ballot(bb < a.batch && lin >= base + excl && lin < base + incl);
+    const long long excl = incl - sz;
+    const unsigned long long m = __ballot(bb < a.batch && T >= base + excl && T < base + incl);
     if (m) {
       const int src = __builtin_ctzll(m);
-      return {64 * k + src, base + __shfl(excl, src), __shfl(sb, src)};
+      return {64 * k + src, __shfl(rt.st[k], src), base + __shfl(excl, src)};
     }
     base += __shfl(incl, 63);
   }
-  return {-1, base, 0};
+  return {-1, 0, base};
+}
+
+// Key range of tiles [p0, p1) of a segment of sequence b.
+__device__ __forceinline__ SplitRange piece_range(const AttnArgs& a, int b, int p0, int p1) {
+  SplitRange r;
+  const int L = seq_len(a, b);
+  const int nb = (a.block_k + kTileKeys - 1) / kTileKeys;
+  r.blk0 = min(p0, nb);
+  r.nblk = min(p1, nb) - r.blk0;
+  const int c0 = max(p0, nb) - nb, c1 = max(p1, nb) - nb;  // cache tiles [c0, c1)
+  r.kstart = c0 * kTileKeys;
+  r.kend = min(c1 * kTileKeys, L);
+  r.ncache = c1 - c0;
+  r.ntiles = r.nblk + r.ncache;
+  return r;
 }
 
 // Merge of the S split partials of one output row: with per-split reference
@@ -369,7 +376,7 @@ __device__ __forceinline__ void merge_wave_dyn(const AttnArgs& a, const AttnPlan
 // 8 S^T MFMAs, 16 exponentials per lane, 8 O^T MFMAs.
 constexpr int kStreamThreads = kAttnThreads;
 
-template <int D, int NQB, bool EXPL>
+template <int D, int NQB, bool EXPL, bool RAGGED>
 __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a, AttnPlan plan, int direct) {
   constexpr int DCH = D / 8;
   constexpr int ROWB = D * 2;
@@ -389,32 +396,10 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   __shared__ __attribute__((aligned(16))) uint8_t smem[REGION0 + 128 * OPITCH];
   __shared__ float2 xstat[8][32];
 
-  // dispatch order: (b, g) groups interleaved, split 0 (the block keys) first;
-  // with several sequences, work-groups go to sequences by cache length
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  int bg, rg, split, nsplit;
-  size_t slot;
-  if (a.ragged) {
-    const int H = a.n_kv_heads * plan.row_groups;
-    const RaggedTiles rt = ragged_tiles(a);
-    const RaggedSeq sq = ragged_seq(a, rt, H, ragged_chunk_tiles(a, rt, H, a.nwg), lin);
-    if (sq.b < 0) return;  // no work left for this work-group (uniform: every wave finds the same)
-    const int local = lin - sq.first;
-    // the sequence's first work-group records where its splits are, for the merge
-    if (local == 0 && threadIdx.x == 0) a.ws_tab[sq.b] = make_int2(sq.first, sq.nsplit);
-    const int h = local % H;
-    split = local / H;
-    rg = h % plan.row_groups;
-    bg = sq.b * a.n_kv_heads + h / plan.row_groups;
-    nsplit = sq.nsplit;
-    slot = (size_t)lin;
-  } else {
-    bg = lin % (int)gridDim.z;
-    rg = (lin / (int)gridDim.z) % (int)gridDim.y;
-    split = lin / ((int)gridDim.z * (int)gridDim.y);
-    nsplit = a.splits;
-    slot = (size_t)(bg * plan.row_groups + rg) * a.splits + split;
-  }
+  // One piece of work: the key range `sr` of group (bg, rg), its partial
+  // written to `slot` (or, with a single split, the output itself).
+  auto piece = [&](const int bg, const int rg, const SplitRange sr, const size_t slot) __attribute__((always_inline)) {
   const int b = bg / a.n_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -425,7 +410,6 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   const bool active = qb < NQB;
   const int R = plan.rows;
   const int K = a.block_k;
-  const SplitRange sr = split_range(a, b, split, nsplit);
   const int g = bg % a.n_kv_heads;
   const long long q_grp = b * a.q_bs + (long long)g * a.group * a.q_hs;
   const long long o_grp = b * a.o_bs + (long long)g * a.group * a.o_hs;
@@ -466,11 +450,12 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     const int ct = t - sr.nblk;  // cache tile index
     const bool cache = real && !blk;
     const bool whole = cache && ct < nfull;
+    const int bt = sr.blk0 + t;  // block tile index
     const int last = whole ? kTileKeys - 1
-                           : (!real ? 0 : (blk ? min(kTileKeys, K - t * kTileKeys)
+                           : (!real ? 0 : (blk ? min(kTileKeys, K - bt * kTileKeys)
                                                : min(kTileKeys, sr.kend - (sr.kstart + ct * kTileKeys))) - 1);
     const size_t toff = (size_t)ct * TILEB;
-    const size_t boff = blk ? (size_t)t * TILEB : 0;
+    const size_t boff = blk ? (size_t)bt * TILEB : 0;
     const uint8_t* kp = cache ? kc0 + toff : kblk + boff;
     const uint8_t* vp = cache ? vc0 + toff : (real ? vblk + boff : kblk);
 #pragma unroll
@@ -489,7 +474,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     }
   };
   auto tile_valid = [&](int t) __attribute__((always_inline)) {
-    return t < sr.nblk ? min(kTileKeys, K - t * kTileKeys)
+    return t < sr.nblk ? min(kTileKeys, K - (sr.blk0 + t) * kTileKeys)
                        : min(kTileKeys, sr.kend - (sr.kstart + (t - sr.nblk) * kTileKeys));
   };
 
@@ -615,7 +600,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     load_v(st, vf);
     if (t < sr.nblk || t - sr.nblk >= nfull) {
       const bool blk = t < sr.nblk;
-      mask_scores(s, nval, blk, t * kTileKeys);
+      mask_scores(s, nval, blk, (sr.blk0 + t) * kTileKeys);
     }
     update_ref(s);
     float lsum = 0.0f;
@@ -725,6 +710,52 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
       __builtin_nontemporal_store(l_out, a.ws_ml + (slot * plan.rows_per_wg + wrow) * 2 + 1);
     }
   }
+  };
+
+  if constexpr (RAGGED) {
+    // Balanced placement (several sequences): this work-group's units
+    // [T, T1) of the launch's list, one piece per group whose tiles they touch.
+    const int H = a.n_kv_heads * plan.row_groups;
+    long long T, T1;
+    {
+      const long long W = (long long)H * ragged_total(ragged_tiles(a));
+      // with fewer units than work-groups, one unit each: no used
+      // work-group's range is empty, so the slots of every group stay
+      // consecutive
+      const long long n = min((long long)a.nwg, W);
+      if (lin >= n) return;
+      T1 = W * (lin + 1) / n;
+      T = W * lin / n;
+    }
+    bool first = true;
+    while (T < T1) {  // uniform: every wave walks the same pieces
+      const SeqAt sq = seq_at(a, ragged_tiles(a), H, T);
+      if (sq.b < 0) break;  // not reached: T < W lies in some sequence
+      const long long off = T - sq.base;
+      const int h = (int)(off / sq.stiles);
+      const int u0 = (int)(off % sq.stiles);  // units [u0, u1) of the segment
+      const int u1 = (int)min((long long)sq.stiles, T1 - (sq.base + (long long)h * sq.stiles));
+      T += u1 - u0;
+      const int p0 = max(u0 - kPieceCost, 0), p1 = max(u1 - kPieceCost, 0);  // its tiles
+      if (p0 == p1) continue;  // only the segment's cost units: no piece here
+      const int seg = sq.b * H + h;
+      const size_t slot = (size_t)lin + seg;
+      if (threadIdx.x == 0) {  // the group's first and last slots, for the merge
+        if (p0 == 0) a.ws_tab[seg].x = (int)slot;
+        if (p1 == sq.stiles - kPieceCost) a.ws_tab[seg].y = (int)slot;
+      }
+      if (!first) __syncthreads();  // this piece reuses the LDS of the last one
+      first = false;
+      piece(sq.b * a.n_kv_heads + h / plan.row_groups, h % plan.row_groups, piece_range(a, sq.b, p0, p1), slot);
+    }
+  } else {
+    // one piece: dispatch order (b, g) groups interleaved, split 0 (the block keys) first
+    const int bg = lin % (int)gridDim.z;
+    const int rg = (lin / (int)gridDim.z) % (int)gridDim.y;
+    const int split = lin / ((int)gridDim.z * (int)gridDim.y);
+    piece(bg, rg, split_range(a, bg / a.n_kv_heads, split, a.splits),
+          (size_t)(bg * plan.row_groups + rg) * a.splits + split);
+  }
 }
 
 // Stand-alone merge of the partials left by a streaming launch with fuse = 0:
@@ -749,9 +780,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a, A
   merge_wave<D, SMAX>(a, plan, grp, first % plan.rows_per_wg, plan.rows_per_wg);
 }
 
-// Merge after a length-aware streaming launch: one wave per row (two at
-// D 64); the group's splits and their slots come from the table the
-// streaming launch left in the workspace.
+// Merge after a balanced streaming launch: one wave per row (two at D 64);
+// the group's partials sit in consecutive slots, whose first and last the
+// streaming launch left in the workspace table.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_ragged_kernel(AttnArgs a, AttnPlan plan, int total_rows) {
   constexpr int RPW = 128 / D;
@@ -759,18 +790,23 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_ragged_kernel(AttnAr
   const int first = gw * RPW;
   if (first >= total_rows) return;
   const int grp = first / plan.rows_per_wg;
-  const int H = a.n_kv_heads * plan.row_groups;
-  const int2 sq = a.ws_tab[grp / H];  // (first work-group, splits) of the group's sequence
-  merge_wave_dyn<D>(a, plan, grp, (size_t)sq.x + grp % H, H, sq.y, first % plan.rows_per_wg, plan.rows_per_wg);
+  const int2 sl = a.ws_tab[grp];  // first and last slot of the group's partials
+  merge_wave_dyn<D>(a, plan, grp, (size_t)sl.x, 1, sl.y - sl.x + 1, first % plan.rows_per_wg, plan.rows_per_wg);
 }
 
 template <int D, int NQB>
 hipError_t launch_stream(const AttnArgs& a, const AttnPlan& p, int direct, hipStream_t stream) {
   dim3 grid(a.splits, p.row_groups, a.batch * a.n_kv_heads);
-  if (a.blk_mask != nullptr)
-    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, true>), grid, dim3(kStreamThreads), 0, stream, a, p, direct);
-  else
-    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, false>), grid, dim3(kStreamThreads), 0, stream, a, p, direct);
+  if (a.ragged) {
+    if (a.blk_mask != nullptr)
+      hipLaunchKernelGGL((attn_stream_kernel<D, NQB, true, true>), grid, dim3(kStreamThreads), 0, stream, a, p, direct);
+    else
+      hipLaunchKernelGGL((attn_stream_kernel<D, NQB, false, true>), grid, dim3(kStreamThreads), 0, stream, a, p, direct);
+  } else if (a.blk_mask != nullptr) {
+    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, true, false>), grid, dim3(kStreamThreads), 0, stream, a, p, direct);
+  } else {
+    hipLaunchKernelGGL((attn_stream_kernel<D, NQB, false, false>), grid, dim3(kStreamThreads), 0, stream, a, p, direct);
+  }
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ struct AttnArgs {
   float* lse;
   float* ws_ml;       // fp32 (reference max, sum) per row and split
   uint16_t* ws_acc;   // bf16 normalised partial output per row and split
-  int2* ws_tab;       // per sequence: first work-group and splits (length-aware launches)
+  int2* ws_tab;       // per group: first and last partial slot (balanced launches)
   int batch, n_q_heads, n_kv_heads, group, block_k, head_dim, max_len;
   int causal;
   int splits;        // splits of this launch (<= plan.splits)
