@@ -312,66 +312,6 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
 // memory round trip, combined online (the running maximum, sum and value sum
 // are rescaled when a batch raises the maximum).  Lane j < 16 of a row holds
 // the statistics of split s0 + j of batch s0.  Fixed summation order.
-template <int D>
-__device__ __forceinline__ void merge_wave_dyn(const AttnArgs& a, const AttnPlan& p, int grp, size_t slot0,
-                                               int stride, int S, int row, int row_end) {
-  constexpr int LPR = D / 2;
-  constexpr int NB = 16;
-  const int lane = threadIdx.x & 63;
-  const int j = lane & (LPR - 1);
-  const int hw = LPR == 32 ? (lane >> 5) : 0;
-  const int myrow = row + hw;
-  const int rrow = min(myrow, p.rows_per_wg - 1);
-  float M = kNegInf, L = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
-  for (int s0 = 0; s0 < S; s0 += NB) {
-    uint32_t v[NB];
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      const size_t idx = (slot0 + (size_t)min(s0 + t, S - 1) * stride) * p.rows_per_wg + rrow;
-      v[t] = *reinterpret_cast<const uint32_t*>(a.ws_acc + idx * D + 2 * j);
-    }
-    const bool real = j < NB && s0 + j < S;
-    const size_t sidx = (slot0 + (size_t)min(s0 + min(j, NB - 1), S - 1) * stride) * p.rows_per_wg + rrow;
-    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + sidx * 2);
-    const float m = real ? ml.x : kNegInf;
-    const float l = real ? ml.y : 0.0f;
-    const float Mn = fmaxf(M, row_reduce<LPR>(m, [](float x, float y) { return fmaxf(x, y); }));
-    const float sc = M == kNegInf ? 0.0f : fast_exp2(M - Mn);
-    L *= sc;
-    acc0 *= sc;
-    acc1 *= sc;
-    const float wt = m == kNegInf ? 0.0f : fast_exp2(m - Mn) * l;
-    L += row_reduce<LPR>(wt, [](float x, float y) { return x + y; });
-#pragma unroll
-    for (int t = 0; t < NB; ++t) {
-      float ws;
-      if constexpr (LPR == 64) {
-        ws = readlane_f(wt, t);
-      } else {
-        const float w0 = readlane_f(wt, t);
-        const float w1 = readlane_f(wt, t + 32);
-        ws = hw ? w1 : w0;
-      }
-      ws = s0 + t < S ? ws : 0.0f;
-      acc0 = fmaf(ws, __uint_as_float(v[t] << 16), acc0);
-      acc1 = fmaf(ws, __uint_as_float(v[t] & 0xFFFF0000u), acc1);
-    }
-    M = Mn;
-  }
-  if (myrow < row_end) {
-    const int rg = grp % p.row_groups;
-    const int r = rg * p.rows_per_wg + myrow;
-    if (r < p.rows) {
-      const int bg = grp / p.row_groups;
-      const int b = bg / a.n_kv_heads, h = (bg % a.n_kv_heads) * a.group + r / a.block_k, i = r % a.block_k;
-      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      const uint32_t o = (uint32_t)to_bf16_bits(acc0 * inv) | ((uint32_t)to_bf16_bits(acc1 * inv) << 16);
-      *reinterpret_cast<uint32_t*>(a.out + b * a.o_bs + h * a.o_hs + (long long)i * D + 2 * j) = o;
-      if (a.lse != nullptr && j == 0) a.lse[b * a.l_bs + h * a.l_hs + i] = (M + log2f(L)) * kLn2;
-    }
-  }
-}
-
 // The streaming kernel (see the top of the file).  Per wave and tile at D 128:
 // 8 S^T MFMAs, 16 exponentials per lane, 8 O^T MFMAs.
 constexpr int kStreamThreads = kAttnThreads;
@@ -780,18 +720,70 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(AttnArgs a, A
   merge_wave<D, SMAX>(a, plan, grp, first % plan.rows_per_wg, plan.rows_per_wg);
 }
 
-// Merge after a balanced streaming launch: one wave per row (two at D 64);
-// the group's partials sit in consecutive slots, whose first and last the
-// streaming launch left in the workspace table.
+// Merge after a balanced streaming launch: a group's partials sit in
+// consecutive slots, whose first and last the streaming launch left in the
+// workspace table; there are usually few.  A row takes D / 8 lanes, each
+// owning 8 head_dim values (one 16-byte load per partial), and every lane
+// reads each partial's (m, l) itself, so no lane exchange is needed.  Partials
+// are folded four at a time with an online maximum, in slot order.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_ragged_kernel(AttnArgs a, AttnPlan plan, int total_rows) {
-  constexpr int RPW = 128 / D;
-  const int gw = (int)blockIdx.x * (kMergeThreads / 64) + (int)(threadIdx.x >> 6);
-  const int first = gw * RPW;
-  if (first >= total_rows) return;
-  const int grp = first / plan.rows_per_wg;
+  constexpr int LPR = D / 8;
+  constexpr int NB = 4;
+  const int mrow = (int)blockIdx.x * (kMergeThreads / LPR) + (int)threadIdx.x / LPR;
+  if (mrow >= total_rows) return;
+  const int j = (int)threadIdx.x % LPR;
+  const int grp = mrow / plan.rows_per_wg;
+  const int row = mrow % plan.rows_per_wg;
   const int2 sl = a.ws_tab[grp];  // first and last slot of the group's partials
-  merge_wave_dyn<D>(a, plan, grp, (size_t)sl.x, 1, sl.y - sl.x + 1, first % plan.rows_per_wg, plan.rows_per_wg);
+  const int S = sl.y - sl.x + 1;
+  float M = kNegInf, L = 0.0f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += NB) {
+    u32x4 v[NB];
+    float2 ml[NB];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {  // past the last partial: re-read it, weight 0
+      const size_t idx = ((size_t)sl.x + min(s0 + t, S - 1)) * plan.rows_per_wg + row;
+      v[t] = *reinterpret_cast<const u32x4*>(a.ws_acc + idx * D + 8 * j);
+      ml[t] = *reinterpret_cast<const float2*>(a.ws_ml + idx * 2);
+    }
+    float m[NB];
+    float Mn = M;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      m[t] = s0 + t < S ? ml[t].x : kNegInf;
+      Mn = fmaxf(Mn, m[t]);
+    }
+    const float sc = M == kNegInf ? 0.0f : fast_exp2(M - Mn);
+    L *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const float w = m[t] == kNegInf ? 0.0f : fast_exp2(m[t] - Mn) * ml[t].y;
+      L += w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(w, __uint_as_float(v[t][q] << 16), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(w, __uint_as_float(v[t][q] & 0xFFFF0000u), acc[2 * q + 1]);
+      }
+    }
+    M = Mn;
+  }
+  const int rg = grp % plan.row_groups;
+  const int r = rg * plan.rows_per_wg + row;
+  if (r >= plan.rows) return;
+  const int bg = grp / plan.row_groups;
+  const int b = bg / a.n_kv_heads, h = (bg % a.n_kv_heads) * a.group + r / a.block_k, i = r % a.block_k;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = (uint32_t)to_bf16_bits(acc[2 * q] * inv) | ((uint32_t)to_bf16_bits(acc[2 * q + 1] * inv) << 16);
+  *reinterpret_cast<u32x4*>(a.out + b * a.o_bs + h * a.o_hs + (long long)i * D + 8 * j) = o;
+  if (a.lse != nullptr && j == 0) a.lse[b * a.l_bs + h * a.l_hs + i] = (M + log2f(L)) * kLn2;
 }
 
 template <int D, int NQB>
@@ -822,7 +814,7 @@ hipError_t launch_merge_s(const AttnArgs& a, const AttnPlan& p, hipStream_t stre
 template <int D>
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, hipStream_t stream) {
   if (a.ragged) {
-    constexpr int rows_per_block = (kMergeThreads / 64) * (128 / D);
+    constexpr int rows_per_block = kMergeThreads / (D / 8);
     const int total = a.batch * a.n_kv_heads * p.row_groups * p.rows_per_wg;
     dim3 grid((total + rows_per_block - 1) / rows_per_block);
     hipLaunchKernelGGL((attn_merge_ragged_kernel<D>), grid, dim3(kMergeThreads), 0, stream, a, p, total);
