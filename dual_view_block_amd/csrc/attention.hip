@@ -120,11 +120,11 @@ __device__ __forceinline__ int seg_tiles(const AttnArgs& a, int b) {
   return (a.block_k + kTileKeys - 1) / kTileKeys + (seq_len(a, b) + kTileKeys - 1) / kTileKeys;
 }
 // The fixed cost of one piece (its q and first tiles' latency, the closing
-// combine and partial write: about 5.4 us against 1.37 us per tile), counted
-// as this many tiles of work at the head of every segment when the list is
-// divided, so that work-groups whose ranges cross many short segments get
-// fewer tiles.
-constexpr int kPieceCost = 4;
+// combine and partial write: about 7.7 us against 1.2 us per tile, fitted
+// over the work-groups of a 16-sequence launch), counted as this many tiles
+// of work at the head of every segment when the list is divided, so that
+// work-groups whose ranges cross many short segments get fewer tiles.
+constexpr int kPieceCost = 6;
 
 // Up to kRaggedMaxSeqs sequences: lane l of a wave holds the segment tile
 // counts of sequences l, l + 64, ... in registers, read once.
