@@ -689,8 +689,11 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
       piece(sq.b * a.n_kv_heads + h / plan.row_groups, h % plan.row_groups, piece_range(a, sq.b, p0, p1), slot);
     }
   } else {
-    // one piece: dispatch order (b, g) groups interleaved, split 0 (the block keys) first
-    const int bg = lin % (int)gridDim.z;
+    // one piece: dispatch order (b, g) groups interleaved, split 0 (the block
+    // keys) first.  With lengths growing with b (the training clean rows:
+    // sequence b sees b * len_step keys) the longest groups go first, so the
+    // short ones fill in behind them rather than the long ones starting last.
+    const int bg = a.len_step > 0 ? (int)gridDim.z - 1 - lin % (int)gridDim.z : lin % (int)gridDim.z;
     const int rg = (lin / (int)gridDim.z) % (int)gridDim.y;
     const int split = lin / ((int)gridDim.z * (int)gridDim.y);
     piece(bg, rg, split_range(a, bg / a.n_kv_heads, split, a.splits),
