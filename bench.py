@@ -450,12 +450,15 @@ def _time_calls(fn, reps: int, stream) -> float:
 
 
 # The other configuration points, timed as whole steps on their own caches:
-# (label, workload, overrides).  C4 at L = 131072 is timed at K = 32 and K = 1.
+# (label, workload, overrides).  C4 at L = 131072 is timed over its K sweep.
 CONFIG_POINTS = (
     ("C2", "qwen3_1p7b_layer", {}),
     ("C3", "qwen3_8b_8k", {}),
     ("C4", "qwen3_8b_128k", {}),
     ("C4", "qwen3_8b_128k", {"block_k": 1}),
+    ("C4", "qwen3_8b_128k", {"block_k": 4}),
+    ("C4", "qwen3_8b_128k", {"block_k": 8}),
+    ("C4", "qwen3_8b_128k", {"block_k": 16}),
     ("C5", "ragged_b16", {}),
 )
 
