@@ -38,17 +38,40 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* _
   const int end = min(vocab, begin + chunk_len);
   const float* rp = logits + row * (size_t)vocab;
   unsigned long long best = 0;  // below every packed key of a real element
+  // kUnroll loads in flight per thread before any is reduced.  Positions past
+  // the chunk end are clamped to its last vector (or element): a repeated
+  // element repeats its key, which cannot change a maximum.
+  constexpr int kUnroll = 8;
   if ((vocab & 3) == 0) {
     // chunk_len is a multiple of 4, so begin is 16-byte aligned within the row
-    for (int v = begin + 4 * threadIdx.x; v < end; v += 4 * kThreads) {
-      const float4 x = *reinterpret_cast<const float4*>(rp + v);
-      best = umax64(best, pack_key(x.x, v));
-      best = umax64(best, pack_key(x.y, v + 1));
-      best = umax64(best, pack_key(x.z, v + 2));
-      best = umax64(best, pack_key(x.w, v + 3));
+    for (int v0 = begin + 4 * threadIdx.x; v0 < end; v0 += 4 * kThreads * kUnroll) {
+      float4 x[kUnroll];
+      int vv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        vv[u] = min(v0 + 4 * kThreads * u, end - 4);
+        x[u] = *reinterpret_cast<const float4*>(rp + vv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        best = umax64(best, pack_key(x[u].x, vv[u]));
+        best = umax64(best, pack_key(x[u].y, vv[u] + 1));
+        best = umax64(best, pack_key(x[u].z, vv[u] + 2));
+        best = umax64(best, pack_key(x[u].w, vv[u] + 3));
+      }
     }
   } else {
-    for (int v = begin + threadIdx.x; v < end; v += kThreads) best = umax64(best, pack_key(rp[v], v));
+    for (int v0 = begin + threadIdx.x; v0 < end; v0 += kThreads * kUnroll) {
+      float x[kUnroll];
+      int vv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        vv[u] = min(v0 + kThreads * u, end - 1);
+        x[u] = rp[vv[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) best = umax64(best, pack_key(x[u], vv[u]));
+    }
   }
   __shared__ unsigned long long red[kThreads / 64];
   best = wave_max64(best);
@@ -59,6 +82,20 @@ __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* _
     for (int w = 1; w < kThreads / 64; ++w) m = umax64(m, red[w]);
     part[row * gridDim.x + c] = m;
   }
+}
+
+// Maximum of a row's chunk keys, eight loads in flight at a time (indices
+// past the last chunk repeat it).
+__device__ __forceinline__ unsigned long long chunks_max(const unsigned long long* pp, int chunks) {
+  unsigned long long m = 0;
+  for (int c0 = 0; c0 < chunks; c0 += 8) {
+    unsigned long long k[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) k[u] = pp[min(c0 + u, chunks - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = umax64(m, k[u]);
+  }
+  return m;
 }
 
 __global__ __launch_bounds__(64) void greedy_finalize_kernel(int block_k, int chunks,
@@ -73,9 +110,7 @@ __global__ __launch_bounds__(64) void greedy_finalize_kernel(int block_k, int ch
     int am = -1;
     bool mismatch = false;
     if (i < block_k) {
-      const unsigned long long* pp = part + ((size_t)b * block_k + i) * chunks;
-      unsigned long long m = 0;
-      for (int c = 0; c < chunks; ++c) m = umax64(m, pp[c]);
+      const unsigned long long m = chunks_max(part + ((size_t)b * block_k + i) * chunks, chunks);
       am = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
       mismatch = cand[(size_t)b * block_k + i] != am;
       if (row_argmax != nullptr) row_argmax[(size_t)b * block_k + i] = am;
@@ -110,9 +145,7 @@ __global__ __launch_bounds__(64) void tree_finalize_kernel(int K, int chunks, co
   for (int h = 0; h < 2; ++h) {
     const int i = lane + 64 * h;
     if (i < K) {
-      const unsigned long long* pp = part + ((size_t)b * K + i) * chunks;
-      unsigned long long m = 0;
-      for (int c = 0; c < chunks; ++c) m = umax64(m, pp[c]);
+      const unsigned long long m = chunks_max(part + ((size_t)b * K + i) * chunks, chunks);
       am[h] = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
       par[h] = parent[(size_t)b * K + i];
       tok[h] = tokens[(size_t)b * K + i];
