@@ -539,6 +539,7 @@ orthrus_status orthrus_train_attn_fwd(const orthrus_train_attn_desc* d, const ui
     a.c_bs = 0;
     a.c_gs = L * D;
     a.len_step = 0;
+    a.rank_blocks = 1;  // the longest prefixes first
     const orthrus_status r = run_train_part(d, d->n_blocks, (int)K, 0, a, stream);
     if (r != ORTHRUS_OK) return r;
   }

@@ -52,6 +52,7 @@
 //    wrote.
 #include "attn_frag.h"
 #include "common.h"
+#include "block_order.h"
 
 #include <math.h>
 
@@ -693,7 +694,10 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     // keys) first.  With lengths growing with b (the training clean rows:
     // sequence b sees b * len_step keys) the longest groups go first, so the
     // short ones fill in behind them rather than the long ones starting last.
-    const int bg = a.len_step > 0 ? (int)gridDim.z - 1 - lin % (int)gridDim.z : lin % (int)gridDim.z;
+    int bg = a.len_step > 0 ? (int)gridDim.z - 1 - lin % (int)gridDim.z : lin % (int)gridDim.z;
+    // anchor blocks of a training sequence: likewise longest first, ranked on the device
+    if (a.rank_blocks && a.batch <= kRankMaxBlocks)
+      bg = block_by_rank(a.cache_len, a.batch, a.max_len, bg / a.n_kv_heads) * a.n_kv_heads + bg % a.n_kv_heads;
     const int rg = (lin / (int)gridDim.z) % (int)gridDim.y;
     const int split = lin / ((int)gridDim.z * (int)gridDim.y);
     piece(bg, rg, split_range(a, bg / a.n_kv_heads, split, a.splits),

@@ -32,6 +32,7 @@
 // the MFMA contraction.
 #include "attn_frag.h"
 #include "common.h"
+#include "block_order.h"
 
 #include <math.h>
 
@@ -68,7 +69,9 @@ __global__ __launch_bounds__(kBwdThreads) void train_bwd_kernel(const TrainBwdAr
   // 441 -> 385 us at L 2048, 256 blocks of 32, 32/8 heads.
   const int lin = (int)blockIdx.x + (int)gridDim.x * (int)blockIdx.y;
   const int g = lin % (int)gridDim.y;  // KV head
-  const int n = lin / (int)gridDim.y;  // anchor block
+  // anchor block: longest prefix first (see block_order.h)
+  const int n = a.n_blocks <= kRankMaxBlocks ? block_by_rank(a.anchors, a.n_blocks, a.seq_len, lin / (int)gridDim.y)
+                                             : lin / (int)gridDim.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
