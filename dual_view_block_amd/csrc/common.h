@@ -30,7 +30,7 @@ struct AttnPlan {
   int splits;        // most splits per (sequence, KV head, row group) the workspace holds
   size_t ml_bytes;       // fp32 (max, sum) per row and split
   size_t acc_bytes;      // bf16 normalised partial outputs per row and split
-  size_t tab_bytes;      // int2 per sequence: first work-group and splits (length-aware launches)
+  size_t tab_bytes;      // int2 per group: first and last partial slot (balanced launches)
   size_t ws_bytes;       // total workspace
 };
 
@@ -49,8 +49,8 @@ struct AttnArgs {
   int batch, n_q_heads, n_kv_heads, group, block_k, head_dim, max_len;
   int causal;
   int splits;        // splits of this launch (<= plan.splits)
-  int ragged;        // 1: several sequences, work-groups shared out by cache length
-  int nwg;           // work-groups of the streaming launch (ragged placement)
+  int ragged;        // 1: several sequences, the work-groups share one list of tiles (balanced)
+  int nwg;           // work-groups of the streaming launch (balanced placement)
   float scale_log2;  // softmax scale * log2(e)
   // Element strides.  Block row i of q head h in sequence b is at
   // q + b*q_bs + h*q_hs + i*head_dim (out likewise with o_*, lse with l_*, in
