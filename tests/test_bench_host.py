@@ -101,3 +101,32 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_trace_summary_phases(tmp_path, capsys):
+    """--summarize-trace with --trace-phases: the streaming kernel's dispatches
+    a..b-1 of its most frequent launch shape, in launch order, summarised per
+    phase (values written out here: durations 10, 20, ... µs)."""
+    import sqlite3
+
+    db = tmp_path / "t.db"
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (name text, start integer, end integer, grid_x integer, grid_y integer, "
+                "grid_z integer, workgroup_x integer)")
+    k = "void orthrus::(anonymous namespace)::attn_stream_kernel<128, 4, false, false>(orthrus::AttnArgs)"
+    m = "void orthrus::(anonymous namespace)::attn_merge_kernel<128, 32>(orthrus::AttnArgs)"
+    t = 0
+    for i in range(6):  # stream dispatch i lasts 10 (i + 1) us, each followed by a merge of 1 us
+        con.execute("insert into kernels values (?, ?, ?, 16384, 1, 8, 512)", (k, t, t + 10_000 * (i + 1)))
+        t += 10_000 * (i + 1)
+        con.execute("insert into kernels values (?, ?, ?, 65536, 1, 1, 256)", (m, t, t + 1_000))
+        t += 1_000
+    # one dispatch of another launch shape, which must not count
+    con.execute("insert into kernels values (?, ?, ?, 1024, 1, 128, 512)", (k, t, t + 999_000))
+    con.commit()
+    con.close()
+    bench.summarize_trace(str(db), "first=0:2,rest=2:6")
+    out = capsys.readouterr().out
+    assert "| first | 2 | 15.00 | 15.00 | 10.00 |" in out
+    assert "| rest | 4 | 45.00 | 45.00 | 30.00 |" in out
+    assert "(16384 × 1 × 8)" in out
