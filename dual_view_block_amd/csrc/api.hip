@@ -3,6 +3,7 @@
 // stream-ordered launches.  No allocation, no synchronisation, no state.
 #include "../../include/orthrus.h"
 #include "common.h"
+#include "block_order.h"
 
 #include <math.h>
 #include <atomic>
@@ -148,6 +149,8 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.ragged = (d->batch > 1 && d->batch <= kRaggedMaxSeqs && a.splits > 1 &&
               env_int("ORTHRUS_EVEN_SPLITS", 0) == 0) ? 1 : 0;
   a.nwg = d->batch * d->n_kv_heads * plan.row_groups * a.splits;
+  // one work-group per group (no split): the sequences are taken longest first
+  a.rank_blocks = (a.splits == 1 && d->batch > 1 && d->batch <= kRankMaxBlocks) ? 1 : 0;
   const float scale = d->softmax_scale > 0.0f ? d->softmax_scale : 1.0f / sqrtf((float)d->head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   if ((phases & 1) && getenv("ORTHRUS_DEBUG") != nullptr)

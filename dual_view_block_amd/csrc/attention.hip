@@ -695,7 +695,8 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     // sequence b sees b * len_step keys) the longest groups go first, so the
     // short ones fill in behind them rather than the long ones starting last.
     int bg = a.len_step > 0 ? (int)gridDim.z - 1 - lin % (int)gridDim.z : lin % (int)gridDim.z;
-    // anchor blocks of a training sequence: likewise longest first, ranked on the device
+    // anchor blocks of a training sequence, or a decode batch without splits:
+    // likewise longest first, ranked on the device
     if (a.rank_blocks && a.batch <= kRankMaxBlocks)
       bg = block_by_rank(a.cache_len, a.batch, a.max_len, bg / a.n_kv_heads) * a.n_kv_heads + bg % a.n_kv_heads;
     const int rg = (lin / (int)gridDim.z) % (int)gridDim.y;

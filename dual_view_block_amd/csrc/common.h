@@ -62,9 +62,10 @@ struct AttnArgs {
   // > 0: sequence b attends to cache rows [0, b*len_step) and cache_len is
   // not read (causal rows processed in groups of block_k)
   int len_step;
-  // 1: the sequences are anchor blocks of one training sequence, taken
-  // longest first (work-group j of a KV head takes the block of rank j by
-  // ceil(cache_len / 64), see block_order.h); 0: in index order
+  // 1: the sequences (anchor blocks of a training sequence, or a decode batch
+  // with one work-group per group) are taken longest first: work-group j of a
+  // KV head takes the sequence of rank j by ceil(cache_len / 64) (see
+  // block_order.h); 0: in index order
   int rank_blocks;
   // Explicit block masks (block_k <= 64): bit j of blk_mask[b*block_k + i]
   // set = block key j visible to block row i; NULL = the mode's mask.

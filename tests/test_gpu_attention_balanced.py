@@ -136,3 +136,18 @@ def test_hundred_sequences(mode):
     x, pieces, _, _ = _case(lens, 2, 1, 128, 4, seed=31)
     assert len({p[1] for p in pieces}) == 100
     _check(x, mode, "100 sequences")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_unsplit_batch_taken_longest_first(mode):
+    """40 sequences of 0..4000 keys with 8 KV heads: 320 groups, so one
+    work-group per group and no split; the work-groups take the sequences
+    longest first (ranked on the device from the lengths)."""
+    rng = np.random.default_rng(13)
+    lens = [int(v) for v in rng.integers(0, 4000, size=40)]
+    w = Workload("unsplit", 1, 40, 32, 8, 128, max(lens), 32, 10, 1.0, 43, max_len=4096)
+    x = attention_inputs(w, device=DEV)
+    x["cache_len"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    assert dvb.orthrus_attn_num_splits(dvb.attn_desc(x["q"], x["k_cache"])) == 1
+    _check(x, mode, "unsplit batch of 40")
+
