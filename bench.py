@@ -300,12 +300,16 @@ def time_steps(step, steps: int, warmup: int, graph: bool):
     return t0.elapsed_time(t1) / steps, wall / steps * 1e3
 
 
-def time_kernels(step, reps: int = 3):
+KERNEL_WARM_RUNS, KERNEL_TIMED_RUNS = 1, 5
+
+
+def time_kernels(step, reps: int = KERNEL_TIMED_RUNS, warm: int = KERNEL_WARM_RUNS):
     """Average device duration per launch, from HIP events on the launch stream
     around a run of back-to-back launches over every layer of both views: the
     streaming kernel alone (orthrus_block_attn_partial), the merge kernel alone
-    (orthrus_block_attn_merge) and the whole call (orthrus_block_attn_*).  The
-    median over `reps` runs is reported."""
+    (orthrus_block_attn_merge) and the whole call (orthrus_block_attn_*).  After
+    `warm` untimed runs, the median over `reps` timed runs is reported (the
+    first run after the steps measured up to 10 % slower than the rest)."""
     import torch
 
     stream = torch.cuda.current_stream()
@@ -314,8 +318,11 @@ def time_kernels(step, reps: int = 3):
     out = {}
     for what in ("stream", "merge", "call"):
         per = []
+        fns = [c.partial if what == "stream" else (c.merge if what == "merge" else c.__call__) for c in calls]
+        for _ in range(warm):
+            for fn in fns:
+                fn(sp)
         for _ in range(reps):
-            fns = [c.partial if what == "stream" else (c.merge if what == "merge" else c.__call__) for c in calls]
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for fn in fns:
@@ -830,7 +837,8 @@ def main():
     n_l = len(step.calls["diff"]) + len(step.calls["verify"])
     pre = (1 if args.graph else 0) + args.warmup
     t0 = (pre + args.steps) * n_l
-    phases = {"timed_steps": (pre * n_l, t0), "back_to_back": (t0, t0 + 3 * n_l)}
+    b0 = t0 + KERNEL_WARM_RUNS * n_l
+    phases = {"timed_steps": (pre * n_l, t0), "back_to_back": (b0, b0 + KERNEL_TIMED_RUNS * n_l)}
     phase_arg = ",".join(f"{k}={a}:{b}" for k, (a, b) in phases.items())
     print(f"[bench] streaming-kernel dispatch phases: {phase_arg}", file=sys.stderr, flush=True)
     print(f"[bench] step {ms * 1e3:.1f} us (host wall {wall_ms * 1e3:.1f} us), streaming kernel "
@@ -928,7 +936,8 @@ def main():
                      "kernel": "attn_stream_kernel<128,4> (one launch per orthrus_block_attn_* call)",
                      "algorithmic_bytes_per_launch": pbytes,
                      "duration_us": round(kern["attn_stream_us"], 3),
-                     "duration_from": "HIP events around 3 runs of back-to-back streaming launches, median",
+                     "duration_from": f"HIP events around {KERNEL_TIMED_RUNS} runs of back-to-back streaming "
+                                      f"launches after {KERNEL_WARM_RUNS} untimed, median",
                      "trace_phases": phase_arg,
                      "call_achieved_gbs": round(attn_bytes(w) / (kern["attn_call_us"] * 1e-6) / 1e9, 1)},
     }
