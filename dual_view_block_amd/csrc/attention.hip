@@ -237,6 +237,11 @@ __device__ __forceinline__ float row_reduce(float v, Op op) {
   return v;
 }
 
+// Merge of one output row (two at D = 64, one per half-wave) from the S <= SMAX
+// partials of group grp: every lane loads the row's two values of each split
+// and the statistics of splits j, j + LPR, ... in one memory round trip, the
+// row's maximum and weight sum are reduced across its lanes, and the values
+// are summed in split order.
 template <int D, int SMAX>
 __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p, int grp, int row, int row_end) {
   constexpr int LPR = D / 2;                  // lanes per row
@@ -308,11 +313,6 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
   }
 }
 
-// Merge of one output row (two at D = 64, one per half-wave) from S partials
-// at slots slot0 + s * stride, for any S: batches of 16 splits, each batch one
-// memory round trip, combined online (the running maximum, sum and value sum
-// are rescaled when a batch raises the maximum).  Lane j < 16 of a row holds
-// the statistics of split s0 + j of batch s0.  Fixed summation order.
 // The streaming kernel (see the top of the file).  Per wave and tile at D 128:
 // 8 S^T MFMAs, 16 exponentials per lane, 8 O^T MFMAs.
 constexpr int kStreamThreads = kAttnThreads;
