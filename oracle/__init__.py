@@ -19,7 +19,10 @@ What is computed follows the Orthrus pages:
 * the training-time dual-pass block-mask attention, forward and the backward
   of the diffusion rows -- ``oracle.train_attn``;
 * tree verification (draft trees from top-M marginals, ancestor masks, greedy
-  consensus along the tree, path commit) -- ``oracle.tree``.
+  consensus along the tree, path commit) -- ``oracle.tree``;
+* dynamic block sizes (a block length per sequence, the consensus and commit
+  over it, and the rule that picks the next length from acceptance) --
+  ``oracle.dynamic``.
 
 Every function is the plain definition written out in float64 (or exact
 integers), one sequence / head at a time, with explicit masks.  Library
@@ -42,6 +45,8 @@ from .kl import forward_kl, forward_kl_rows
 from .train_attn import dual_pass_backward, dual_pass_forward, training_attention_flops
 from .tree import (ancestor_masks, build_tree, commit_path, masks_to_bits, topk_logprobs,
                    tree_greedy_consensus)
+from .dynamic import (block_attention_dyn, commit_block_dyn, greedy_consensus_dyn, live_lengths,
+                      next_block_len, sample_consensus_dyn)
 
 __all__ = [
     "MASK_DIFF_BIDIR", "MASK_VERIFY_CAUSAL", "block_attention",
@@ -51,5 +56,6 @@ __all__ = [
     "tokens_committed", "bits_to_bf16", "commit_block", "decode_cycles", "forward_kl",
     "forward_kl_rows", "dual_pass_forward", "dual_pass_backward", "training_attention_flops",
     "MASK_EXPLICIT", "ancestor_masks", "build_tree", "commit_path", "masks_to_bits", "topk_logprobs",
-    "tree_greedy_consensus",
+    "tree_greedy_consensus", "block_attention_dyn", "commit_block_dyn", "greedy_consensus_dyn",
+    "live_lengths", "next_block_len", "sample_consensus_dyn",
 ]

@@ -1,0 +1,241 @@
+"""Pins for the dynamic-block oracle (CPU only).
+
+Each test ties ``oracle.dynamic`` to something other than itself:
+
+* attention: torch's float64 scaled_dot_product_attention over the keys a
+  k_b-position block sees, with the mask built here from the definition
+  (cache positions all visible; block keys j < k_b, all of them or j <= i);
+* greedy consensus: a pure-Python scan written out here;
+* T > 0 consensus: properties the definition fixes (rows past k_b are never
+  read, a <= k_b, a = k_b exactly when every live test passes, the residual
+  draw uses u_K), and identity with the static sampler when k_b = K;
+* commit: a hand-worked cycle (rows, length, tokens, anchor) with marked
+  block rows past k_b that must never reach the cache;
+* the block-length rule: a hand table over (a, k).
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle.attention import MASK_DIFF_BIDIR as DIFF, MASK_VERIFY_CAUSAL as VERIFY
+from synth import Workload, attention_inputs
+
+
+def _case(B, Hq, Hkv, K, D, lens, seed):
+    w = Workload("dyn", 1, B, Hq, Hkv, D, max(max(lens), 1), K, 10, 1.0, seed)
+    x = attention_inputs(w, seed_offset=seed)
+    x["cache_len"] = torch.tensor(lens, dtype=torch.int32)
+    return x
+
+
+@pytest.mark.parametrize("mode", [DIFF, VERIFY])
+def test_attention_matches_sdpa_on_the_live_block(mode):
+    B, Hq, Hkv, K, D = 3, 4, 2, 6, 16
+    lens = [9, 0, 14]
+    kl = [1, 6, 4]
+    x = _case(B, Hq, Hkv, K, D, lens, 3)
+    out, lse = oracle.block_attention_dyn(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"],
+                                          x["cache_len"], torch.tensor(kl, dtype=torch.int32), mode)
+    G = Hq // Hkv
+    for b in range(B):
+        L, k = lens[b], kl[b]
+        for h in range(Hq):
+            g = h // G
+            keys = torch.cat([x["k_cache"][b, g, :L], x["k_blk"][b, g, :k]]).double()
+            vals = torch.cat([x["v_cache"][b, g, :L], x["v_blk"][b, g, :k]]).double()
+            mask = torch.zeros((k, L + k), dtype=torch.bool)
+            mask[:, :L] = True
+            for i in range(k):
+                for j in range(k):
+                    mask[i, L + j] = mode == DIFF or j <= i
+            qr = x["q"][b, h, :k].double()
+            ref = F.scaled_dot_product_attention(qr[None], keys[None], vals[None], attn_mask=mask[None],
+                                                 scale=1.0 / np.sqrt(D))[0]
+            s = (qr @ keys.T) / np.sqrt(D)
+            ref_lse = torch.logsumexp(s.masked_fill(~mask, float("-inf")), dim=1)
+            np.testing.assert_allclose(out[b, h, :k], ref.numpy(), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[b, h, :k], ref_lse.numpy(), rtol=0, atol=1e-12)
+            assert np.isnan(out[b, h, k:]).all() and np.isnan(lse[b, h, k:]).all()
+
+
+def test_attention_ignores_dead_block_rows_and_keys():
+    """Rows and keys past k_b may hold anything: the live rows do not change."""
+    B, Hq, Hkv, K, D = 2, 2, 1, 8, 8
+    x = _case(B, Hq, Hkv, K, D, [5, 3], 7)
+    kl = torch.tensor([3, 5], dtype=torch.int32)
+    out, lse = oracle.block_attention_dyn(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"],
+                                          x["cache_len"], kl, VERIFY)
+    y = {n: t.clone() for n, t in x.items()}
+    for b, k in enumerate(kl.tolist()):
+        y["q"][b, :, k:] = 100.0
+        y["k_blk"][b, :, k:] = -50.0
+        y["v_blk"][b, :, k:] = 1e4
+    out2, lse2 = oracle.block_attention_dyn(y["q"], y["k_blk"], y["v_blk"], y["k_cache"], y["v_cache"],
+                                            y["cache_len"], kl, VERIFY)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_lengths_are_clamped():
+    np.testing.assert_array_equal(oracle.live_lengths([-3, 0, 1, 7, 9, 40], 9), [1, 1, 1, 7, 9, 9])
+
+
+def _greedy_scan(logits, cand, k):
+    """Greedy rule written out: first-index argmax per row, first mismatch."""
+    am = []
+    for i in range(k):
+        row = logits[i]
+        best = 0
+        for v in range(1, len(row)):
+            if row[v] > row[best]:
+                best = v
+        am.append(best)
+    a = 0
+    while a < k and cand[a] == am[a]:
+        a += 1
+    return a, am, (am[a] if a < k else -1)
+
+
+def test_greedy_consensus_matches_a_written_out_scan():
+    rng = np.random.default_rng(5)
+    B, K, V = 5, 7, 11
+    logits = rng.normal(size=(B, K, V))
+    am_true = logits.argmax(axis=2)
+    cand = am_true.copy()
+    cand[0, 2] = (cand[0, 2] + 1) % V     # mismatch inside the live block
+    cand[1, 5] = (cand[1, 5] + 1) % V     # mismatch past k_b = 3: must not count
+    cand[3, 0] = (cand[3, 0] + 1) % V     # mismatch at row 0
+    kl = [4, 3, 7, 1, 2]
+    acc, am, corr = oracle.greedy_consensus_dyn(logits, cand, kl)
+    for b in range(B):
+        a, m, c = _greedy_scan(logits[b], cand[b], kl[b])
+        assert acc[b] == a and corr[b] == c
+        assert list(am[b, :kl[b]]) == m and (am[b, kl[b]:] == -1).all()
+    assert list(acc) == [2, 3, 7, 0, 2]
+    assert list(corr[[1, 2, 4]]) == [-1, -1, -1]
+
+
+def _probs(rng, B, K, V):
+    z = rng.normal(size=(B, K, V)) * 2.0
+    p = np.exp(z - z.max(axis=2, keepdims=True))
+    return (p / p.sum(axis=2, keepdims=True)).astype(np.float32)
+
+
+def test_sampler_reads_no_dead_row_and_uses_the_last_uniform():
+    rng = np.random.default_rng(11)
+    B, K, V = 6, 5, 13
+    P, Q = _probs(rng, B, K, V), _probs(rng, B, K, V)
+    cand = rng.integers(0, V, size=(B, K))
+    U = (rng.integers(0, 2 ** 24, size=(B, K + 1)) / 2 ** 24).astype(np.float32)
+    kl = [1, 2, 3, 5, 4, 2]
+    acc, corr = oracle.sample_consensus_dyn(P, Q, cand, U, kl)
+    # dead rows, their candidates and their accept uniforms changed: same result
+    P2, Q2, c2, U2 = P.copy(), Q.copy(), cand.copy(), U.copy()
+    for b, k in enumerate(kl):
+        P2[b, k:] = 1.0 / V
+        Q2[b, k:] = 0.5
+        c2[b, k:] = 0
+        U2[b, k:K] = 0.0
+    acc2, corr2 = oracle.sample_consensus_dyn(P2, Q2, c2, U2, kl)
+    np.testing.assert_array_equal(acc, acc2)
+    np.testing.assert_array_equal(corr, corr2)
+    assert (acc <= np.array(kl)).all()
+    # the residual draw moves with u_K, not with u_{k_b}
+    U3 = U.copy()
+    U3[:, K] = 1.0 - U3[:, K]
+    _, corr3 = oracle.sample_consensus_dyn(P, Q, cand, U3, kl)
+    rejected = acc < np.array(kl)
+    assert rejected.any()
+    assert (corr3[rejected] != corr[rejected]).any()
+
+
+def test_sampler_accepts_the_whole_live_block_when_every_test_passes():
+    rng = np.random.default_rng(2)
+    B, K, V = 4, 6, 9
+    P = _probs(rng, B, K, V)
+    cand = P.argmax(axis=2)
+    U = np.zeros((B, K + 1), dtype=np.float32)   # u = 0 < p/q: every live test passes
+    kl = [1, 3, 6, 2]
+    acc, corr = oracle.sample_consensus_dyn(P, P, cand, U, kl)
+    assert list(acc) == kl and (corr == -1).all()
+    # one failing test at row k_b - 1 (q = 2p there, u just below 1)
+    P2 = P.copy()
+    Qm = P.copy()
+    U2 = U.copy()
+    for b, k in enumerate(kl):
+        U2[b, k - 1] = np.float32(1.0 - 2.0 ** -24)
+        Qm[b, k - 1, cand[b, k - 1]] = min(1.0, 2.0 * P2[b, k - 1, cand[b, k - 1]])
+    acc2, corr2 = oracle.sample_consensus_dyn(P2, Qm, cand, U2, kl)
+    assert list(acc2) == [k - 1 for k in kl]
+    assert (corr2 >= 0).all()
+
+
+def test_sampler_with_the_full_block_is_the_static_sampler():
+    rng = np.random.default_rng(4)
+    B, K, V = 3, 4, 7
+    P, Q = _probs(rng, B, K, V), _probs(rng, B, K, V)
+    cand = rng.integers(0, V, size=(B, K))
+    U = (rng.integers(0, 2 ** 24, size=(B, K + 1)) / 2 ** 24).astype(np.float32)
+    a1, c1 = oracle.sample_consensus_dyn(P, Q, cand, U, [K] * B)
+    a2, c2 = oracle.sample_consensus(P, Q, cand, U)
+    np.testing.assert_array_equal(a1, a2)
+    np.testing.assert_array_equal(c1, c2)
+
+
+# (a, k) -> k' with K = 32, k_min = 2 (R30), worked out by hand
+RULE = [
+    (8, 8, 16), (32, 32, 32), (20, 32, 32), (15, 32, 16), (16, 32, 32), (14, 32, 16), (0, 32, 16),
+    (3, 8, 4), (4, 8, 8), (0, 2, 2), (1, 2, 2), (2, 2, 4), (0, 3, 2), (2, 3, 3), (3, 3, 6),
+    (0, 5, 3), (1, 5, 3), (2, 5, 5), (16, 16, 32), (31, 32, 32),
+]
+
+
+@pytest.mark.parametrize("a,k,nk", RULE)
+def test_block_length_rule(a, k, nk):
+    assert oracle.next_block_len(a, k, 32, 2) == nk
+
+
+def test_block_length_rule_floor_and_cap():
+    assert oracle.next_block_len(0, 4, 32, 4) == 4      # never below k_min
+    assert oracle.next_block_len(0, 1, 32, 1) == 1
+    assert oracle.next_block_len(1, 1, 32, 1) == 2
+    assert oracle.next_block_len(20, 20, 24, 1) == 24   # capped at K
+    assert oracle.next_block_len(1, 3, 8, 5) == 5       # a k below the floor is lifted
+
+
+def test_commit_hand_worked():
+    """One layer, one KV head, D = 8 (one 16-byte vector per row), K = 6,
+    max_len 16.  Block row i holds the value 100 + 10 b + i in every lane;
+    rows past k_b hold 0x7777, which must never reach the cache."""
+    n_layers, B, Hkv, K, D, max_len = 1, 4, 1, 6, 8, 16
+    kc = np.zeros((n_layers, B, Hkv, max_len, D), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    kb = np.zeros((n_layers, B, Hkv, K, D), dtype=np.uint16)
+    kl = [3, 3, 6, 2]
+    for b in range(B):
+        for i in range(K):
+            kb[:, b, :, i] = 100 + 10 * b + i if i < kl[b] else 0x7777
+    vb = kb + np.uint16(1000)
+    lens = [5, 5, 0, 15]
+    acc = [3, 1, 6, 2]        # b0: whole block; b1: one accepted; b2: whole block; b3: no room
+    corr = [-1, 77, -1, 55]
+    cand = np.arange(B * K).reshape(B, K) + 10
+    r = oracle.commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cand, kl, k_min=2)
+    # b0: k_b = 3, a = 3: rows 0..2 at 5..7, tokens cand[0..2], anchor cand[2]
+    assert r["cache_len"][0] == 8 and r["n_tokens"][0] == 3
+    assert list(r["tokens"][0]) == [10, 11, 12, -1, -1, -1] and r["next_anchor"][0] == 12
+    assert (r["k_cache"][0, 0, 0, 5:8, 0] == [100, 101, 102]).all()
+    assert (r["k_cache"][0, 0, 0, 8:, 0] == 0).all()
+    assert r["blk_len"][0] == 6
+    # b1: a = 1 < k_b: rows 0..1 at 5..6, tokens cand[0], 77; anchor 77
+    assert r["cache_len"][1] == 7 and list(r["tokens"][1][:2]) == [16, 77] and r["next_anchor"][1] == 77
+    assert (r["v_cache"][0, 1, 0, 5:7, 0] == [1110, 1111]).all() and (r["v_cache"][0, 1, 0, 7:, 0] == 0).all()
+    assert r["blk_len"][1] == 3          # 2 (a + 1) = 4 > 3: keep
+    # b2: k_b = K = 6, a = 6: the static commit of the whole block
+    assert r["cache_len"][2] == 6 and r["next_anchor"][2] == cand[2, 5] and r["blk_len"][2] == 6
+    # b3: 15 + 2 > 16: refused, nothing written, length and block length kept
+    assert r["cache_len"][3] == 15 and r["n_tokens"][3] == 0 and r["blk_len"][3] == 2
+    assert (r["k_cache"][0, 3] == 0).all()
+    assert not (r["k_cache"] == 0x7777).any() and not (r["v_cache"] == 0x7777 + 1000).any()
