@@ -45,9 +45,9 @@ import math
 
 import numpy as np
 
-from .attention import _as_f64, _as_int, block_attention
+from .attention import MASK_DIFF_BIDIR, MASK_VERIFY_CAUSAL, _as_f64, _as_int, block_attention
 from .consensus import _np, greedy_consensus, sample_consensus
-from .cycle import _bits, _ints, commit_block
+from .cycle import _bits, _ints, bits_to_bf16, commit_block
 
 
 def live_lengths(blk_len, block_k: int) -> np.ndarray:
@@ -164,3 +164,42 @@ def commit_block_dyn(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, corr
             new_k[b] = next_block_len(int(acc[b]), k, K, int(k_min))
     return {"k_cache": kc, "v_cache": vc, "cache_len": new_len, "next_anchor": next_anchor,
             "tokens": tokens, "n_tokens": n_tokens, "blk_len": new_k}
+
+
+def decode_cycles_dyn(k_cache, v_cache, cache_len, blk_len, k_min: int, cycles, scale=None,
+                      keep_attention=True):
+    """``oracle.cycle.decode_cycles`` with a block length per sequence: each
+    cycle runs both views' attention, the greedy consensus and the commit over
+    each sequence's first k_b positions, and the commit's block-length rule
+    sets the next cycle's k_b (R29, R30).
+
+    Returns (records, state) as ``decode_cycles``; every record also holds
+    ``blk_len_in`` (the lengths the cycle ran with) and ``blk_len`` (the next
+    ones), attention outputs NaN past k_b, and ``state`` the final ``blk_len``.
+    """
+    kc, vc = _bits(k_cache), _bits(v_cache)
+    lens = _ints(cache_len).copy()
+    K = _as_f64(cycles[0]["diff"][0][0]).shape[2]
+    kl = live_lengths(blk_len, K)
+    records = []
+    for cyc in cycles:
+        rec = {"cache_len_in": lens.copy(), "blk_len_in": kl.copy()}
+        kc_t, vc_t = bits_to_bf16(kc), bits_to_bf16(vc)
+        if keep_attention:
+            rec["diff_out"], rec["verify_out"] = [], []
+            for layer, (dv, vv) in enumerate(zip(cyc["diff"], cyc["verify"])):
+                od, _ = block_attention_dyn(dv[0], dv[1], dv[2], kc_t[layer], vc_t[layer], lens, kl,
+                                            MASK_DIFF_BIDIR, scale)
+                ov, _ = block_attention_dyn(vv[0], vv[1], vv[2], kc_t[layer], vc_t[layer], lens, kl,
+                                            MASK_VERIFY_CAUSAL, scale)
+                rec["diff_out"].append(od)
+                rec["verify_out"].append(ov)
+        acc, _, corr = greedy_consensus_dyn(cyc["logits"], cyc["cand"], kl)
+        kb = np.stack([_bits(vv[1]) for vv in cyc["verify"]])
+        vb = np.stack([_bits(vv[2]) for vv in cyc["verify"]])
+        res = commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cyc["cand"], kl, k_min)
+        kc, vc, lens, kl = res["k_cache"], res["v_cache"], res["cache_len"], res["blk_len"]
+        rec.update(accept_len=acc, correction=corr, cache_len=lens.copy(), blk_len=kl.copy(),
+                   next_anchor=res["next_anchor"], tokens=res["tokens"], n_tokens=res["n_tokens"])
+        records.append(rec)
+    return records, {"k_cache": kc, "v_cache": vc, "cache_len": lens, "blk_len": kl}

@@ -239,3 +239,54 @@ def test_commit_hand_worked():
     assert r["cache_len"][3] == 15 and r["n_tokens"][3] == 0 and r["blk_len"][3] == 2
     assert (r["k_cache"][0, 3] == 0).all()
     assert not (r["k_cache"] == 0x7777).any() and not (r["v_cache"] == 0x7777 + 1000).any()
+
+
+def _cycles(w, n, rate, seed):
+    from synth import cycle_inputs
+    sets = cycle_inputs(w, n, accept_rate=rate, seed_offset=seed)
+    shape = (w.layers, w.batch, w.n_kv_heads, w.capacity, w.head_dim)
+    kc = torch.randn(shape, generator=torch.Generator().manual_seed(seed + 1)).to(torch.bfloat16)
+    vc = torch.randn(shape, generator=torch.Generator().manual_seed(seed + 2)).to(torch.bfloat16)
+    return sets, kc, vc
+
+
+def test_cycles_with_every_block_at_capacity_are_the_static_cycles():
+    """k_b = K and k_min = K: the rule can never move k, so every cycle is the
+    static (pinned) cycle."""
+    w = Workload("dyncyc", 2, 2, 4, 2, 16, 40, 4, 50, 4.0, 5, max_len=40 + 4 * 4)
+    sets, kc, vc = _cycles(w, 4, 0.6, 3)
+    L = torch.tensor([40, 9], dtype=torch.int32)
+    r1, s1 = oracle.decode_cycles(kc, vc, L, sets)
+    r2, s2 = oracle.decode_cycles_dyn(kc, vc, L, [4, 4], 4, sets)
+    for a, b in zip(r1, r2):
+        for n in ("accept_len", "correction", "cache_len", "next_anchor", "tokens", "n_tokens"):
+            np.testing.assert_array_equal(a[n], b[n])
+        for x, y in zip(a["diff_out"] + a["verify_out"], b["diff_out"] + b["verify_out"]):
+            np.testing.assert_array_equal(x, y)
+        assert b["blk_len"].tolist() == [4, 4]
+    np.testing.assert_array_equal(s1["k_cache"], s2["k_cache"])
+    np.testing.assert_array_equal(s1["cache_len"], s2["cache_len"])
+
+
+def test_cycle_block_lengths_follow_the_rule_and_the_lengths_add_up():
+    w = Workload("dyncyc2", 1, 3, 2, 1, 16, 30, 8, 40, 4.0, 6, max_len=30 + 8 * 6)
+    sets, kc, vc = _cycles(w, 6, 0.7, 9)
+    recs, st = oracle.decode_cycles_dyn(kc, vc, [30, 0, 12], [8, 2, 5], 2, sets)
+    lens = np.array([30, 0, 12])
+    k = np.array([8, 2, 5])
+    for c, rec in enumerate(recs):
+        assert rec["blk_len_in"].tolist() == k.tolist()
+        a = rec["accept_len"]
+        # the planted first mismatch j*, cut at the block length
+        assert (a == np.minimum(sets[c]["j_star"].numpy(), k)).all()
+        n = a + (a < k)
+        assert rec["n_tokens"].tolist() == n.tolist()
+        lens = lens + n
+        assert rec["cache_len"].tolist() == lens.tolist()
+        k = np.array([oracle.next_block_len(int(a[b]), int(k[b]), 8, 2) for b in range(3)])
+        assert rec["blk_len"].tolist() == k.tolist()
+        for out in rec["verify_out"]:
+            for b in range(3):
+                assert np.isnan(out[b, :, rec["blk_len_in"][b]:]).all()
+                assert np.isfinite(out[b, :, :rec["blk_len_in"][b]]).all()
+    assert st["blk_len"].tolist() == k.tolist()
