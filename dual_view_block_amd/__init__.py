@@ -31,7 +31,8 @@ __all__ = [
     "PreparedCommit", "orthrus_kl_workspace_size", "orthrus_forward_kl", "PreparedForwardKL",
     "TrainAttnDesc", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd", "orthrus_block_attn_masked",
     "orthrus_topk_logprobs", "orthrus_tree_build", "orthrus_tree_masks", "orthrus_consensus_tree_greedy",
-    "orthrus_cache_commit_path", "orthrus_block_attn_noalloc",
+    "orthrus_cache_commit_path", "orthrus_block_attn_noalloc", "orthrus_block_attn_dyn",
+    "orthrus_consensus_greedy_dyn", "orthrus_consensus_sample_dyn", "orthrus_cache_commit_dyn",
 ]
 
 
@@ -166,10 +167,10 @@ class PreparedAttention:
     """
 
     def __init__(self, mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
-                 softmax_scale: float = 0.0, block_mask=None):
+                 softmax_scale: float = 0.0, block_mask=None, blk_len=None):
         _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len)
         self.desc = attn_desc(q, k_cache, softmax_scale)
-        self._keep = (q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace, block_mask)
+        self._keep = (q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace, block_mask, blk_len)
         nbytes = orthrus_attn_workspace_size(self.desc)
         if workspace.numel() < nbytes:
             raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")
@@ -191,6 +192,14 @@ class PreparedAttention:
             self._fn = lib.orthrus_block_attn_masked
             a = self._args
             self._args = (a[0],) + a[2:8] + (block_mask.data_ptr(),) + a[8:]
+            self._partial = self._merge = None
+        if blk_len is not None:  # dynamic block sizes: the whole call only
+            if block_mask is not None:
+                raise ValueError("a block length per sequence goes with the mode masks only")
+            _need(blk_len, "blk_len", torch.int32, (q.shape[0],), q.device)
+            self._fn = lib.orthrus_block_attn_dyn
+            a = self._args
+            self._args = a[:8] + (blk_len.data_ptr(),) + a[8:]
             self._partial = self._merge = None
 
     def __call__(self, stream_ptr: int) -> None:
@@ -214,7 +223,7 @@ class PreparedAttention:
 class PreparedGreedy:
     """A greedy-consensus call with every pointer resolved once."""
 
-    def __init__(self, logits, cand, accept_len, row_argmax, correction, workspace):
+    def __init__(self, logits, cand, accept_len, row_argmax, correction, workspace, blk_len=None):
         B, K, V = logits.shape
         dev = logits.device
         _need(logits, "logits", torch.float32, (B, K, V))
@@ -222,11 +231,16 @@ class PreparedGreedy:
         nbytes = orthrus_consensus_workspace_size(B, K, V)
         if workspace.numel() < nbytes:
             raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")
-        self._keep = (logits, cand, accept_len, row_argmax, correction, workspace)
-        self._fn = _lib.load().orthrus_consensus_greedy
+        self._keep = (logits, cand, accept_len, row_argmax, correction, workspace, blk_len)
+        lib = _lib.load()
+        self._fn = lib.orthrus_consensus_greedy
         self._args = (B, K, V, logits.data_ptr(), cand.data_ptr(), accept_len.data_ptr(),
                       row_argmax.data_ptr() if row_argmax is not None else None, correction.data_ptr(),
                       workspace.data_ptr(), workspace.numel())
+        if blk_len is not None:  # dynamic block sizes
+            _need(blk_len, "blk_len", torch.int32, (B,), dev)
+            self._fn = lib.orthrus_consensus_greedy_dyn
+            self._args = self._args[:5] + (blk_len.data_ptr(),) + self._args[5:]
 
     def __call__(self, stream_ptr: int) -> None:
         st = self._fn(*self._args, stream_ptr)
@@ -314,7 +328,7 @@ class PreparedCommit:
     ``orthrus_cache_commit``); calling it issues one C call on the stream."""
 
     def __init__(self, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand,
-                 next_anchor, tokens, n_tokens):
+                 next_anchor, tokens, n_tokens, blk_len=None, k_min: int = 1):
         self.desc = _check_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand)
         B, K, dev = self.desc.batch, self.desc.block_k, k_cache.device
         _need(next_anchor, "next_anchor", torch.int32, (B,), dev)
@@ -322,8 +336,14 @@ class PreparedCommit:
         _need(n_tokens, "n_tokens", torch.int32, (B,), dev)
         self._keep = (k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand,
                       next_anchor, tokens, n_tokens)
-        self._fn = _lib.load().orthrus_cache_commit
+        lib = _lib.load()
+        self._fn = lib.orthrus_cache_commit
         self._args = (ctypes.byref(self.desc),) + tuple(t.data_ptr() for t in self._keep)
+        if blk_len is not None:  # dynamic block sizes: the commit also advances blk_len
+            _need(blk_len, "blk_len", torch.int32, (B,), dev)
+            self._keep = self._keep + (blk_len,)
+            self._fn = lib.orthrus_cache_commit_dyn
+            self._args = self._args + (blk_len.data_ptr(), int(k_min))
 
     def __call__(self, stream_ptr: int) -> None:
         st = self._fn(*self._args, stream_ptr)
@@ -355,6 +375,102 @@ def orthrus_cache_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, 
         cache_len.data_ptr(), accept_len.data_ptr(), correction.data_ptr(), cand.data_ptr(),
         next_anchor.data_ptr(), tokens.data_ptr(), n_tokens.data_ptr(), _stream_ptr(stream))
     _lib.check("orthrus_cache_commit", st)
+    return next_anchor, tokens, n_tokens
+
+
+def orthrus_block_attn_dyn(q, k_blk, v_blk, k_cache, v_cache, cache_len, blk_len, mode: int, out=None, lse=None,
+                           workspace=None, softmax_scale: float = 0.0, want_lse: bool = True, stream=None):
+    """Block attention with a block length per sequence (int32 [B] on the
+    device): rows past a sequence's length are not written.  Returns
+    (out, lse or None) as ``orthrus_block_attn``."""
+    _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len)
+    desc = attn_desc(q, k_cache, softmax_scale)
+    dev = q.device
+    _need(blk_len, "blk_len", torch.int32, (q.shape[0],), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, tuple(q.shape), dev)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, tuple(q.shape[:3]), dev)
+    ws = _workspace(orthrus_attn_workspace_size(desc), dev, workspace)
+    st = _lib.load().orthrus_block_attn_dyn(
+        ctypes.byref(desc), int(mode), q.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), cache_len.data_ptr(), blk_len.data_ptr(), out.data_ptr(),
+        lse.data_ptr() if lse is not None else None, ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_block_attn_dyn", st)
+    return out, lse
+
+
+def orthrus_consensus_greedy_dyn(logits, cand, blk_len, accept_len=None, row_argmax=None, correction=None,
+                                 workspace=None, want_row_argmax: bool = True, stream=None):
+    """Greedy consensus over each sequence's first blk_len[b] rows; returns
+    (accept_len [B], row_argmax [B,K] (-1 past the block) or None, correction [B])."""
+    B, K, V = logits.shape
+    dev = logits.device
+    _need(logits, "logits", torch.float32, (B, K, V))
+    _need(cand, "cand", torch.int32, (B, K), dev)
+    _need(blk_len, "blk_len", torch.int32, (B,), dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if correction is None:
+        correction = torch.empty(B, dtype=torch.int32, device=dev)
+    if row_argmax is None and want_row_argmax:
+        row_argmax = torch.empty((B, K), dtype=torch.int32, device=dev)
+    ws = _workspace(orthrus_consensus_workspace_size(B, K, V), dev, workspace)
+    st = _lib.load().orthrus_consensus_greedy_dyn(
+        B, K, V, logits.data_ptr(), cand.data_ptr(), blk_len.data_ptr(), accept_len.data_ptr(),
+        row_argmax.data_ptr() if row_argmax is not None else None, correction.data_ptr(),
+        ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    _lib.check("orthrus_consensus_greedy_dyn", st)
+    return accept_len, row_argmax, correction
+
+
+def orthrus_consensus_sample_dyn(p_target, q_draft, cand, uniforms, blk_len, accept_len=None, correction=None,
+                                 workspace=None, stream=None):
+    """T>0 consensus over each sequence's first blk_len[b] rows; returns
+    (accept_len [B], correction [B])."""
+    B, K, V = p_target.shape
+    dev = p_target.device
+    _need(p_target, "p_target", torch.float32, (B, K, V))
+    _need(q_draft, "q_draft", torch.float32, (B, K, V), dev)
+    _need(cand, "cand", torch.int32, (B, K), dev)
+    _need(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+    _need(blk_len, "blk_len", torch.int32, (B,), dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if correction is None:
+        correction = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = _workspace(orthrus_consensus_workspace_size(B, K, V), dev, workspace)
+    st = _lib.load().orthrus_consensus_sample_dyn(
+        B, K, V, p_target.data_ptr(), q_draft.data_ptr(), cand.data_ptr(), uniforms.data_ptr(),
+        blk_len.data_ptr(), accept_len.data_ptr(), correction.data_ptr(), ws.data_ptr(), ws.numel(),
+        _stream_ptr(stream))
+    _lib.check("orthrus_consensus_sample_dyn", st)
+    return accept_len, correction
+
+
+def orthrus_cache_commit_dyn(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand, blk_len,
+                             k_min: int = 1, next_anchor=None, tokens=None, n_tokens=None, stream=None):
+    """``orthrus_cache_commit`` over each sequence's first blk_len[b] block
+    positions; blk_len is then advanced in place to the next cycle's lengths.
+    Returns (next_anchor [B], tokens [B, K], n_tokens [B])."""
+    desc = _check_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand)
+    B, K, dev = desc.batch, desc.block_k, k_cache.device
+    _need(blk_len, "blk_len", torch.int32, (B,), dev)
+    if next_anchor is None:
+        next_anchor = torch.empty(B, dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if n_tokens is None:
+        n_tokens = torch.empty(B, dtype=torch.int32, device=dev)
+    st = _lib.load().orthrus_cache_commit_dyn(
+        ctypes.byref(desc), k_cache.data_ptr(), v_cache.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
+        cache_len.data_ptr(), accept_len.data_ptr(), correction.data_ptr(), cand.data_ptr(),
+        next_anchor.data_ptr(), tokens.data_ptr(), n_tokens.data_ptr(), blk_len.data_ptr(), int(k_min),
+        _stream_ptr(stream))
+    _lib.check("orthrus_cache_commit_dyn", st)
     return next_anchor, tokens, n_tokens
 
 

@@ -37,7 +37,8 @@ EXPORTS = (
     "orthrus_kl_workspace_size", "orthrus_forward_kl", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd",
     "orthrus_block_attn_masked", "orthrus_topk_workspace_size", "orthrus_topk_logprobs", "orthrus_tree_build",
     "orthrus_tree_masks", "orthrus_consensus_tree_greedy", "orthrus_cache_commit_path", "orthrus_status_string",
-    "orthrus_block_attn_noalloc",
+    "orthrus_block_attn_noalloc", "orthrus_block_attn_dyn", "orthrus_consensus_greedy_dyn",
+    "orthrus_consensus_sample_dyn", "orthrus_cache_commit_dyn",
 )
 # bytes of the device scratch behind orthrus_block_attn_noalloc
 ORTHRUS_NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -115,6 +116,10 @@ _SIGS = {
     "orthrus_cache_commit_path": (_I32, [ctypes.POINTER(CommitDesc)] + [_P] * 13),
     "orthrus_status_string": (ctypes.c_char_p, [_I32]),
     "orthrus_block_attn_noalloc": (_I32, [_DESC, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "orthrus_block_attn_dyn": (_I32, [_DESC, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "orthrus_consensus_greedy_dyn": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "orthrus_consensus_sample_dyn": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "orthrus_cache_commit_dyn": (_I32, [ctypes.POINTER(CommitDesc)] + [_P] * 12 + [_I32, _P]),
 }
 
 _lib = None

@@ -95,7 +95,8 @@ int device_cus() {
 orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q, const uint16_t* k_blk,
                         const uint16_t* v_blk, const uint16_t* k_cache, const uint16_t* v_cache,
                         const int32_t* cache_len, uint16_t* out, float* lse, void* workspace,
-                        size_t workspace_bytes, void* stream, int phases, const uint64_t* block_mask = nullptr) {
+                        size_t workspace_bytes, void* stream, int phases, const uint64_t* block_mask = nullptr,
+                        const int32_t* blk_len = nullptr) {
   const orthrus_status st = check_desc(d);
   if (st != ORTHRUS_OK) return st;
   if (mode != ORTHRUS_MASK_DIFF_BIDIR && mode != ORTHRUS_MASK_VERIFY_CAUSAL && mode != ORTHRUS_MASK_EXPLICIT)
@@ -114,6 +115,7 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
                        !aligned16(v_cache) || !aligned4(cache_len)))
     return ORTHRUS_ERR_MISALIGNED;
   if ((phases & 2) && (!aligned16(out) || (lse && !aligned4(lse)))) return ORTHRUS_ERR_MISALIGNED;
+  if (blk_len && !aligned4(blk_len)) return ORTHRUS_ERR_MISALIGNED;
   const AttnPlan plan = make_plan(d);
   if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
   const int cus = device_cus();
@@ -142,6 +144,7 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   a.causal = mode == ORTHRUS_MASK_VERIFY_CAUSAL ? 1 : 0;
   set_decode_strides(a);
   a.blk_mask = mode == ORTHRUS_MASK_EXPLICIT ? block_mask : nullptr;
+  a.blk_len = blk_len;
   a.splits = attn_launch_splits(plan, d->batch, d->n_kv_heads, d->max_len, cus);
   const int cap = env_int("ORTHRUS_MAX_SPLITS", a.splits);  // tuning: may only lower the split count
   if (cap < a.splits) a.splits = cap;
@@ -306,6 +309,70 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m) {
   return a < b + m && b < a + n;
 }
 
+orthrus_status run_greedy(int32_t batch, int32_t block_k, int32_t vocab, const float* logits, const int32_t* cand,
+                          const int32_t* blk_len, int32_t* accept_len, int32_t* row_argmax, int32_t* correction,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const orthrus_status st = check_consensus_sizes(batch, block_k, vocab);
+  if (st != ORTHRUS_OK) return st;
+  if (!logits || !cand || !accept_len || !correction || !workspace) return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(logits) || !aligned4(cand) || !aligned4(accept_len) || !aligned4(correction) ||
+      (row_argmax && !aligned4(row_argmax)) || (blk_len && !aligned4(blk_len)) || !aligned16(workspace))
+    return ORTHRUS_ERR_MISALIGNED;
+  const ConsensusPlan plan = make_consensus_plan(batch, block_k, vocab);
+  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+  const hipError_t e = launch_consensus_greedy(batch, block_k, vocab, logits, cand, blk_len, accept_len,
+                                               row_argmax, correction, workspace, plan,
+                                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status run_sample(int32_t batch, int32_t block_k, int32_t vocab, const float* p_target, const float* q_draft,
+                          const int32_t* cand, const float* uniforms, const int32_t* blk_len, int32_t* accept_len,
+                          int32_t* correction, void* workspace, size_t workspace_bytes, void* stream) {
+  const orthrus_status st = check_consensus_sizes(batch, block_k, vocab);
+  if (st != ORTHRUS_OK) return st;
+  if (!p_target || !q_draft || !cand || !uniforms || !accept_len || !correction || !workspace)
+    return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(p_target) || !aligned16(q_draft) || !aligned4(cand) || !aligned4(uniforms) ||
+      !aligned4(accept_len) || !aligned4(correction) || (blk_len && !aligned4(blk_len)) || !aligned16(workspace))
+    return ORTHRUS_ERR_MISALIGNED;
+  const ConsensusPlan plan = make_consensus_plan(batch, block_k, vocab);
+  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
+  const hipError_t e = launch_consensus_sample(batch, block_k, vocab, p_target, q_draft, cand, uniforms, blk_len,
+                                               accept_len, correction, workspace, plan,
+                                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
+orthrus_status run_commit(const orthrus_commit_desc* d, uint16_t* k_cache, uint16_t* v_cache,
+                          const uint16_t* k_blk, const uint16_t* v_blk, int32_t* cache_len,
+                          const int32_t* accept_len, const int32_t* correction, const int32_t* cand,
+                          int32_t* next_anchor, int32_t* tokens, int32_t* n_tokens, int32_t* blk_len, int k_min,
+                          void* stream) {
+  const orthrus_status st = check_commit_desc(d);
+  if (st != ORTHRUS_OK) return st;
+  if (!k_cache || !v_cache || !k_blk || !v_blk || !cache_len || !accept_len || !correction || !cand ||
+      !next_anchor || !tokens || !n_tokens)
+    return ORTHRUS_ERR_NULL_PTR;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_blk) || !aligned16(v_blk) ||
+      !aligned4(cache_len) || !aligned4(accept_len) || !aligned4(correction) || !aligned4(cand) ||
+      !aligned4(next_anchor) || !aligned4(tokens) || !aligned4(n_tokens) || (blk_len && !aligned4(blk_len)))
+    return ORTHRUS_ERR_MISALIGNED;
+  // the copies read the block while writing the cache: the two must not share memory
+  const size_t planes = (size_t)d->n_layers * d->batch * d->n_kv_heads;
+  const size_t cache_bytes = planes * d->max_len * d->head_dim * sizeof(uint16_t);
+  const size_t blk_bytes = planes * d->block_k * d->head_dim * sizeof(uint16_t);
+  if (overlaps(k_cache, cache_bytes, k_blk, blk_bytes) || overlaps(k_cache, cache_bytes, v_blk, blk_bytes) ||
+      overlaps(v_cache, cache_bytes, k_blk, blk_bytes) || overlaps(v_cache, cache_bytes, v_blk, blk_bytes) ||
+      overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
+    return ORTHRUS_ERR_BAD_SHAPE;
+  const hipError_t e = launch_cache_commit(d->n_layers, d->batch, d->n_kv_heads, d->head_dim, d->block_k,
+                                           d->max_len, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len,
+                                           correction, cand, next_anchor, tokens, n_tokens, blk_len, k_min,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace orthrus
 
@@ -329,6 +396,17 @@ orthrus_status orthrus_block_attn(const orthrus_attn_desc* d, int32_t mode, cons
                                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return run_attn(d, (int)mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
                   workspace_bytes, stream, 3);
+}
+
+orthrus_status orthrus_block_attn_dyn(const orthrus_attn_desc* d, int32_t mode, const uint16_t* q,
+                                      const uint16_t* k_blk, const uint16_t* v_blk, const uint16_t* k_cache,
+                                      const uint16_t* v_cache, const int32_t* cache_len, const int32_t* blk_len,
+                                      uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (mode != ORTHRUS_MASK_DIFF_BIDIR && mode != ORTHRUS_MASK_VERIFY_CAUSAL) return ORTHRUS_ERR_BAD_SHAPE;
+  if (!blk_len) return ORTHRUS_ERR_NULL_PTR;
+  return run_attn(d, (int)mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
+                  workspace_bytes, stream, 3, nullptr, blk_len);
 }
 
 orthrus_status orthrus_block_attn_masked(const orthrus_attn_desc* d, const uint16_t* q, const uint16_t* k_blk,
@@ -396,37 +474,34 @@ orthrus_status orthrus_consensus_greedy(int32_t batch, int32_t block_k, int32_t 
                                         const int32_t* cand, int32_t* accept_len, int32_t* row_argmax,
                                         int32_t* correction, void* workspace, size_t workspace_bytes,
                                         void* stream) {
-  const orthrus_status st = check_consensus_sizes(batch, block_k, vocab);
-  if (st != ORTHRUS_OK) return st;
-  if (!logits || !cand || !accept_len || !correction || !workspace) return ORTHRUS_ERR_NULL_PTR;
-  if (!aligned16(logits) || !aligned4(cand) || !aligned4(accept_len) || !aligned4(correction) ||
-      (row_argmax && !aligned4(row_argmax)) || !aligned16(workspace))
-    return ORTHRUS_ERR_MISALIGNED;
-  const ConsensusPlan plan = make_consensus_plan(batch, block_k, vocab);
-  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
-  const hipError_t e = launch_consensus_greedy(batch, block_k, vocab, logits, cand, accept_len, row_argmax,
-                                               correction, workspace, plan,
-                                               reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+  return run_greedy(batch, block_k, vocab, logits, cand, nullptr, accept_len, row_argmax, correction, workspace,
+                    workspace_bytes, stream);
+}
+
+orthrus_status orthrus_consensus_greedy_dyn(int32_t batch, int32_t block_k, int32_t vocab, const float* logits,
+                                            const int32_t* cand, const int32_t* blk_len, int32_t* accept_len,
+                                            int32_t* row_argmax, int32_t* correction, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  if (!blk_len) return ORTHRUS_ERR_NULL_PTR;
+  return run_greedy(batch, block_k, vocab, logits, cand, blk_len, accept_len, row_argmax, correction, workspace,
+                    workspace_bytes, stream);
 }
 
 orthrus_status orthrus_consensus_sample(int32_t batch, int32_t block_k, int32_t vocab, const float* p_target,
                                         const float* q_draft, const int32_t* cand, const float* uniforms,
                                         int32_t* accept_len, int32_t* correction, void* workspace,
                                         size_t workspace_bytes, void* stream) {
-  const orthrus_status st = check_consensus_sizes(batch, block_k, vocab);
-  if (st != ORTHRUS_OK) return st;
-  if (!p_target || !q_draft || !cand || !uniforms || !accept_len || !correction || !workspace)
-    return ORTHRUS_ERR_NULL_PTR;
-  if (!aligned16(p_target) || !aligned16(q_draft) || !aligned4(cand) || !aligned4(uniforms) ||
-      !aligned4(accept_len) || !aligned4(correction) || !aligned16(workspace))
-    return ORTHRUS_ERR_MISALIGNED;
-  const ConsensusPlan plan = make_consensus_plan(batch, block_k, vocab);
-  if (workspace_bytes < plan.ws_bytes) return ORTHRUS_ERR_WORKSPACE_TOO_SMALL;
-  const hipError_t e = launch_consensus_sample(batch, block_k, vocab, p_target, q_draft, cand, uniforms,
-                                               accept_len, correction, workspace, plan,
-                                               reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+  return run_sample(batch, block_k, vocab, p_target, q_draft, cand, uniforms, nullptr, accept_len, correction,
+                    workspace, workspace_bytes, stream);
+}
+
+orthrus_status orthrus_consensus_sample_dyn(int32_t batch, int32_t block_k, int32_t vocab, const float* p_target,
+                                            const float* q_draft, const int32_t* cand, const float* uniforms,
+                                            const int32_t* blk_len, int32_t* accept_len, int32_t* correction,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!blk_len) return ORTHRUS_ERR_NULL_PTR;
+  return run_sample(batch, block_k, vocab, p_target, q_draft, cand, uniforms, blk_len, accept_len, correction,
+                    workspace, workspace_bytes, stream);
 }
 
 orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_cache, uint16_t* v_cache,
@@ -434,28 +509,19 @@ orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_ca
                                     const int32_t* accept_len, const int32_t* correction,
                                     const int32_t* cand, int32_t* next_anchor, int32_t* tokens,
                                     int32_t* n_tokens, void* stream) {
-  const orthrus_status st = check_commit_desc(d);
-  if (st != ORTHRUS_OK) return st;
-  if (!k_cache || !v_cache || !k_blk || !v_blk || !cache_len || !accept_len || !correction || !cand ||
-      !next_anchor || !tokens || !n_tokens)
-    return ORTHRUS_ERR_NULL_PTR;
-  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_blk) || !aligned16(v_blk) ||
-      !aligned4(cache_len) || !aligned4(accept_len) || !aligned4(correction) || !aligned4(cand) ||
-      !aligned4(next_anchor) || !aligned4(tokens) || !aligned4(n_tokens))
-    return ORTHRUS_ERR_MISALIGNED;
-  // the copies read the block while writing the cache: the two must not share memory
-  const size_t planes = (size_t)d->n_layers * d->batch * d->n_kv_heads;
-  const size_t cache_bytes = planes * d->max_len * d->head_dim * sizeof(uint16_t);
-  const size_t blk_bytes = planes * d->block_k * d->head_dim * sizeof(uint16_t);
-  if (overlaps(k_cache, cache_bytes, k_blk, blk_bytes) || overlaps(k_cache, cache_bytes, v_blk, blk_bytes) ||
-      overlaps(v_cache, cache_bytes, k_blk, blk_bytes) || overlaps(v_cache, cache_bytes, v_blk, blk_bytes) ||
-      overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
-    return ORTHRUS_ERR_BAD_SHAPE;
-  const hipError_t e = launch_cache_commit(d->n_layers, d->batch, d->n_kv_heads, d->head_dim, d->block_k,
-                                           d->max_len, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len,
-                                           correction, cand, next_anchor, tokens, n_tokens,
-                                           reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
+  return run_commit(d, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand, next_anchor,
+                    tokens, n_tokens, nullptr, 1, stream);
+}
+
+orthrus_status orthrus_cache_commit_dyn(const orthrus_commit_desc* d, uint16_t* k_cache, uint16_t* v_cache,
+                                        const uint16_t* k_blk, const uint16_t* v_blk, int32_t* cache_len,
+                                        const int32_t* accept_len, const int32_t* correction,
+                                        const int32_t* cand, int32_t* next_anchor, int32_t* tokens,
+                                        int32_t* n_tokens, int32_t* blk_len, int32_t k_min, void* stream) {
+  if (!blk_len) return ORTHRUS_ERR_NULL_PTR;
+  if (d && (k_min < 1 || k_min > d->block_k)) return ORTHRUS_ERR_BAD_SHAPE;
+  return run_commit(d, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand, next_anchor,
+                    tokens, n_tokens, blk_len, k_min, stream);
 }
 
 size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, int32_t dtype) {

@@ -76,6 +76,14 @@ __device__ __forceinline__ int seq_len(const AttnArgs& a, int b) {
   return L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
 }
 
+// Live block length of sequence b (dynamic block size): its first k_b block
+// positions are the block; block_k when no per-sequence length is given.
+__device__ __forceinline__ int live_k(const AttnArgs& a, int b) {
+  if (a.blk_len == nullptr) return a.block_k;
+  const int k = a.blk_len[b];
+  return k < 1 ? 1 : (k > a.block_k ? a.block_k : k);
+}
+
 __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int split, int S) {
   SplitRange r;
   const int L = seq_len(a, b);
@@ -237,11 +245,7 @@ __device__ __forceinline__ float row_reduce(float v, Op op) {
   return v;
 }
 
-// Merge of one output row (two at D = 64, one per half-wave) from the S <= SMAX
-// partials of group grp: every lane loads the row's two values of each split
-// and the statistics of splits j, j + LPR, ... in one memory round trip, the
-// row's maximum and weight sum are reduced across its lanes, and the values
-// are summed in split order.
+// The merge itself (described above the lane reductions).
 template <int D, int SMAX>
 __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p, int grp, int row, int row_end) {
   constexpr int LPR = D / 2;                  // lanes per row
@@ -299,12 +303,14 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
     acc0 = fmaf(ws, __uint_as_float(v[s] << 16), acc0);
     acc1 = fmaf(ws, __uint_as_float(v[s] & 0xFFFF0000u), acc1);
   }
-  if (myrow < row_end) {
-    const int rg = grp % p.row_groups;
-    const int r = rg * p.rows_per_wg + myrow;  // row inside the (b, g) group: head_in_group*K + i
-    if (r < p.rows) {
-      const int bg = grp / p.row_groups;
-      const int b = bg / a.n_kv_heads, h = (bg % a.n_kv_heads) * a.group + r / a.block_k, i = r % a.block_k;
+  // rows past the live block length (a block shorter than block_k) were read
+  // but are not written
+  const int bg = grp / p.row_groups, rg = grp % p.row_groups;
+  const int kb = __builtin_amdgcn_readfirstlane(live_k(a, bg / a.n_kv_heads));  // one group per wave
+  const int r = rg * p.rows_per_wg + myrow;  // row inside the (b, g) group: head_in_group*kb + i
+  if (myrow < row_end && r < a.group * kb) {
+    {
+      const int b = bg / a.n_kv_heads, h = (bg % a.n_kv_heads) * a.group + r / kb, i = r % kb;
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       const uint32_t o = (uint32_t)to_bf16_bits(acc0 * inv) | ((uint32_t)to_bf16_bits(acc1 * inv) << 16);
       *reinterpret_cast<uint32_t*>(a.out + b * a.o_bs + h * a.o_hs + (long long)i * D + 2 * j) = o;
@@ -348,16 +354,20 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   const int qb = w >> 1;  // query block
   const int kh = w & 1;   // key half of every tile
   const int half = lane >> 5;
-  const bool active = qb < NQB;
-  const int R = plan.rows;
+  // block_k rows per q head in memory; kb of them live (the rows are packed
+  // h * kb + i), R live rows per (sequence, KV head)
   const int K = a.block_k;
+  const int kb = __builtin_amdgcn_readfirstlane(live_k(a, b));  // b is the work-group's sequence
+  const int R = a.group * kb;
+  if (rg * plan.rows_per_wg >= R) return;  // no live row in this row group
+  const bool active = qb < NQB && rg * plan.rows_per_wg + qb * 32 < R;
   const int g = bg % a.n_kv_heads;
   const long long q_grp = b * a.q_bs + (long long)g * a.group * a.q_hs;
   const long long o_grp = b * a.o_bs + (long long)g * a.group * a.o_hs;
   const long long l_grp = b * a.l_bs + (long long)g * a.group * a.l_hs;
   const int wrow = qb * 32 + (lane & 31);
   const int qrow = rg * plan.rows_per_wg + wrow;
-  const int qrow_i = qrow % K;
+  const int qrow_i = qrow % kb;
 
   // ---- tile copies: thread tid moves 16-byte chunks n = tid + c*512 of the K
   // tile and of the V tile (row n / DCH, chunk n % DCH, so consecutive lanes
@@ -414,8 +424,10 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
       *reinterpret_cast<u32x4*>(sb + dv[c]) = r[CPT + c];
     }
   };
+  // valid keys of tile t (block tiles: the live block keys; <= 0 for a block
+  // tile wholly past them, whose loads still stay inside the block buffer)
   auto tile_valid = [&](int t) __attribute__((always_inline)) {
-    return t < sr.nblk ? min(kTileKeys, K - (sr.blk0 + t) * kTileKeys)
+    return t < sr.nblk ? min(kTileKeys, kb - (sr.blk0 + t) * kTileKeys)
                        : min(kTileKeys, sr.kend - (sr.kstart + (t - sr.nblk) * kTileKeys));
   };
 
@@ -482,7 +494,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     int rel = lim - 4 * half - 32 * kh;
     asm volatile("" : "+v"(rel));
     if (EXPL && block_tile) {
-      const int mrow = min(qrow, R - 1) % K;
+      const int mrow = min(qrow, R - 1) % kb;
       const uint32_t em = (uint32_t)(a.blk_mask[(size_t)b * K + mrow] >> (4 * half + 32 * kh));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -519,7 +531,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   bf16x8 qf[NDS];
   {
     const int row = min(qrow, R - 1);
-    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + q_grp + (row / K) * a.q_hs + (long long)(row % K) * D);
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q + q_grp + (row / kb) * a.q_hs + (long long)(row % kb) * D);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) qf[ds] = active ? qp[2 * ds + half] : bf16x8{};
   }
@@ -638,14 +650,14 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     if (one_split) {
       const int gr = rg * plan.rows_per_wg + r;
       if (gr < R)
-        *reinterpret_cast<u32x4*>(a.out + o_grp + (gr / K) * a.o_hs + (long long)(gr % K) * D + ch * 8) = v;
+        *reinterpret_cast<u32x4*>(a.out + o_grp + (gr / kb) * a.o_hs + (long long)(gr % kb) * D + ch * 8) = v;
     } else {
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.ws_acc + (slot * plan.rows_per_wg + r) * D + ch * 8));
     }
   }
   if (active && kh == 0 && half == 0) {
     if (one_split) {
-      if (a.lse != nullptr && qrow < R) a.lse[l_grp + (qrow / K) * a.l_hs + qrow % K] = (m_out + log2f(l_out)) * kLn2;
+      if (a.lse != nullptr && qrow < R) a.lse[l_grp + (qrow / kb) * a.l_hs + qrow % kb] = (m_out + log2f(l_out)) * kLn2;
     } else {
       __builtin_nontemporal_store(m_out, a.ws_ml + (slot * plan.rows_per_wg + wrow) * 2);
       __builtin_nontemporal_store(l_out, a.ws_ml + (slot * plan.rows_per_wg + wrow) * 2 + 1);
@@ -780,11 +792,14 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_ragged_kernel(AttnAr
     }
     M = Mn;
   }
+  // rows past the live block length (a block shorter than block_k) were
+  // folded from unwritten partials and are not written
   const int rg = grp % plan.row_groups;
-  const int r = rg * plan.rows_per_wg + row;
-  if (r >= plan.rows) return;
   const int bg = grp / plan.row_groups;
-  const int b = bg / a.n_kv_heads, h = (bg % a.n_kv_heads) * a.group + r / a.block_k, i = r % a.block_k;
+  const int kb = live_k(a, bg / a.n_kv_heads);
+  const int r = rg * plan.rows_per_wg + row;
+  if (r >= a.group * kb) return;
+  const int b = bg / a.n_kv_heads, h = (bg % a.n_kv_heads) * a.group + r / kb, i = r % kb;
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   u32x4 o;
 #pragma unroll

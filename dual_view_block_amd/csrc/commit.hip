@@ -32,6 +32,10 @@ struct CommitArgs {
   int32_t* next_anchor;
   int32_t* tokens;
   int32_t* n_tokens;
+  // dynamic block sizes: NULL, or the live block length per sequence
+  // (clamped to [1, block_k]), rewritten in place with the next cycle's
+  int32_t* blk_len;
+  int k_min;       // floor of the block-length rule
   int planes;      // n_layers * B * Hkv
   int batch, n_kv_heads, head_dim, block_k, max_len;
 };
@@ -46,12 +50,32 @@ __device__ __forceinline__ int commit_rows(int t, int a, int K, int max_len) {
   return t <= max_len - r ? r : -1;
 }
 
+// Block length of sequence b in this cycle: its first k_b positions.
+__device__ __forceinline__ int live_k(const CommitArgs& a, int b) {
+  if (a.blk_len == nullptr) return a.block_k;
+  const int k = a.blk_len[b];
+  return k < 1 ? 1 : (k > a.block_k ? a.block_k : k);
+}
+
+// The next cycle's block length after a committed cycle that accepted a of k
+// (Orthrus paper notes §7.4, §9.6: a large block where acceptance is high, a
+// small one where it is low): double it when the whole block was accepted,
+// halve it (rounding up) when at most half of it was used -- the accepted
+// candidates plus the correction -- and keep it otherwise; never below k_min
+// or above the capacity.
+__device__ __forceinline__ int next_block_len(int a, int k, int cap, int k_min) {
+  int nk = k;
+  if (a == k) nk = 2 * k;
+  else if (2 * (a + 1) <= k) nk = max((k + 1) / 2, k_min);
+  return min(max(nk, k_min), cap);
+}
+
 // grid.x = planes, grid.y = 2 (keys, values)
 __global__ __launch_bounds__(kCommitThreads) void commit_rows_kernel(const CommitArgs a) {
   const int plane = blockIdx.x;
   const int b = (plane / a.n_kv_heads) % a.batch;
   const int t = a.cache_len[b];
-  const int r = commit_rows(t, a.accept_len[b], a.block_k, a.max_len);
+  const int r = commit_rows(t, a.accept_len[b], live_k(a, b), a.max_len);
   if (r <= 0) return;
   const bool vals = blockIdx.y != 0;
   const uint16_t* src = (vals ? a.v_blk : a.k_blk) + (size_t)plane * a.block_k * a.head_dim;
@@ -66,22 +90,24 @@ __global__ __launch_bounds__(kCommitThreads) void commit_rows_kernel(const Commi
 __global__ __launch_bounds__(kCommitThreads) void commit_state_kernel(const CommitArgs a) {
   const int b = blockIdx.x * kCommitThreads + threadIdx.x;
   if (b >= a.batch) return;
-  const int K = a.block_k;
+  const int K = a.block_k;  // row stride of cand and tokens
+  const int kb = live_k(a, b);
   const int t = a.cache_len[b];
   const int acc = a.accept_len[b];
-  const int r = commit_rows(t, acc, K, a.max_len);
+  const int r = commit_rows(t, acc, kb, a.max_len);
   int32_t* tok = a.tokens + (size_t)b * K;
   if (r < 0) {
     for (int i = 0; i < K; ++i) tok[i] = -1;
     a.n_tokens[b] = 0;
     a.next_anchor[b] = -1;
+    if (a.blk_len != nullptr) a.blk_len[b] = kb;
     return;
   }
   const int32_t* cd = a.cand + (size_t)b * K;
   for (int i = 0; i < acc; ++i) tok[i] = cd[i];
   int last = acc > 0 ? cd[acc - 1] : -1;
   int n = acc;
-  if (acc < K) {
+  if (acc < kb) {
     last = a.correction[b];
     tok[n++] = last;
   }
@@ -89,6 +115,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_state_kernel(const Comm
   a.n_tokens[b] = n;
   a.next_anchor[b] = last;
   a.cache_len[b] = t + r;
+  if (a.blk_len != nullptr) a.blk_len[b] = next_block_len(acc, kb, K, a.k_min);
 }
 
 // ---- commit of an accepted tree path: rows path[0..a] (root first) of the
@@ -196,8 +223,11 @@ hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head
                                int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,
                                const uint16_t* v_blk, int32_t* cache_len, const int32_t* accept_len,
                                const int32_t* correction, const int32_t* cand, int32_t* next_anchor,
-                               int32_t* tokens, int32_t* n_tokens, hipStream_t stream) {
+                               int32_t* tokens, int32_t* n_tokens, int32_t* blk_len, int k_min,
+                               hipStream_t stream) {
   CommitArgs a{};
+  a.blk_len = blk_len;
+  a.k_min = k_min;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.k_blk = k_blk;

@@ -70,6 +70,11 @@ struct AttnArgs {
   // Explicit block masks (block_k <= 64): bit j of blk_mask[b*block_k + i]
   // set = block key j visible to block row i; NULL = the mode's mask.
   const uint64_t* blk_mask;
+  // Live block length per sequence (device, [batch]): sequence b's block is
+  // its first k_b = clamp(blk_len[b], 1, block_k) positions; its rows are
+  // packed h*k_b + i and rows i >= k_b are neither computed nor written.
+  // NULL = block_k for every sequence.
+  const int32_t* blk_len;
 };
 
 // Contiguous decode layouts: q/out [B,Hq,K,D], lse [B,Hq,K], blocks
@@ -87,6 +92,7 @@ inline void set_decode_strides(AttnArgs& a) {
   a.len_step = 0;
   a.rank_blocks = 0;
   a.blk_mask = nullptr;
+  a.blk_len = nullptr;
 }
 
 // Splits a launch uses on a device with `cus` compute units.
@@ -106,14 +112,16 @@ struct ConsensusPlan {
   size_t ws_bytes;
 };
 
+// blk_len: NULL, or the live block length per sequence (device, [batch]):
+// rows i >= clamp(blk_len[b], 1, block_k) are not part of sequence b's block.
 hipError_t launch_consensus_greedy(int batch, int block_k, int vocab, const float* logits,
-                                   const int32_t* cand, int32_t* accept_len,
+                                   const int32_t* cand, const int32_t* blk_len, int32_t* accept_len,
                                    int32_t* row_argmax, int32_t* correction, void* workspace,
                                    const ConsensusPlan& plan, hipStream_t stream);
 
 hipError_t launch_consensus_sample(int batch, int block_k, int vocab, const float* p_target,
                                    const float* q_draft, const int32_t* cand,
-                                   const float* uniforms, int32_t* accept_len,
+                                   const float* uniforms, const int32_t* blk_len, int32_t* accept_len,
                                    int32_t* correction, void* workspace,
                                    const ConsensusPlan& plan, hipStream_t stream);
 
@@ -142,12 +150,15 @@ hipError_t launch_train_bwd(const TrainBwdArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- commit
 // Row copies of the verified block into the cache, then the in-place state
-// update (two launches on `stream`).
+// update (two launches on `stream`).  blk_len: NULL, or the live block length
+// per sequence, which the state update replaces with the next cycle's
+// (floor k_min).
 hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head_dim, int block_k,
                                int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,
                                const uint16_t* v_blk, int32_t* cache_len, const int32_t* accept_len,
                                const int32_t* correction, const int32_t* cand, int32_t* next_anchor,
-                               int32_t* tokens, int32_t* n_tokens, hipStream_t stream);
+                               int32_t* tokens, int32_t* n_tokens, int32_t* blk_len, int k_min,
+                               hipStream_t stream);
 
 // ---------------------------------------------------------------- forward KL
 // Forward KL (and, if grad != NULL, its gradient) of `rows` logit rows: one

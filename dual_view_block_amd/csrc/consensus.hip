@@ -28,12 +28,23 @@ using namespace keys;
 
 constexpr int kThreads = 256;
 
+// Live block length of sequence b: blk_len[b] clamped to [1, block_k], or
+// block_k when no per-sequence lengths are given.
+__device__ __forceinline__ int live_k(const int32_t* blk_len, int b, int block_k) {
+  if (blk_len == nullptr) return block_k;
+  const int k = blk_len[b];
+  return k < 1 ? 1 : (k > block_k ? block_k : k);
+}
+
 // ---------------------------------------------------------------- greedy --
 __global__ __launch_bounds__(kThreads) void argmax_partial_kernel(const float* __restrict__ logits,
                                                                   int vocab, int chunk_len,
-                                                                  unsigned long long* part) {
+                                                                  unsigned long long* part, int block_k,
+                                                                  const int32_t* blk_len) {
   const int c = blockIdx.x;
   const size_t row = blockIdx.y;
+  // rows past the sequence's live block length are not needed
+  if (blk_len != nullptr && (int)(row % block_k) >= live_k(blk_len, (int)(row / block_k), block_k)) return;
   const int begin = c * chunk_len;
   const int end = min(vocab, begin + chunk_len);
   const float* rp = logits + row * (size_t)vocab;
@@ -100,23 +111,26 @@ __device__ __forceinline__ unsigned long long chunks_max(const unsigned long lon
 
 __global__ __launch_bounds__(64) void greedy_finalize_kernel(int block_k, int chunks,
                                                              const unsigned long long* part,
-                                                             const int32_t* cand, int32_t* accept_len,
-                                                             int32_t* row_argmax, int32_t* correction) {
+                                                             const int32_t* cand, const int32_t* blk_len,
+                                                             int32_t* accept_len, int32_t* row_argmax,
+                                                             int32_t* correction) {
   const int b = blockIdx.x;
+  const int kb = live_k(blk_len, b, block_k);  // rows [0, kb) are the block
   // rows in groups of 64 (one per lane); the first group with a mismatch ends the scan
-  int a = block_k, am_a = -1;
+  int a = kb, am_a = -1;
   for (int base = 0; base < block_k; base += 64) {
     const int i = base + (int)threadIdx.x;
     int am = -1;
     bool mismatch = false;
-    if (i < block_k) {
+    if (i >= kb && i < block_k && row_argmax != nullptr) row_argmax[(size_t)b * block_k + i] = -1;
+    if (i < kb) {
       const unsigned long long m = chunks_max(part + ((size_t)b * block_k + i) * chunks, chunks);
       am = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
       mismatch = cand[(size_t)b * block_k + i] != am;
       if (row_argmax != nullptr) row_argmax[(size_t)b * block_k + i] = am;
     }
     const unsigned long long mm = __ballot(mismatch);
-    if (mm && a == block_k) {
+    if (mm && a == kb) {
       const int lane = __builtin_ctzll(mm);
       a = base + lane;
       am_a = __shfl(am, lane);
@@ -124,7 +138,7 @@ __global__ __launch_bounds__(64) void greedy_finalize_kernel(int block_k, int ch
   }
   if (threadIdx.x == 0) {
     accept_len[b] = a;
-    correction[b] = a < block_k ? am_a : -1;
+    correction[b] = a < kb ? am_a : -1;
   }
 }
 
@@ -184,14 +198,16 @@ __global__ __launch_bounds__(64) void sample_accept_kernel(int block_k, int voca
                                                            const float* __restrict__ q,
                                                            const int32_t* __restrict__ cand,
                                                            const float* __restrict__ uniforms,
+                                                           const int32_t* blk_len,
                                                            int32_t* accept_len, int32_t* correction,
                                                            int32_t* ws_a) {
   const int b = blockIdx.x;
-  int a = block_k;
-  for (int base = 0; base < block_k && a == block_k; base += 64) {  // groups of 64 rows
+  const int kb = live_k(blk_len, b, block_k);  // rows [0, kb) are the block
+  int a = kb;
+  for (int base = 0; base < kb && a == kb; base += 64) {  // groups of 64 rows
     const int i = base + (int)threadIdx.x;
     bool reject = false;
-    if (i < block_k) {
+    if (i < kb) {
       const size_t row = (size_t)b * block_k + i;
       const int c = cand[row];
       const bool valid = c >= 0 && c < vocab;
@@ -206,8 +222,8 @@ __global__ __launch_bounds__(64) void sample_accept_kernel(int block_k, int voca
   }
   if (threadIdx.x == 0) {
     accept_len[b] = a;
-    ws_a[b] = a;
-    if (a >= block_k) correction[b] = -1;
+    ws_a[b] = a < kb ? a : block_k;  // block_k: no residual draw
+    if (a >= kb) correction[b] = -1;
   }
 }
 
@@ -390,19 +406,19 @@ __global__ __launch_bounds__(kThreads) void residual_select_kernel(int block_k, 
 }  // namespace
 
 hipError_t launch_consensus_greedy(int batch, int block_k, int vocab, const float* logits,
-                                   const int32_t* cand, int32_t* accept_len, int32_t* row_argmax,
-                                   int32_t* correction, void* workspace, const ConsensusPlan& plan,
-                                   hipStream_t stream) {
+                                   const int32_t* cand, const int32_t* blk_len, int32_t* accept_len,
+                                   int32_t* row_argmax, int32_t* correction, void* workspace,
+                                   const ConsensusPlan& plan, hipStream_t stream) {
   auto* part = reinterpret_cast<unsigned long long*>(workspace);
   const int chunks = plan.greedy_chunks;
   int chunk_len = (vocab + chunks - 1) / chunks;
   chunk_len = (chunk_len + 3) & ~3;
   hipLaunchKernelGGL(argmax_partial_kernel, dim3(chunks, batch * block_k), dim3(kThreads), 0, stream,
-                     logits, vocab, chunk_len, part);
+                     logits, vocab, chunk_len, part, block_k, blk_len);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(greedy_finalize_kernel, dim3(batch), dim3(64), 0, stream, block_k, chunks, part,
-                     cand, accept_len, row_argmax, correction);
+                     cand, blk_len, accept_len, row_argmax, correction);
   return hipGetLastError();
 }
 
@@ -415,7 +431,7 @@ hipError_t launch_consensus_tree_greedy(int batch, int block_k, int vocab, const
   chunk_len = (chunk_len + 3) & ~3;  // as for the greedy rule: whole 16-byte groups per chunk
   auto* part = reinterpret_cast<unsigned long long*>(workspace);
   hipLaunchKernelGGL(argmax_partial_kernel, dim3(chunks, batch * block_k), dim3(kThreads), 0, stream, logits,
-                     vocab, chunk_len, part);
+                     vocab, chunk_len, part, block_k, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tree_finalize_kernel, dim3(batch), dim3(64), 0, stream, block_k, chunks, part, tokens, parent,
@@ -425,15 +441,15 @@ hipError_t launch_consensus_tree_greedy(int batch, int block_k, int vocab, const
 
 hipError_t launch_consensus_sample(int batch, int block_k, int vocab, const float* p_target,
                                    const float* q_draft, const int32_t* cand, const float* uniforms,
-                                   int32_t* accept_len, int32_t* correction, void* workspace,
-                                   const ConsensusPlan& plan, hipStream_t stream) {
+                                   const int32_t* blk_len, int32_t* accept_len, int32_t* correction,
+                                   void* workspace, const ConsensusPlan& plan, hipStream_t stream) {
   auto* ws = reinterpret_cast<uint8_t*>(workspace);
   auto* sums = reinterpret_cast<unsigned long long*>(ws);
   auto* ws_a = reinterpret_cast<int32_t*>(ws + (size_t)batch * plan.sample_chunks * 2 * 8);
   const int chunks = plan.sample_chunks;
   const int chunk_len = (vocab + chunks - 1) / chunks;
   hipLaunchKernelGGL(sample_accept_kernel, dim3(batch), dim3(64), 0, stream, block_k, vocab, p_target,
-                     q_draft, cand, uniforms, accept_len, correction, ws_a);
+                     q_draft, cand, uniforms, blk_len, accept_len, correction, ws_a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(residual_chunks_kernel, dim3(chunks, batch), dim3(kThreads), 0, stream, block_k,

@@ -37,14 +37,22 @@ class DecodeCycles:
     ``diff_out[s][layer]``, ``verify_out[s][layer]`` (bf16 [B,Hq,K,D]),
     ``accept_len[s]``, ``correction[s]``, ``next_anchor[s]``, ``tokens[s]``,
     ``n_tokens[s]``.
+
+    Dynamic block sizes (paper notes §7.4, §9.6): with ``blk_len`` (int32 [B]
+    on the device) every call of a cycle runs over each sequence's first
+    blk_len[b] block positions (the K of the inputs is the capacity), and the
+    commit rewrites blk_len with the next cycle's lengths (floor ``k_min``),
+    so the block size follows acceptance without the host.
     """
 
-    def __init__(self, k_cache, v_cache, cache_len, sets, softmax_scale: float = 0.0):
+    def __init__(self, k_cache, v_cache, cache_len, sets, softmax_scale: float = 0.0, blk_len=None,
+                 k_min: int = 1):
         if k_cache.dim() != 5:
             raise ValueError("k_cache must be [n_layers, B, Hkv, max_len, D]")
         self.n_layers = k_cache.shape[0]
         dev = k_cache.device
         self.k_cache, self.v_cache, self.cache_len = k_cache, v_cache, cache_len
+        self.blk_len = blk_len
         B = k_cache.shape[1]
         first_q = sets[0]["diff"][0][0]
         K = first_q.shape[2]
@@ -75,14 +83,15 @@ class DecodeCycles:
             for l in range(self.n_layers):
                 q, k_blk, v_blk = s["diff"][l]
                 calls.append(PreparedAttention(ORTHRUS_MASK_DIFF_BIDIR, q, k_blk, v_blk, k_cache[l], v_cache[l],
-                                               cache_len, d_out[l], None, self.attn_ws, softmax_scale))
+                                               cache_len, d_out[l], None, self.attn_ws, softmax_scale,
+                                               blk_len=blk_len))
             for l in range(self.n_layers):
                 calls.append(PreparedAttention(ORTHRUS_MASK_VERIFY_CAUSAL, s["verify"][l][0], kb[l], vb[l],
                                                k_cache[l], v_cache[l], cache_len, v_out[l], None, self.attn_ws,
-                                               softmax_scale))
-            calls.append(PreparedGreedy(s["logits"], s["cand"], acc, None, corr, self.cons_ws))
+                                               softmax_scale, blk_len=blk_len))
+            calls.append(PreparedGreedy(s["logits"], s["cand"], acc, None, corr, self.cons_ws, blk_len=blk_len))
             calls.append(PreparedCommit(k_cache, v_cache, kb, vb, cache_len, acc, corr, s["cand"], anchor,
-                                        toks, ntok))
+                                        toks, ntok, blk_len=blk_len, k_min=k_min))
             self._calls.append(calls)
             self._blocks.append((kb, vb))
             self.diff_out.append(d_out)

@@ -141,6 +141,25 @@ orthrus_status orthrus_block_attn_masked(const orthrus_attn_desc* d, const uint1
                                          uint16_t* out, float* lse, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/* Block attention with a block length per sequence (dynamic block sizes,
+ * paper notes §7.4 and §9.6: the block size chosen per sequence from
+ * acceptance).  blk_len int32 [B] on the device: sequence b's block in this
+ * call is its first k_b = clamp(blk_len[b], 1, K) positions.  Its block rows
+ * i < k_b attend to the cache [0, cache_len[b]) and to block keys j < k_b --
+ * all of them (ORTHRUS_MASK_DIFF_BIDIR) or j <= i (ORTHRUS_MASK_VERIFY_CAUSAL;
+ * other modes: ORTHRUS_ERR_BAD_SHAPE) -- exactly as orthrus_block_attn with
+ * K = k_b.  Block keys j >= k_b are invisible, and rows i >= k_b of out and
+ * lse are not written.  The buffers keep their [.., K, ..] layouts, so one
+ * descriptor and one workspace serve every length; rows past k_b are not
+ * computed, so a short block costs less matrix work.  blk_len NULL:
+ * ORTHRUS_ERR_NULL_PTR.  Everything else is orthrus_block_attn. */
+orthrus_status orthrus_block_attn_dyn(const orthrus_attn_desc* d, int32_t mode,
+                                      const uint16_t* q, const uint16_t* k_blk,
+                                      const uint16_t* v_blk, const uint16_t* k_cache,
+                                      const uint16_t* v_cache, const int32_t* cache_len,
+                                      const int32_t* blk_len, uint16_t* out, float* lse,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of the device scratch behind orthrus_block_attn_noalloc (16 MiB per
  * device, held from library load until the process ends). */
 #define ORTHRUS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
@@ -200,6 +219,19 @@ orthrus_status orthrus_consensus_greedy(int32_t batch, int32_t block_k, int32_t 
                                         int32_t* correction, void* workspace,
                                         size_t workspace_bytes, void* stream);
 
+/* Greedy consensus over a block length per sequence (dynamic block sizes,
+ * paper notes §7.4 and §9.6).  blk_len int32 [B] on the device, k_b =
+ * clamp(blk_len[b], 1, K): orthrus_consensus_greedy over rows [0, k_b) of
+ * sequence b -- accept_len a <= k_b, correction = argmax of row a if a < k_b,
+ * else -1 -- with row_argmax (if not NULL) -1 for rows i >= k_b.  Rows past
+ * k_b of logits and cand are never read.  blk_len NULL: ORTHRUS_ERR_NULL_PTR.
+ * Sizes, workspace and everything else as orthrus_consensus_greedy. */
+orthrus_status orthrus_consensus_greedy_dyn(int32_t batch, int32_t block_k, int32_t vocab,
+                                            const float* logits, const int32_t* cand,
+                                            const int32_t* blk_len, int32_t* accept_len,
+                                            int32_t* row_argmax, int32_t* correction,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* T>0 consensus by exact rejection sampling (paper notes §4.3 and §7.2,
  * Leviathan/Chen rule).
  *   p_target  fp32 [B, K, V]  AR probabilities at the sampling temperature
@@ -224,6 +256,21 @@ orthrus_status orthrus_consensus_sample(int32_t batch, int32_t block_k, int32_t 
                                         int32_t* accept_len, int32_t* correction,
                                         void* workspace, size_t workspace_bytes,
                                         void* stream);
+
+/* T>0 consensus over a block length per sequence (dynamic block sizes,
+ * paper notes §7.4 and §9.6).  blk_len int32 [B] on the device, k_b =
+ * clamp(blk_len[b], 1, K): orthrus_consensus_sample over rows [0, k_b) of
+ * sequence b -- accept tests with u_0 .. u_{k_b-1}, a <= k_b, correction -1
+ * if a == k_b, else drawn from row a's residual with u_K (the uniforms keep
+ * their [B, K+1] layout).  Rows past k_b of p_target, q_draft and cand are
+ * never read.  blk_len NULL: ORTHRUS_ERR_NULL_PTR.  Everything else as
+ * orthrus_consensus_sample. */
+orthrus_status orthrus_consensus_sample_dyn(int32_t batch, int32_t block_k, int32_t vocab,
+                                            const float* p_target, const float* q_draft,
+                                            const int32_t* cand, const float* uniforms,
+                                            const int32_t* blk_len, int32_t* accept_len,
+                                            int32_t* correction, void* workspace,
+                                            size_t workspace_bytes, void* stream);
 
 /* Shapes of one cycle commit.  The cache and block arrays of all n_layers
  * layers are laid out layer-major, one after the other (a caller with
@@ -274,6 +321,31 @@ orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_ca
                                     const int32_t* accept_len, const int32_t* correction,
                                     const int32_t* cand, int32_t* next_anchor, int32_t* tokens,
                                     int32_t* n_tokens, void* stream);
+
+/* orthrus_cache_commit with a block length per sequence (dynamic block
+ * sizes, paper notes §7.4 and §9.6), which it also advances.
+ *   blk_len  int32 [B] on the device: read as k_b = clamp(blk_len[b], 1, K),
+ *            then rewritten IN PLACE with the next cycle's block length.
+ *   k_min    floor of the block length, 1 <= k_min <= K (else
+ *            ORTHRUS_ERR_BAD_SHAPE).
+ * The commit is orthrus_cache_commit with K = k_b for sequence b: with
+ * r = a + [a < k_b], verify rows 0..r-1 go to cache rows t..t+r-1, the
+ * correction is emitted when a < k_b, and a = k_b makes cand[b, k_b-1] the
+ * next anchor; a commit is refused when t < 0, a outside [0, k_b] or
+ * t + r > max_len.  cand and tokens keep their [B, K] layout.  The next
+ * length, after a committed cycle, is
+ *   min(2 k_b, K)              if a == k_b  (the whole block was accepted),
+ *   max(ceil(k_b / 2), k_min)  if 2 (a + 1) <= k_b  (at most half was used),
+ *   k_b                        otherwise,
+ * clamped to [k_min, K]; a refused commit writes k_b back.  blk_len NULL:
+ * ORTHRUS_ERR_NULL_PTR; other errors as orthrus_cache_commit. */
+orthrus_status orthrus_cache_commit_dyn(const orthrus_commit_desc* d, uint16_t* k_cache,
+                                        uint16_t* v_cache, const uint16_t* k_blk,
+                                        const uint16_t* v_blk, int32_t* cache_len,
+                                        const int32_t* accept_len, const int32_t* correction,
+                                        const int32_t* cand, int32_t* next_anchor,
+                                        int32_t* tokens, int32_t* n_tokens, int32_t* blk_len,
+                                        int32_t k_min, void* stream);
 
 /* Element type of logits for orthrus_forward_kl. */
 typedef enum {

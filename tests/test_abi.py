@@ -215,11 +215,14 @@ def test_valid_call_without_gpu_reports_hip_error():
         "c = _lib.CommitDesc(1, 1, 1, 64, 4, 256)\n"
         "print(lib.orthrus_cache_commit(ctypes.byref(c), 1 << 40, 2 << 40, 3 << 40, 4 << 40, P, P, P, P, P, P, "
         "P, None))\n"
+        "print(lib.orthrus_block_attn_dyn(ctypes.byref(d), 1, P, P, P, P, P, P, P, P, P, P, 1 << 30, None))\n"
+        "print(lib.orthrus_cache_commit_dyn(ctypes.byref(c), 1 << 40, 2 << 40, 3 << 40, 4 << 40, P, P, P, P, P, "
+        "P, P, P, 2, None))\n"
     ) % ROOT
     env = dict(os.environ, HIP_VISIBLE_DEVICES="")
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, env=env)
     assert res.returncode == 0, res.stderr
-    assert [int(x) for x in res.stdout.strip().splitlines()[-2:]] == [_lib.ORTHRUS_ERR_HIP] * 2
+    assert [int(x) for x in res.stdout.strip().splitlines()[-4:]] == [_lib.ORTHRUS_ERR_HIP] * 4
 
 
 def test_product_path_never_touches_the_oracle():
@@ -252,3 +255,43 @@ def test_noalloc_entry_point_rejects_before_any_hip_call():
     assert call(_desc(), out=None) == _lib.ORTHRUS_ERR_NULL_PTR
     assert call(_desc(), kc=4104) == _lib.ORTHRUS_ERR_MISALIGNED
     assert call(_desc(head_dim=96)) == _lib.ORTHRUS_ERR_UNSUPPORTED
+
+
+def test_dynamic_block_entry_points_check_arguments_on_the_host():
+    """The per-sequence block-length variants need their length array and the
+    mode masks; the commit's floor must lie in [1, K]; the rest is checked as
+    in the fixed-length calls."""
+    lib = _lib.load()
+    P = 4096
+    d = _desc()
+
+    def attn(mode=0, blk=P, **ptrs):
+        p = dict(q=P, kb=P, vb=P, kc=P, vc=P, lens=P, out=P, lse=P, ws=P)
+        p.update(ptrs)
+        return lib.orthrus_block_attn_dyn(ctypes.byref(d), mode, p["q"], p["kb"], p["vb"], p["kc"], p["vc"],
+                                          p["lens"], blk, p["out"], p["lse"], p["ws"], 1 << 30, None)
+
+    assert attn(blk=None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert attn(mode=_lib.ORTHRUS_MASK_EXPLICIT) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert attn(blk=P + 2) == _lib.ORTHRUS_ERR_MISALIGNED
+    assert attn(q=None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert lib.orthrus_consensus_greedy_dyn(1, 4, 10, P, P, None, P, P, P, P, 1 << 20, None) == \
+        _lib.ORTHRUS_ERR_NULL_PTR
+    assert lib.orthrus_consensus_greedy_dyn(1, 4, 10, P, P, P + 2, P, P, P, P, 1 << 20, None) == \
+        _lib.ORTHRUS_ERR_MISALIGNED
+    assert lib.orthrus_consensus_greedy_dyn(1, 129, 10, P, P, P, P, P, P, P, 1 << 20, None) == \
+        _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_consensus_sample_dyn(1, 4, 10, P, P, P, P, None, P, P, P, 1 << 20, None) == \
+        _lib.ORTHRUS_ERR_NULL_PTR
+    assert lib.orthrus_consensus_sample_dyn(1, 4, 10, P, P, P, P, P, P, P, P, 1, None) == \
+        _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL
+    c = _cdesc()
+
+    def commit(blk=P, k_min=1):
+        return lib.orthrus_cache_commit_dyn(ctypes.byref(c), 1 << 40, 2 << 40, 3 << 40, 4 << 40, P, P, P, P, P,
+                                            P, P, blk, k_min, None)
+
+    assert commit(blk=None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert commit(k_min=0) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert commit(k_min=33) == _lib.ORTHRUS_ERR_BAD_SHAPE
+    assert commit(blk=P + 2) == _lib.ORTHRUS_ERR_MISALIGNED

@@ -1,0 +1,252 @@
+"""GPU parity of dynamic block sizes (a block length per sequence).
+
+Every entry point with a per-sequence block length k_b is checked against
+``oracle.dynamic`` on the same seeded inputs:
+
+* attention (``orthrus_block_attn_dyn``): the rows of each sequence's first
+  k_b positions within max-abs 2e-2 / relative L2 5e-3 (lse 1e-3), and every
+  row past k_b left exactly as it was (out and lse are pre-filled with a
+  marker).  The cases cover the one-sequence split launch (query blocks past
+  G k_b idle), the balanced launch of several sequences, K = 128 with row
+  groups that hold no live row, the single-split launch that writes the
+  output directly, head_dim 64, and k_b = 1 and k_b = K.
+* greedy and T>0 consensus, the commit with its block-length rule, and whole
+  decode cycles: bit-exact integers and cache bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dual_view_block_amd as dvb
+import oracle
+from dual_view_block_amd.cycle import DecodeCycles
+from oracle.cycle import bits_to_bf16
+from synth import Workload, attention_inputs, cycle_inputs, greedy_inputs, sample_inputs
+from tests._parity import assert_attn_close, assert_lse_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+MODES = {"diff": oracle.MASK_DIFF_BIDIR, "verify": oracle.MASK_VERIFY_CAUSAL}
+MARK_OUT = 3.0      # bf16-exact marker for rows that must stay untouched
+MARK_LSE = -7.0
+
+
+def _inputs(B, Hq, Hkv, D, K, lens, max_len, seed):
+    w = Workload("dyn", 1, B, Hq, Hkv, D, max(max(lens), 1), K, 10, 1.0, seed, max_len=max_len)
+    x = attention_inputs(w, device=DEV)
+    x["cache_len"] = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return x
+
+
+def _check_attn(x, kl, mode, what):
+    B, Hq, K, D = x["q"].shape
+    blk = torch.tensor(kl, dtype=torch.int32, device=DEV)
+    out = torch.full_like(x["q"], MARK_OUT)
+    lse = torch.full(x["q"].shape[:3], MARK_LSE, dtype=torch.float32, device=DEV)
+    dvb.orthrus_block_attn_dyn(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"], x["cache_len"], blk,
+                               MODES[mode], out=out, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.block_attention_dyn(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"],
+                                              x["cache_len"], kl, MODES[mode])
+    live_g = torch.cat([out[b, :, :k].reshape(-1, D) for b, k in enumerate(kl)])
+    live_r = np.concatenate([ref[b, :, :k].reshape(-1, D) for b, k in enumerate(kl)])
+    errs = assert_attn_close(live_g, live_r, f"{what}/{mode}")
+    assert_lse_close(torch.cat([lse[b, :, :k].reshape(-1) for b, k in enumerate(kl)]),
+                     np.concatenate([ref_lse[b, :, :k].reshape(-1) for b, k in enumerate(kl)]), f"{what}/{mode}")
+    for b, k in enumerate(kl):
+        assert bool((out[b, :, k:] == MARK_OUT).all()), f"{what}/{mode}: row past k_b={k} written (b={b})"
+        assert bool((lse[b, :, k:] == MARK_LSE).all()), f"{what}/{mode}: lse past k_b={k} written (b={b})"
+    print(f"{what}/{mode} k={kl}: max_abs={errs[0]:.2e} rel_l2={errs[1]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+@pytest.mark.parametrize("k", [1, 5, 20, 31, 32])
+def test_one_sequence_qwen3_8b_heads(mode, k):
+    """Qwen3-8B heads, K = 32, L = 3000 (32 splits): the 4 k rows of each KV
+    head fill ceil(4k / 32) of the work-group's 4 query blocks."""
+    x = _inputs(1, 32, 8, 128, 32, [3000], 4096, seed=100 + k)
+    _check_attn(x, [k], mode, "one sequence")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_balanced_batch(mode):
+    """Four sequences of 0..5000 keys (the balanced placement) with block
+    lengths 1, 32, 7 and 17."""
+    x = _inputs(4, 32, 8, 128, 32, [0, 5000, 130, 2048], 5120, seed=7)
+    _check_attn(x, [1, 32, 7, 17], mode, "balanced")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+@pytest.mark.parametrize("lens,kl", [([700], [5]), ([700], [64]), ([700], [100]), ([700], [128]),
+                                     ([700, 0, 300], [5, 128, 64])])
+def test_large_block_row_groups(mode, lens, kl):
+    """K = 128 with G = 4: 512 rows in 4 row groups of 128; with k_b = 5 three
+    of them hold no live row and stream nothing."""
+    x = _inputs(len(lens), 32, 8, 128, 128, lens, 1024, seed=sum(kl))
+    _check_attn(x, kl, mode, "K=128")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+@pytest.mark.parametrize("D,Hq", [(128, 32), (64, 16)])
+def test_single_split_direct_write(mode, D, Hq):
+    """Capacity 64: one split, so the streaming kernel writes the rows itself."""
+    x = _inputs(1, Hq, 8, D, 16, [40], 64, seed=D)
+    _check_attn(x, [9], mode, f"direct D{D}")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_head_dim_64_batch(mode):
+    x = _inputs(2, 16, 8, 64, 32, [1000, 77], 1024, seed=64)
+    _check_attn(x, [13, 32], mode, "D64")
+
+
+def test_greedy_consensus():
+    """Six sequences, K = 32, V = 151936, block lengths 1..32 with first
+    mismatches before, at and after the block end."""
+    w = Workload("g", 1, 6, 32, 8, 128, 1, 32, 151936, 3.0, 51)
+    js = torch.tensor([0, 3, 20, 32, 5, 8])
+    kl = [1, 5, 16, 32, 32, 8]
+    logits, cand, _ = greedy_inputs(w, first_mismatch=js)
+    ref_a, ref_am, ref_c = oracle.greedy_consensus_dyn(logits, cand, kl)
+    am = torch.full((6, 32), 12345, dtype=torch.int32, device=DEV)
+    a, am, c = dvb.orthrus_consensus_greedy_dyn(logits.to(DEV), cand.to(DEV),
+                                                torch.tensor(kl, dtype=torch.int32, device=DEV), row_argmax=am)
+    torch.cuda.synchronize()
+    assert a.cpu().tolist() == ref_a.tolist() == [0, 3, 16, 32, 5, 8]
+    assert c.cpu().tolist() == ref_c.tolist()
+    assert np.array_equal(am.cpu().numpy(), ref_am)
+    print(f"greedy dyn: a={a.cpu().tolist()} corr={c.cpu().tolist()}", flush=True)
+
+
+@pytest.mark.parametrize("noise", [None, 0.3])
+def test_sample_consensus(noise):
+    """T>0 over block lengths 1..16 of K = 16, V = 8192; with a draft close to
+    the target (noise 0.3) acceptance runs to the block end."""
+    w = Workload("s", 1, 6, 32, 8, 128, 1, 16, 8192, 3.0, 52)
+    p, q, cand, u = sample_inputs(w, draft_noise=noise)
+    kl = [1, 2, 5, 16, 9, 16]
+    ref_a, ref_c = oracle.sample_consensus_dyn(p, q, cand, u, kl)
+    a, c = dvb.orthrus_consensus_sample_dyn(p.to(DEV), q.to(DEV), cand.to(DEV), u.to(DEV),
+                                            torch.tensor(kl, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert a.cpu().tolist() == ref_a.tolist()
+    assert c.cpu().tolist() == ref_c.tolist()
+    print(f"sample dyn noise={noise}: a={a.cpu().tolist()} corr={c.cpu().tolist()}", flush=True)
+
+
+def _bf16(shape, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16)
+
+
+def test_commit_and_block_length_rule():
+    """Three layers, eight sequences: whole blocks, early mismatches, a = k_b
+    at k_b = 1, a > k_b (refused), a cache that fills exactly and one that
+    overflows (refused), k_b out of range (clamped); then the next lengths."""
+    n_layers, B, Hkv, D, K, max_len = 3, 8, 8, 128, 32, 300
+    kc, vc = _bf16((n_layers, B, Hkv, max_len, D), 1), _bf16((n_layers, B, Hkv, max_len, D), 2)
+    kb, vb = _bf16((n_layers, B, Hkv, K, D), 3), _bf16((n_layers, B, Hkv, K, D), 4)
+    lens = [10, 10, 0, 290, 291, 5, 100, 50]
+    kl = [8, 32, 1, 10, 10, 4, 0, 40]
+    acc = [8, 3, 1, 9, 10, 5, 0, 31]
+    g = torch.Generator().manual_seed(9)
+    cand = torch.randint(0, 151936, (B, K), generator=g, dtype=torch.int32)
+    corr = torch.randint(0, 151936, (B,), generator=g, dtype=torch.int32)
+    ref = oracle.commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cand, kl, k_min=2)
+    dlen = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dblk = torch.tensor(kl, dtype=torch.int32, device=DEV)
+    anchor, toks, ntok = dvb.orthrus_cache_commit_dyn(kc, vc, kb, vb, dlen, torch.tensor(acc, dtype=torch.int32,
+                                                                                           device=DEV),
+                                                      corr.to(DEV), cand.to(DEV), dblk, k_min=2)
+    torch.cuda.synchronize()
+    assert dlen.cpu().tolist() == ref["cache_len"].tolist()
+    assert dblk.cpu().tolist() == ref["blk_len"].tolist()
+    assert ntok.cpu().tolist() == ref["n_tokens"].tolist()
+    assert anchor.cpu().tolist() == ref["next_anchor"].tolist()
+    assert toks.cpu().tolist() == ref["tokens"].tolist()
+    assert torch.equal(kc.cpu(), bits_to_bf16(ref["k_cache"]))
+    assert torch.equal(vc.cpu(), bits_to_bf16(ref["v_cache"]))
+    print(f"commit dyn: lens={dlen.cpu().tolist()} blk_len={dblk.cpu().tolist()}", flush=True)
+
+
+def _to_dev(sets):
+    return [{"diff": [tuple(t.to(DEV) for t in v) for v in s["diff"]],
+             "verify": [tuple(t.to(DEV) for t in v) for v in s["verify"]],
+             "logits": s["logits"].to(DEV), "cand": s["cand"].to(DEV)} for s in sets]
+
+
+def _cycle_case(w, n, rate, seed):
+    sets = cycle_inputs(w, n, accept_rate=rate, seed_offset=seed)
+    shape = (w.layers, w.batch, w.n_kv_heads, w.capacity, w.head_dim)
+    kc = torch.randn(shape, generator=torch.Generator().manual_seed(seed + 1)).to(torch.bfloat16)
+    vc = torch.randn(shape, generator=torch.Generator().manual_seed(seed + 2)).to(torch.bfloat16)
+    return sets, kc, vc
+
+
+def test_decode_cycles_with_adaptive_block_lengths():
+    """Six cycles of three sequences (two layers, GQA 4, D 128, K 32) whose
+    block lengths start at 32, 4 and 9 and then follow the rule on the
+    device; every cycle's integers, attention rows and the final cache match
+    the oracle's cycles."""
+    w = Workload("dcyc", 2, 3, 8, 2, 128, 700, 32, 4096, 3.0, 24, max_len=700 + 6 * 32)
+    sets, kc, vc = _cycle_case(w, 6, 0.75, 5)
+    lens, kl, k_min = [700, 0, 129], [32, 4, 9], 2
+    recs, st = oracle.decode_cycles_dyn(kc, vc, lens, kl, k_min, sets)
+    dkc, dvc = kc.to(DEV), vc.to(DEV)
+    dlen = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dblk = torch.tensor(kl, dtype=torch.int32, device=DEV)
+    drv = DecodeCycles(dkc, dvc, dlen, _to_dev(sets), blk_len=dblk, k_min=k_min)
+    drv.run(len(sets))
+    torch.cuda.synchronize()
+    for c, rec in enumerate(recs):
+        for name in ("accept_len", "correction", "next_anchor", "tokens", "n_tokens"):
+            got = getattr(drv, name)[c].cpu().numpy()
+            assert np.array_equal(got, rec[name]), f"cycle {c} {name}: {got} vs {rec[name]}"
+        k_in = rec["blk_len_in"]
+        D = w.head_dim
+        for layer in range(w.layers):
+            for view, outs in (("diff", drv.diff_out), ("verify", drv.verify_out)):
+                got = torch.cat([outs[c][layer][b, :, :k_in[b]].reshape(-1, D) for b in range(w.batch)])
+                ref = np.concatenate([rec[f"{view}_out"][layer][b, :, :k_in[b]].reshape(-1, D)
+                                      for b in range(w.batch)])
+                assert_attn_close(got, ref, f"c{c}/l{layer}/{view}")
+    assert dlen.cpu().tolist() == st["cache_len"].tolist()
+    assert dblk.cpu().tolist() == st["blk_len"].tolist()
+    assert torch.equal(dkc.cpu(), bits_to_bf16(st["k_cache"]))
+    assert torch.equal(dvc.cpu(), bits_to_bf16(st["v_cache"]))
+    print("block lengths per cycle:", [r["blk_len_in"].tolist() for r in recs], "->", st["blk_len"].tolist(),
+          flush=True)
+
+
+def test_adaptive_cycles_graph_replay_matches_eager():
+    """A captured round of 3 adaptive cycles replayed twice, with eager work
+    and synchronisations between the replays, equals 6 eager cycles bit for
+    bit after each replay (lengths, block lengths and cache)."""
+    w = Workload("dcyc_g", 2, 2, 8, 2, 128, 600, 32, 2048, 3.0, 25, max_len=600 + 6 * 32)
+    sets, kc, vc = _cycle_case(w, 3, 0.7, 13)
+    lens, kl = [600, 41], [32, 8]
+    dev_sets = _to_dev(sets)
+
+    def state():
+        return (kc.to(DEV), vc.to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                torch.tensor(kl, dtype=torch.int32, device=DEV))
+
+    ek, ev, el, eb = state()
+    eager = DecodeCycles(ek, ev, el, dev_sets, blk_len=eb, k_min=2)
+    gk, gv, gl, gb = state()
+    graphed = DecodeCycles(gk, gv, gl, dev_sets, blk_len=gb, k_min=2)
+    graphed.run(1)  # warm the calls once, then restore the state before capture
+    torch.cuda.synchronize()
+    for t, s in zip((gk, gv, gl, gb), state()):
+        t.copy_(s)
+    graphed.capture()
+    for rnd in range(2):
+        eager.run(3, first_cycle=3 * rnd)
+        torch.cuda.synchronize()
+        graphed.replay()
+        torch.cuda.synchronize()
+        assert gl.cpu().tolist() == el.cpu().tolist(), rnd
+        assert gb.cpu().tolist() == eb.cpu().tolist(), rnd
+        assert torch.equal(gk, ek) and torch.equal(gv, ev), rnd
+    print(f"graph replay: lengths {el.cpu().tolist()}, block lengths {eb.cpu().tolist()}", flush=True)
