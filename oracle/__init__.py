@@ -45,8 +45,8 @@ from .kl import forward_kl, forward_kl_rows
 from .train_attn import dual_pass_backward, dual_pass_forward, training_attention_flops
 from .tree import (ancestor_masks, build_tree, commit_path, masks_to_bits, topk_logprobs,
                    tree_greedy_consensus)
-from .dynamic import (block_attention_dyn, commit_block_dyn, decode_cycles_dyn, greedy_consensus_dyn,
-                      live_lengths, next_block_len, sample_consensus_dyn)
+from .dynamic import (block_attention_dyn, block_len_from_stat, commit_block_dyn, decode_cycles_dyn,
+                      greedy_consensus_dyn, live_lengths, sample_consensus_dyn, update_accept_stat)
 
 __all__ = [
     "MASK_DIFF_BIDIR", "MASK_VERIFY_CAUSAL", "block_attention",
@@ -57,5 +57,6 @@ __all__ = [
     "forward_kl_rows", "dual_pass_forward", "dual_pass_backward", "training_attention_flops",
     "MASK_EXPLICIT", "ancestor_masks", "build_tree", "commit_path", "masks_to_bits", "topk_logprobs",
     "tree_greedy_consensus", "block_attention_dyn", "commit_block_dyn", "greedy_consensus_dyn",
-    "live_lengths", "next_block_len", "sample_consensus_dyn", "decode_cycles_dyn",
+    "live_lengths", "sample_consensus_dyn", "decode_cycles_dyn", "update_accept_stat",
+    "block_len_from_stat",
 ]

@@ -26,22 +26,29 @@ Readings of points the pages leave open:
   u_0 .. u_{k_b-1} for the accept tests, u_K for the residual draw).  The
   commit treats the block as k_b positions long: a = k_b means no correction
   and cand[k_b - 1] becomes the next anchor (R3 with K = k_b).
-* R30 -- the block-length rule.  After a committed cycle with accepted length
-  a under block length k (capacity K, floor k_min):
-      k' = min(2k, K)            if a = k        (the whole block was accepted)
-      k' = max(ceil(k/2), k_min) if 2(a + 1) <= k (at most half of it was used)
-      k' = k                     otherwise,
-  then clamped to [k_min, K].  A refused commit (R17) keeps k.  The pages name
-  only the direction (large K where acceptance is high); doubling and halving
-  is the plainest rule with that direction whose state is one integer per
-  sequence.
+* R30 -- the block-length rule.  The pages tie the block size to a task's
+  acceptance rate (large K where it is high, small where it is low) and name
+  no rule.  Reading: the acceptance rate is the probability p that a draft
+  candidate matches, given the ones before it matched (the run of accepted
+  candidates is then geometric, as the pages' accept-length figures suggest).
+  Each sequence keeps an exponentially forgetting estimate of it -- accepted
+  candidates A over tested candidates N, both decayed by 7/8 per cycle (the
+  maximum-likelihood estimate of p from runs cut at the block end) -- and the
+  next block is the smallest power of two k with p^k <= 1/8 (the whole block
+  is accepted, and tokens possibly left on the table, in at most one cycle in
+  eight), clamped to [k_min, K]; with no evidence yet (N = 0) it is K.  All in
+  integers so that every implementation takes the same decision: A and N are
+  16-bit fields of one int32 (A high, N low) in units of 1/16 candidate; a
+  committed cycle with a accepted of k (t = a + [a < k] tested) sets
+  A <- A - floor(A/8) + 16 a and N <- N - floor(N/8) + 16 t; p is
+  P = floor(65536 A / N) (A above N counts as N), P^k is formed by squaring
+  with floor(x^2 / 65536), and 1/8 is 8192.  A refused commit (R17) changes
+  neither the statistics nor k.
 
 Each function applies the static definitions (``oracle.attention``,
 ``oracle.consensus``, ``oracle.cycle``) to each sequence's sliced block.
 """
 from __future__ import annotations
-
-import math
 
 import numpy as np
 
@@ -118,24 +125,50 @@ def sample_consensus_dyn(p_target, q_draft, cand, uniforms, blk_len):
     return acc, corr
 
 
-def next_block_len(a: int, k: int, block_k: int, k_min: int) -> int:
-    """The block length after a committed cycle (R30)."""
-    if a == k:
-        nk = min(2 * k, block_k)
-    elif 2 * (a + 1) <= k:
-        nk = max(math.ceil(k / 2), k_min)
+STAT_UNIT = 16        # one candidate in the acceptance statistics (R30)
+OVERRUN_Q16 = 8192    # 1/8: the largest whole-block acceptance probability wanted
+
+
+def stat_fields(stat: int):
+    """(A, N) of a packed acceptance statistic (R30); A is at most N."""
+    s = int(stat) & 0xFFFFFFFF
+    a_, n_ = s >> 16, s & 0xFFFF
+    return min(a_, n_), n_
+
+
+def update_accept_stat(stat: int, a: int, k: int) -> int:
+    """The statistic after a committed cycle that accepted a of k (R30)."""
+    A, N = stat_fields(stat)
+    t = a + (1 if a < k else 0)
+    A = A - A // 8 + STAT_UNIT * a
+    N = N - N // 8 + STAT_UNIT * t
+    return (A << 16) | N
+
+
+def block_len_from_stat(stat: int, block_k: int, k_min: int) -> int:
+    """The smallest power of two k with p^k <= 1/8 under the estimate (R30),
+    clamped to [k_min, K]; K with no evidence."""
+    A, N = stat_fields(stat)
+    if N == 0:
+        k = block_k
     else:
-        nk = k
-    return int(min(max(nk, k_min), block_k))
+        x = (A * 65536) // N      # p in Q16
+        k = 1
+        while k < block_k and x > OVERRUN_Q16:
+            x = (x * x) >> 16     # p^(2k)
+            k *= 2
+    return int(min(max(k, k_min), block_k))
 
 
 def commit_block_dyn(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand,
-                     blk_len, k_min: int):
+                     blk_len, accept_stat, k_min: int):
     """The commit of ``oracle.cycle.commit_block`` with sequence b's block cut
-    to its first k_b positions (R29), then the block-length rule (R30).
+    to its first k_b positions (R29), then the block-length rule (R30) from the
+    packed acceptance statistics ``accept_stat`` [B].
 
     Returns the dict of ``commit_block`` (tokens padded to [B, K] with -1) plus
-    ``blk_len`` int64 [B], the next cycle's block lengths.
+    ``blk_len`` and ``accept_stat`` int64 [B], the next cycle's lengths and
+    statistics.
     """
     kc, vc = _bits(k_cache), _bits(v_cache)
     kb, vb = _bits(k_blk), _bits(v_blk)
@@ -151,6 +184,8 @@ def commit_block_dyn(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, corr
     tokens = np.full((B, K), -1, dtype=np.int64)
     n_tokens = np.zeros(B, dtype=np.int64)
     new_k = kl.copy()
+    stats = [int(x) & 0xFFFFFFFF for x in _ints(accept_stat)]
+    new_stat = np.array(stats, dtype=np.int64)
     for b in range(B):
         k = int(kl[b])
         r = commit_block(kc[:, b:b + 1], vc[:, b:b + 1], kb[:, b:b + 1, :, :k], vb[:, b:b + 1, :, :k],
@@ -160,14 +195,15 @@ def commit_block_dyn(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, corr
         next_anchor[b] = r["next_anchor"][0]
         tokens[b, :k] = r["tokens"][0]
         n_tokens[b] = r["n_tokens"][0]
-        if n_tokens[b] > 0:  # committed (a refused commit emits nothing and keeps k)
-            new_k[b] = next_block_len(int(acc[b]), k, K, int(k_min))
+        if n_tokens[b] > 0:  # committed (a refused commit emits nothing and keeps k and the statistics)
+            new_stat[b] = update_accept_stat(stats[b], int(acc[b]), k)
+            new_k[b] = block_len_from_stat(int(new_stat[b]), K, int(k_min))
     return {"k_cache": kc, "v_cache": vc, "cache_len": new_len, "next_anchor": next_anchor,
-            "tokens": tokens, "n_tokens": n_tokens, "blk_len": new_k}
+            "tokens": tokens, "n_tokens": n_tokens, "blk_len": new_k, "accept_stat": new_stat}
 
 
 def decode_cycles_dyn(k_cache, v_cache, cache_len, blk_len, k_min: int, cycles, scale=None,
-                      keep_attention=True):
+                      keep_attention=True, accept_stat=None):
     """``oracle.cycle.decode_cycles`` with a block length per sequence: each
     cycle runs both views' attention, the greedy consensus and the commit over
     each sequence's first k_b positions, and the commit's block-length rule
@@ -181,6 +217,7 @@ def decode_cycles_dyn(k_cache, v_cache, cache_len, blk_len, k_min: int, cycles, 
     lens = _ints(cache_len).copy()
     K = _as_f64(cycles[0]["diff"][0][0]).shape[2]
     kl = live_lengths(blk_len, K)
+    stat = np.zeros(len(lens), dtype=np.int64) if accept_stat is None else _ints(accept_stat).copy()
     records = []
     for cyc in cycles:
         rec = {"cache_len_in": lens.copy(), "blk_len_in": kl.copy()}
@@ -197,9 +234,10 @@ def decode_cycles_dyn(k_cache, v_cache, cache_len, blk_len, k_min: int, cycles, 
         acc, _, corr = greedy_consensus_dyn(cyc["logits"], cyc["cand"], kl)
         kb = np.stack([_bits(vv[1]) for vv in cyc["verify"]])
         vb = np.stack([_bits(vv[2]) for vv in cyc["verify"]])
-        res = commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cyc["cand"], kl, k_min)
-        kc, vc, lens, kl = res["k_cache"], res["v_cache"], res["cache_len"], res["blk_len"]
+        res = commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cyc["cand"], kl, stat, k_min)
+        kc, vc, lens, kl, stat = res["k_cache"], res["v_cache"], res["cache_len"], res["blk_len"], res["accept_stat"]
         rec.update(accept_len=acc, correction=corr, cache_len=lens.copy(), blk_len=kl.copy(),
+                   accept_stat=stat.copy(),
                    next_anchor=res["next_anchor"], tokens=res["tokens"], n_tokens=res["n_tokens"])
         records.append(rec)
-    return records, {"k_cache": kc, "v_cache": vc, "cache_len": lens, "blk_len": kl}
+    return records, {"k_cache": kc, "v_cache": vc, "cache_len": lens, "blk_len": kl, "accept_stat": stat}

@@ -11,7 +11,8 @@ Each test ties ``oracle.dynamic`` to something other than itself:
   draw uses u_K), and identity with the static sampler when k_b = K;
 * commit: a hand-worked cycle (rows, length, tokens, anchor) with marked
   block rows past k_b that must never reach the cache;
-* the block-length rule: a hand table over (a, k).
+* the block-length rule: statistics and decisions worked out by hand, and the
+  float rule (smallest power of two k with p^k <= 1/8) on a grid of rates.
 """
 import numpy as np
 import pytest
@@ -184,25 +185,58 @@ def test_sampler_with_the_full_block_is_the_static_sampler():
     np.testing.assert_array_equal(c1, c2)
 
 
-# (a, k) -> k' with K = 32, k_min = 2 (R30), worked out by hand
-RULE = [
-    (8, 8, 16), (32, 32, 32), (20, 32, 32), (15, 32, 16), (16, 32, 32), (14, 32, 16), (0, 32, 16),
-    (3, 8, 4), (4, 8, 8), (0, 2, 2), (1, 2, 2), (2, 2, 4), (0, 3, 2), (2, 3, 3), (3, 3, 6),
-    (0, 5, 3), (1, 5, 3), (2, 5, 5), (16, 16, 32), (31, 32, 32),
+def test_acceptance_statistic_update_by_hand():
+    """A and N (high and low 16 bits, units of 1/16 candidate) decay by 7/8
+    and add the cycle's accepted and tested candidates (R30)."""
+    s1 = oracle.update_accept_stat(0, 3, 32)          # 3 accepted, then a rejection: 4 tested
+    assert s1 == (48 << 16) | 64
+    s2 = oracle.update_accept_stat(s1, 8, 8)          # whole block of 8: 8 tested, no rejection
+    assert s2 == ((48 - 6 + 128) << 16) | (64 - 8 + 128)
+    s3 = oracle.update_accept_stat(0, 0, 4)           # rejected at once: 1 tested
+    assert s3 == 16
+
+
+# (packed statistic, K, k_min) -> next block length, worked out by hand:
+#   (48, 64): P = 49152 -> 36864 (k 2) -> 20736 (k 4) -> 6561 (k 8) <= 8192
+#   (170, 184): P = 60549 -> 55941 -> 47750 -> 34790 -> 18468 (k 16) -> 5204 (k 32)
+#   (0, 16): P = 0 <= 8192 at k = 1
+#   (16, 32): P = 32768 -> 16384 (k 2) -> 4096 (k 4)
+HAND = [
+    (0, 32, 4, 32),                          # no evidence: K
+    ((48 << 16) | 64, 32, 2, 8),
+    ((48 << 16) | 64, 32, 16, 16),           # floor
+    ((170 << 16) | 184, 32, 1, 32),
+    ((170 << 16) | 184, 24, 1, 24),          # capped at a K that is no power of two
+    (16, 32, 1, 1),
+    (16, 32, 4, 4),
+    ((16 << 16) | 32, 32, 1, 4),
+    ((100 << 16) | 50, 32, 1, 32),           # A above N counts as N: p = 1
 ]
 
 
-@pytest.mark.parametrize("a,k,nk", RULE)
-def test_block_length_rule(a, k, nk):
-    assert oracle.next_block_len(a, k, 32, 2) == nk
+@pytest.mark.parametrize("stat,K,k_min,k", HAND)
+def test_block_length_from_statistic_by_hand(stat, K, k_min, k):
+    assert oracle.block_len_from_stat(stat, K, k_min) == k
 
 
-def test_block_length_rule_floor_and_cap():
-    assert oracle.next_block_len(0, 4, 32, 4) == 4      # never below k_min
-    assert oracle.next_block_len(0, 1, 32, 1) == 1
-    assert oracle.next_block_len(1, 1, 32, 1) == 2
-    assert oracle.next_block_len(20, 20, 24, 1) == 24   # capped at K
-    assert oracle.next_block_len(1, 3, 8, 5) == 5       # a k below the floor is lifted
+@pytest.mark.parametrize("p,K,k", [(0.3, 32, 2), (0.5, 32, 4), (0.6, 32, 8), (0.7, 32, 8), (0.75, 32, 8),
+                                   (0.85, 32, 16), (0.9, 32, 32), (0.95, 32, 32), (0.95, 128, 64),
+                                   (0.99, 128, 128), (0.1, 32, 1)])
+def test_block_length_is_the_smallest_power_of_two_with_rare_overrun(p, K, k):
+    """Away from the boundaries (1/8)^(1/k) the integer rule picks what the
+    float rule does: the smallest power of two k with p^k <= 1/8."""
+    want = 1
+    while want < K and p ** want > 0.125:
+        want *= 2
+    assert want == k
+    N = 16000
+    stat = (int(round(p * N)) << 16) | N
+    assert oracle.block_len_from_stat(stat, K, 1) == k
+
+
+def test_block_length_grows_with_the_match_rate():
+    ks = [oracle.block_len_from_stat((a << 16) | 4096, 128, 1) for a in range(0, 4097, 64)]
+    assert ks == sorted(ks) and ks[0] == 1 and ks[-1] == 128
 
 
 def test_commit_hand_worked():
@@ -222,21 +256,24 @@ def test_commit_hand_worked():
     acc = [3, 1, 6, 2]        # b0: whole block; b1: one accepted; b2: whole block; b3: no room
     corr = [-1, 77, -1, 55]
     cand = np.arange(B * K).reshape(B, K) + 10
-    r = oracle.commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cand, kl, k_min=2)
+    r = oracle.commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cand, kl, [0, 0, 0, 0], k_min=2)
     # b0: k_b = 3, a = 3: rows 0..2 at 5..7, tokens cand[0..2], anchor cand[2]
     assert r["cache_len"][0] == 8 and r["n_tokens"][0] == 3
     assert list(r["tokens"][0]) == [10, 11, 12, -1, -1, -1] and r["next_anchor"][0] == 12
     assert (r["k_cache"][0, 0, 0, 5:8, 0] == [100, 101, 102]).all()
     assert (r["k_cache"][0, 0, 0, 8:, 0] == 0).all()
-    assert r["blk_len"][0] == 6
+    # 3 of 3: A = N = 48, p = 1: the whole capacity
+    assert r["accept_stat"][0] == (48 << 16) | 48 and r["blk_len"][0] == 6
     # b1: a = 1 < k_b: rows 0..1 at 5..6, tokens cand[0], 77; anchor 77
     assert r["cache_len"][1] == 7 and list(r["tokens"][1][:2]) == [16, 77] and r["next_anchor"][1] == 77
     assert (r["v_cache"][0, 1, 0, 5:7, 0] == [1110, 1111]).all() and (r["v_cache"][0, 1, 0, 7:, 0] == 0).all()
-    assert r["blk_len"][1] == 3          # 2 (a + 1) = 4 > 3: keep
+    # 1 of 3, then a rejection: A = 16, N = 32, p = 1/2: p^4 = 1/16 <= 1/8
+    assert r["accept_stat"][1] == (16 << 16) | 32 and r["blk_len"][1] == 4
     # b2: k_b = K = 6, a = 6: the static commit of the whole block
     assert r["cache_len"][2] == 6 and r["next_anchor"][2] == cand[2, 5] and r["blk_len"][2] == 6
     # b3: 15 + 2 > 16: refused, nothing written, length and block length kept
     assert r["cache_len"][3] == 15 and r["n_tokens"][3] == 0 and r["blk_len"][3] == 2
+    assert r["accept_stat"][3] == 0
     assert (r["k_cache"][0, 3] == 0).all()
     assert not (r["k_cache"] == 0x7777).any() and not (r["v_cache"] == 0x7777 + 1000).any()
 
@@ -257,7 +294,7 @@ def test_cycles_with_every_block_at_capacity_are_the_static_cycles():
     sets, kc, vc = _cycles(w, 4, 0.6, 3)
     L = torch.tensor([40, 9], dtype=torch.int32)
     r1, s1 = oracle.decode_cycles(kc, vc, L, sets)
-    r2, s2 = oracle.decode_cycles_dyn(kc, vc, L, [4, 4], 4, sets)
+    r2, s2 = oracle.decode_cycles_dyn(kc, vc, L, [4, 4], 4, sets)  # k_min = K: the rule can only give K
     for a, b in zip(r1, r2):
         for n in ("accept_len", "correction", "cache_len", "next_anchor", "tokens", "n_tokens"):
             np.testing.assert_array_equal(a[n], b[n])
@@ -274,6 +311,7 @@ def test_cycle_block_lengths_follow_the_rule_and_the_lengths_add_up():
     recs, st = oracle.decode_cycles_dyn(kc, vc, [30, 0, 12], [8, 2, 5], 2, sets)
     lens = np.array([30, 0, 12])
     k = np.array([8, 2, 5])
+    stat = [0, 0, 0]
     for c, rec in enumerate(recs):
         assert rec["blk_len_in"].tolist() == k.tolist()
         a = rec["accept_len"]
@@ -283,7 +321,9 @@ def test_cycle_block_lengths_follow_the_rule_and_the_lengths_add_up():
         assert rec["n_tokens"].tolist() == n.tolist()
         lens = lens + n
         assert rec["cache_len"].tolist() == lens.tolist()
-        k = np.array([oracle.next_block_len(int(a[b]), int(k[b]), 8, 2) for b in range(3)])
+        stat = [oracle.update_accept_stat(stat[b], int(a[b]), int(k[b])) for b in range(3)]
+        assert rec["accept_stat"].tolist() == stat
+        k = np.array([oracle.block_len_from_stat(stat[b], 8, 2) for b in range(3)])
         assert rec["blk_len"].tolist() == k.tolist()
         for out in rec["verify_out"]:
             for b in range(3):
