@@ -65,6 +65,12 @@ def _parse():
                          "one packed 2048-token sequence at the workload's heads (0 to skip)")
     ap.add_argument("--configs", type=int, default=1,
                     help="also time the other configuration points (C2, C3, C4 at L=131072, C5); 0 skips")
+    ap.add_argument("--dyn-k", type=int, default=1,
+                    help="time dynamic block sizes: the step at live block lengths 1..K and adaptive-length "
+                         "decode cycles against fixed-K cycles (0 to skip)")
+    ap.add_argument("--dyn-k-min", type=int, default=4, help="floor of the adaptive block length")
+    ap.add_argument("--dyn-low-rate", type=float, default=0.5,
+                    help="the low per-candidate match rate the adaptive cycles are also timed at")
     ap.add_argument("--accept-rate", type=float, default=0.912,
                     help="per-candidate match probability of the synthetic acceptance law "
                          "(0.912: 10.8 tokens per cycle at K = 32)")
@@ -226,9 +232,11 @@ def attn_flops(w, causal: bool) -> int:
 
 
 class Step:
-    """Every call of one decode step, prepared once (pointers resolved)."""
+    """Every call of one decode step, prepared once (pointers resolved).  With
+    ``blk_len`` (int32 [B] on the device) every call runs over each sequence's
+    first blk_len[b] block positions (dynamic block sizes)."""
 
-    def __init__(self, w, caches, device):
+    def __init__(self, w, caches, device, blk_len=None):
         import torch
 
         import dual_view_block_amd as dvb
@@ -249,14 +257,14 @@ class Step:
                 out = torch.empty_like(q)
                 lse = torch.empty(q.shape[:3], dtype=torch.float32, device=device)
                 self.calls[view].append(dvb.PreparedAttention(mode, q, kb, vb, kc, vc, self.cache_len, out,
-                                                              lse, ws))
+                                                              lse, ws, blk_len=blk_len))
         logits, cand, _ = greedy_inputs(w, device=device)
         B, K = w.batch, w.block_k
         self.acc = torch.empty(B, dtype=torch.int32, device=device)
         self.am = torch.empty((B, K), dtype=torch.int32, device=device)
         self.corr = torch.empty(B, dtype=torch.int32, device=device)
         cws = torch.empty(dvb.orthrus_consensus_workspace_size(B, K, w.vocab), dtype=torch.uint8, device=device)
-        self.greedy = dvb.PreparedGreedy(logits, cand, self.acc, self.am, self.corr, cws)
+        self.greedy = dvb.PreparedGreedy(logits, cand, self.acc, self.am, self.corr, cws, blk_len=blk_len)
         self.keep += [logits, cand, ws, cws]
 
     def run(self, stream_ptr: int) -> None:
@@ -345,21 +353,38 @@ def commit_bytes(w, rows: float) -> float:
     return 2 * kv + state
 
 
-def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_rate: float):
-    """Synthetic decode cycles (both views of every layer, greedy consensus,
-    commit) issued through dual_view_block_amd.cycle.DecodeCycles: one round of
-    `n_sets` cycles is captured into a HIP graph and replayed; lengths advance
-    on the device.  Returns a dict of the measured figures."""
-    import torch
+def cycle_sets(w, n_sets: int, accept_rate: float, device):
+    """Input sets of synthetic decode cycles: first mismatches at the quantiles
+    of the truncated geometric law with per-candidate match rate
+    `accept_rate`."""
+    from synth import cycle_inputs
 
-    from dual_view_block_amd.cycle import DecodeCycles
-    from synth import cache_lengths, cycle_inputs
-
-    lens = cache_lengths(w, device)
     sets = cycle_inputs(w, n_sets, accept_rate=accept_rate, device=device, stratified=True)
     for s in sets:
         s["logits"], s["cand"] = s["logits"].to(device), s["cand"].to(device)
-    drv = DecodeCycles(kc_all, vc_all, lens, sets)
+    return sets
+
+
+def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_rate: float, sets=None,
+                k_min: int = 0):
+    """Synthetic decode cycles (both views of every layer, greedy consensus,
+    commit) issued through dual_view_block_amd.cycle.DecodeCycles: one round of
+    `n_sets` cycles is captured into a HIP graph and replayed; lengths advance
+    on the device.  With k_min > 0 the block length is adaptive: every
+    sequence starts at K and the commit's rule sets each next length (floor
+    k_min).  Returns a dict of the measured figures."""
+    import torch
+
+    from dual_view_block_amd.cycle import DecodeCycles
+    from synth import cache_lengths
+
+    lens = cache_lengths(w, device)
+    if sets is None:
+        sets = cycle_sets(w, n_sets, accept_rate, device)
+    blk = None
+    if k_min > 0:
+        blk = torch.full((w.batch,), w.block_k, dtype=torch.int32, device=device)
+    drv = DecodeCycles(kc_all, vc_all, lens, sets, blk_len=blk, k_min=max(k_min, 1))
     drv.run(n_sets)                      # eager warm-up round
     torch.cuda.synchronize()
     drv.capture()
@@ -367,6 +392,7 @@ def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_ra
     rounds = max(1, n_cycles // n_sets)
     stream = torch.cuda.current_stream()
     l0 = lens.clone()
+    k_seen = []
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     e0.record(stream)
@@ -374,9 +400,15 @@ def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_ra
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    tokens = int((lens - l0).sum().item())
+    if blk is not None:  # block lengths the timed cycles ended with, then one more eager round to sample them
+        k_end = blk.cpu().tolist()
+        for c in range(n_sets):
+            k_seen.append(int(blk[0].item()))
+            drv.issue(c)
+        torch.cuda.synchronize()
     cycles = rounds * n_sets
     us = e0.elapsed_time(e1) * 1e3 / cycles
-    tokens = int((lens - l0).sum().item())
     n_tok = [int(x) for s in range(n_sets) for x in drv.n_tokens[s].cpu().tolist()]
 
     # the commit alone: back-to-back all-layer commits of one input set on the same stream
@@ -392,7 +424,12 @@ def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_ra
     commit_us = c0.elapsed_time(c1) * 1e3 / reps
     rows = float(drv.n_tokens[0].float().mean().item())
     del drv
-    return {"cycles": cycles, "input_sets": n_sets, "launch": "hip_graph",
+    extra = {}
+    if blk is not None:
+        extra = {"block_len": "adaptive", "k_min": k_min, "block_len_after_timed_cycles": k_end,
+                 "block_len_per_cycle_one_round": k_seen,
+                 "mean_block_len": round(sum(k_seen) / len(k_seen), 2)}
+    return {**extra, "cycles": cycles, "input_sets": n_sets, "launch": "hip_graph",
             "us_per_cycle": round(us, 2), "cycles_per_s": round(1e6 / us, 2),
             "host_wall_us_per_cycle": round(wall / cycles * 1e6, 2),
             "tokens_per_cycle": round(tokens / (cycles * w.batch), 3),
@@ -401,6 +438,45 @@ def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_ra
             "cache_len_after": lens.cpu().tolist(),
             "commit_us": round(commit_us, 3), "commit_rows": rows,
             "commit_achieved_gbs": round(commit_bytes(w, rows) / (commit_us * 1e-6) / 1e9, 1)}
+
+
+def time_dynamic_k(w, caches, kc_all, vc_all, device, args, fixed_cycles):
+    """Dynamic block sizes.  (1) The step with every sequence's block length
+    set to k (capacity K): both views of every layer and the greedy consensus
+    over the first k positions.  (2) Decode cycles whose block length adapts
+    (start K, floor k_min) against fixed-K cycles on the same input sets, at the
+    default match rate and at a low one."""
+    import torch
+
+    blk = torch.full((w.batch,), w.block_k, dtype=torch.int32, device=device)
+    st = Step(w, caches, device, blk_len=blk)
+    by_k = {}
+    for k in (1, 4, 8, 16, w.block_k):
+        if k > w.block_k:
+            continue
+        blk.fill_(k)
+        mk, _ = time_steps(st, args.steps, args.warmup, False)
+        by_k[k] = round(mk * 1e3, 2)
+        print(f"[bench] live block length {k} of {w.block_k}: step {mk * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del st
+    out = {"step_us_vs_live_block_len": by_k, "k_min": args.dyn_k_min, "cycles": {}}
+    for rate in (args.accept_rate, args.dyn_low_rate):
+        sets = cycle_sets(w, args.cycle_sets, rate, device)
+        fixed = fixed_cycles if (rate == args.accept_rate and fixed_cycles is not None) else \
+            time_cycles(w, kc_all, vc_all, device, args.cycles, args.cycle_sets, rate, sets=sets)
+        adapt = time_cycles(w, kc_all, vc_all, device, args.cycles, args.cycle_sets, rate, sets=sets,
+                            k_min=args.dyn_k_min)
+        keep = ("us_per_cycle", "tokens_per_cycle", "tokens_per_s")
+        out["cycles"][str(rate)] = {
+            "fixed_k": {k: fixed[k] for k in keep},
+            "adaptive": {k: adapt[k] for k in keep + ("mean_block_len", "block_len_per_cycle_one_round")},
+            "adaptive_over_fixed_tokens_per_s": round(adapt["tokens_per_s"] / fixed["tokens_per_s"], 3)}
+        print(f"[bench] match rate {rate}: fixed K={w.block_k} {fixed['tokens_per_s']:.0f} tokens/s "
+              f"({fixed['us_per_cycle']:.0f} us/cycle), adaptive {adapt['tokens_per_s']:.0f} tokens/s "
+              f"({adapt['us_per_cycle']:.0f} us/cycle, mean block {adapt['mean_block_len']})",
+              file=sys.stderr, flush=True)
+        del sets
+    return out
 
 
 def time_forward_kl(device, rows: int, vocab: int, reps: int = 10):
@@ -865,6 +941,10 @@ def main():
         print(f"[bench] cycles: {cyc['us_per_cycle']:.1f} us/cycle, {cyc['tokens_per_cycle']:.2f} tokens/cycle, "
               f"commit {cyc['commit_us']:.2f} us", file=sys.stderr, flush=True)
 
+    dyn = None
+    if args.dyn_k:
+        dyn = time_dynamic_k(w, caches, kc_all, vc_all, device, args, cyc)
+
     tcy = None
     if args.tree_cycles > 0:
         tcy = time_tree_cycles(w, kc_all, vc_all, device, args.tree_cycles)
@@ -943,6 +1023,8 @@ def main():
     }
     if cyc is not None:
         line["decode_cycles"] = cyc
+    if dyn is not None:
+        line["dynamic_k"] = dyn
     if fkl is not None:
         line["forward_kl"] = fkl
     if tra is not None:

@@ -328,7 +328,7 @@ class PreparedCommit:
     ``orthrus_cache_commit``); calling it issues one C call on the stream."""
 
     def __init__(self, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand,
-                 next_anchor, tokens, n_tokens, blk_len=None, k_min: int = 1):
+                 next_anchor, tokens, n_tokens, blk_len=None, accept_stat=None, k_min: int = 1):
         self.desc = _check_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand)
         B, K, dev = self.desc.batch, self.desc.block_k, k_cache.device
         _need(next_anchor, "next_anchor", torch.int32, (B,), dev)
@@ -341,9 +341,10 @@ class PreparedCommit:
         self._args = (ctypes.byref(self.desc),) + tuple(t.data_ptr() for t in self._keep)
         if blk_len is not None:  # dynamic block sizes: the commit also advances blk_len
             _need(blk_len, "blk_len", torch.int32, (B,), dev)
-            self._keep = self._keep + (blk_len,)
+            _need(accept_stat, "accept_stat", torch.int32, (B,), dev)
+            self._keep = self._keep + (blk_len, accept_stat)
             self._fn = lib.orthrus_cache_commit_dyn
-            self._args = self._args + (blk_len.data_ptr(), int(k_min))
+            self._args = self._args + (blk_len.data_ptr(), accept_stat.data_ptr(), int(k_min))
 
     def __call__(self, stream_ptr: int) -> None:
         st = self._fn(*self._args, stream_ptr)
@@ -452,13 +453,16 @@ def orthrus_consensus_sample_dyn(p_target, q_draft, cand, uniforms, blk_len, acc
 
 
 def orthrus_cache_commit_dyn(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand, blk_len,
-                             k_min: int = 1, next_anchor=None, tokens=None, n_tokens=None, stream=None):
+                             accept_stat, k_min: int = 1, next_anchor=None, tokens=None, n_tokens=None,
+                             stream=None):
     """``orthrus_cache_commit`` over each sequence's first blk_len[b] block
-    positions; blk_len is then advanced in place to the next cycle's lengths.
+    positions; the acceptance statistics (int32 [B], 0 for a new sequence) and
+    blk_len are then advanced in place to the next cycle's.
     Returns (next_anchor [B], tokens [B, K], n_tokens [B])."""
     desc = _check_commit(k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand)
     B, K, dev = desc.batch, desc.block_k, k_cache.device
     _need(blk_len, "blk_len", torch.int32, (B,), dev)
+    _need(accept_stat, "accept_stat", torch.int32, (B,), dev)
     if next_anchor is None:
         next_anchor = torch.empty(B, dtype=torch.int32, device=dev)
     if tokens is None:
@@ -468,8 +472,8 @@ def orthrus_cache_commit_dyn(k_cache, v_cache, k_blk, v_blk, cache_len, accept_l
     st = _lib.load().orthrus_cache_commit_dyn(
         ctypes.byref(desc), k_cache.data_ptr(), v_cache.data_ptr(), k_blk.data_ptr(), v_blk.data_ptr(),
         cache_len.data_ptr(), accept_len.data_ptr(), correction.data_ptr(), cand.data_ptr(),
-        next_anchor.data_ptr(), tokens.data_ptr(), n_tokens.data_ptr(), blk_len.data_ptr(), int(k_min),
-        _stream_ptr(stream))
+        next_anchor.data_ptr(), tokens.data_ptr(), n_tokens.data_ptr(), blk_len.data_ptr(), accept_stat.data_ptr(),
+        int(k_min), _stream_ptr(stream))
     _lib.check("orthrus_cache_commit_dyn", st)
     return next_anchor, tokens, n_tokens
 

@@ -119,7 +119,7 @@ _SIGS = {
     "orthrus_block_attn_dyn": (_I32, [_DESC, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "orthrus_consensus_greedy_dyn": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "orthrus_consensus_sample_dyn": (_I32, [_I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "orthrus_cache_commit_dyn": (_I32, [ctypes.POINTER(CommitDesc)] + [_P] * 12 + [_I32, _P]),
+    "orthrus_cache_commit_dyn": (_I32, [ctypes.POINTER(CommitDesc)] + [_P] * 13 + [_I32, _P]),
 }
 
 _lib = None

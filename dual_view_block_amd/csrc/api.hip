@@ -347,8 +347,8 @@ orthrus_status run_sample(int32_t batch, int32_t block_k, int32_t vocab, const f
 orthrus_status run_commit(const orthrus_commit_desc* d, uint16_t* k_cache, uint16_t* v_cache,
                           const uint16_t* k_blk, const uint16_t* v_blk, int32_t* cache_len,
                           const int32_t* accept_len, const int32_t* correction, const int32_t* cand,
-                          int32_t* next_anchor, int32_t* tokens, int32_t* n_tokens, int32_t* blk_len, int k_min,
-                          void* stream) {
+                          int32_t* next_anchor, int32_t* tokens, int32_t* n_tokens, int32_t* blk_len,
+                          int32_t* accept_stat, int k_min, void* stream) {
   const orthrus_status st = check_commit_desc(d);
   if (st != ORTHRUS_OK) return st;
   if (!k_cache || !v_cache || !k_blk || !v_blk || !cache_len || !accept_len || !correction || !cand ||
@@ -356,7 +356,8 @@ orthrus_status run_commit(const orthrus_commit_desc* d, uint16_t* k_cache, uint1
     return ORTHRUS_ERR_NULL_PTR;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_blk) || !aligned16(v_blk) ||
       !aligned4(cache_len) || !aligned4(accept_len) || !aligned4(correction) || !aligned4(cand) ||
-      !aligned4(next_anchor) || !aligned4(tokens) || !aligned4(n_tokens) || (blk_len && !aligned4(blk_len)))
+      !aligned4(next_anchor) || !aligned4(tokens) || !aligned4(n_tokens) || (blk_len && !aligned4(blk_len)) ||
+      (accept_stat && !aligned4(accept_stat)))
     return ORTHRUS_ERR_MISALIGNED;
   // the copies read the block while writing the cache: the two must not share memory
   const size_t planes = (size_t)d->n_layers * d->batch * d->n_kv_heads;
@@ -368,8 +369,8 @@ orthrus_status run_commit(const orthrus_commit_desc* d, uint16_t* k_cache, uint1
     return ORTHRUS_ERR_BAD_SHAPE;
   const hipError_t e = launch_cache_commit(d->n_layers, d->batch, d->n_kv_heads, d->head_dim, d->block_k,
                                            d->max_len, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len,
-                                           correction, cand, next_anchor, tokens, n_tokens, blk_len, k_min,
-                                           reinterpret_cast<hipStream_t>(stream));
+                                           correction, cand, next_anchor, tokens, n_tokens, blk_len, accept_stat,
+                                           k_min, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 
@@ -510,18 +511,19 @@ orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_ca
                                     const int32_t* cand, int32_t* next_anchor, int32_t* tokens,
                                     int32_t* n_tokens, void* stream) {
   return run_commit(d, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand, next_anchor,
-                    tokens, n_tokens, nullptr, 1, stream);
+                    tokens, n_tokens, nullptr, nullptr, 1, stream);
 }
 
 orthrus_status orthrus_cache_commit_dyn(const orthrus_commit_desc* d, uint16_t* k_cache, uint16_t* v_cache,
                                         const uint16_t* k_blk, const uint16_t* v_blk, int32_t* cache_len,
                                         const int32_t* accept_len, const int32_t* correction,
                                         const int32_t* cand, int32_t* next_anchor, int32_t* tokens,
-                                        int32_t* n_tokens, int32_t* blk_len, int32_t k_min, void* stream) {
-  if (!blk_len) return ORTHRUS_ERR_NULL_PTR;
+                                        int32_t* n_tokens, int32_t* blk_len, int32_t* accept_stat, int32_t k_min,
+                                        void* stream) {
+  if (!blk_len || !accept_stat) return ORTHRUS_ERR_NULL_PTR;
   if (d && (k_min < 1 || k_min > d->block_k)) return ORTHRUS_ERR_BAD_SHAPE;
   return run_commit(d, k_cache, v_cache, k_blk, v_blk, cache_len, accept_len, correction, cand, next_anchor,
-                    tokens, n_tokens, blk_len, k_min, stream);
+                    tokens, n_tokens, blk_len, accept_stat, k_min, stream);
 }
 
 size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, int32_t dtype) {

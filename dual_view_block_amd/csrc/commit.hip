@@ -33,8 +33,10 @@ struct CommitArgs {
   int32_t* tokens;
   int32_t* n_tokens;
   // dynamic block sizes: NULL, or the live block length per sequence
-  // (clamped to [1, block_k]), rewritten in place with the next cycle's
+  // (clamped to [1, block_k]), rewritten in place with the next cycle's, and
+  // each sequence's packed acceptance statistics (see next_block_len)
   int32_t* blk_len;
+  int32_t* accept_stat;
   int k_min;       // floor of the block-length rule
   int planes;      // n_layers * B * Hkv
   int batch, n_kv_heads, head_dim, block_k, max_len;
@@ -57,17 +59,36 @@ __device__ __forceinline__ int live_k(const CommitArgs& a, int b) {
   return k < 1 ? 1 : (k > a.block_k ? a.block_k : k);
 }
 
-// The next cycle's block length after a committed cycle that accepted a of k
-// (Orthrus paper notes §7.4, §9.6: a large block where acceptance is high, a
-// small one where it is low): double it when the whole block was accepted,
-// halve it (rounding up) when at most half of it was used -- the accepted
-// candidates plus the correction -- and keep it otherwise; never below k_min
-// or above the capacity.
-__device__ __forceinline__ int next_block_len(int a, int k, int cap, int k_min) {
-  int nk = k;
-  if (a == k) nk = 2 * k;
-  else if (2 * (a + 1) <= k) nk = max((k + 1) / 2, k_min);
-  return min(max(nk, k_min), cap);
+// The block-length rule (Orthrus paper notes §7.4, §9.6: a large block where
+// acceptance is high, a small one where it is low).  Each sequence's
+// statistic packs A (high 16 bits) and N (low 16 bits): accepted and tested
+// draft candidates, in units of 1/16, decayed by 7/8 per committed cycle --
+// A / N estimates the probability p that a candidate matches once the ones
+// before it did.  The next block is the smallest power of two k with
+// p^k <= 1/8 (p in Q16, powers by squaring with the floor), clamped to
+// [k_min, cap]; cap while nothing has been seen (N = 0).  Integers only, so
+// every implementation takes the same decision.
+__device__ __forceinline__ uint32_t next_accept_stat(uint32_t stat, int a, int k) {
+  uint32_t A = stat >> 16, N = stat & 0xFFFFu;
+  if (A > N) A = N;
+  const uint32_t tested = (uint32_t)(a + (a < k ? 1 : 0));
+  N = min(N - N / 8 + 16u * tested, 0xFFFFu);  // both fields saturate
+  A = min(A - A / 8 + 16u * (uint32_t)a, N);
+  return (A << 16) | N;
+}
+
+__device__ __forceinline__ int next_block_len(uint32_t stat, int cap, int k_min) {
+  const uint32_t A = min(stat >> 16, stat & 0xFFFFu), N = stat & 0xFFFFu;
+  int k = cap;
+  if (N != 0) {
+    unsigned long long x = ((unsigned long long)A << 16) / N;  // p in Q16
+    k = 1;
+    while (k < cap && x > 8192ull) {  // 8192: 1/8
+      x = (x * x) >> 16;
+      k *= 2;
+    }
+  }
+  return min(max(min(k, cap), k_min), cap);
 }
 
 // grid.x = planes, grid.y = 2 (keys, values)
@@ -100,7 +121,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_state_kernel(const Comm
     for (int i = 0; i < K; ++i) tok[i] = -1;
     a.n_tokens[b] = 0;
     a.next_anchor[b] = -1;
-    if (a.blk_len != nullptr) a.blk_len[b] = kb;
+    if (a.blk_len != nullptr) a.blk_len[b] = kb;  // the statistics stay
     return;
   }
   const int32_t* cd = a.cand + (size_t)b * K;
@@ -115,7 +136,11 @@ __global__ __launch_bounds__(kCommitThreads) void commit_state_kernel(const Comm
   a.n_tokens[b] = n;
   a.next_anchor[b] = last;
   a.cache_len[b] = t + r;
-  if (a.blk_len != nullptr) a.blk_len[b] = next_block_len(acc, kb, K, a.k_min);
+  if (a.blk_len != nullptr) {
+    const uint32_t st = next_accept_stat((uint32_t)a.accept_stat[b], acc, kb);
+    a.accept_stat[b] = (int32_t)st;
+    a.blk_len[b] = next_block_len(st, K, a.k_min);
+  }
 }
 
 // ---- commit of an accepted tree path: rows path[0..a] (root first) of the
@@ -223,10 +248,11 @@ hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head
                                int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,
                                const uint16_t* v_blk, int32_t* cache_len, const int32_t* accept_len,
                                const int32_t* correction, const int32_t* cand, int32_t* next_anchor,
-                               int32_t* tokens, int32_t* n_tokens, int32_t* blk_len, int k_min,
-                               hipStream_t stream) {
+                               int32_t* tokens, int32_t* n_tokens, int32_t* blk_len, int32_t* accept_stat,
+                               int k_min, hipStream_t stream) {
   CommitArgs a{};
   a.blk_len = blk_len;
+  a.accept_stat = accept_stat;
   a.k_min = k_min;
   a.k_cache = k_cache;
   a.v_cache = v_cache;

@@ -152,13 +152,13 @@ hipError_t launch_train_bwd(const TrainBwdArgs& a, hipStream_t stream);
 // Row copies of the verified block into the cache, then the in-place state
 // update (two launches on `stream`).  blk_len: NULL, or the live block length
 // per sequence, which the state update replaces with the next cycle's
-// (floor k_min).
+// (floor k_min) from the acceptance statistics accept_stat (updated too).
 hipError_t launch_cache_commit(int n_layers, int batch, int n_kv_heads, int head_dim, int block_k,
                                int max_len, uint16_t* k_cache, uint16_t* v_cache, const uint16_t* k_blk,
                                const uint16_t* v_blk, int32_t* cache_len, const int32_t* accept_len,
                                const int32_t* correction, const int32_t* cand, int32_t* next_anchor,
-                               int32_t* tokens, int32_t* n_tokens, int32_t* blk_len, int k_min,
-                               hipStream_t stream);
+                               int32_t* tokens, int32_t* n_tokens, int32_t* blk_len, int32_t* accept_stat,
+                               int k_min, hipStream_t stream);
 
 // ---------------------------------------------------------------- forward KL
 // Forward KL (and, if grad != NULL, its gradient) of `rows` logit rows: one

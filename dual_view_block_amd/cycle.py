@@ -41,18 +41,23 @@ class DecodeCycles:
     Dynamic block sizes (paper notes §7.4, §9.6): with ``blk_len`` (int32 [B]
     on the device) every call of a cycle runs over each sequence's first
     blk_len[b] block positions (the K of the inputs is the capacity), and the
-    commit rewrites blk_len with the next cycle's lengths (floor ``k_min``),
-    so the block size follows acceptance without the host.
+    commit rewrites blk_len with the next cycle's lengths (floor ``k_min``)
+    from each sequence's acceptance statistics ``accept_stat`` (int32 [B] on
+    the device; zeros, no history, when not given), so the block size follows
+    acceptance without the host.
     """
 
     def __init__(self, k_cache, v_cache, cache_len, sets, softmax_scale: float = 0.0, blk_len=None,
-                 k_min: int = 1):
+                 k_min: int = 1, accept_stat=None):
         if k_cache.dim() != 5:
             raise ValueError("k_cache must be [n_layers, B, Hkv, max_len, D]")
         self.n_layers = k_cache.shape[0]
         dev = k_cache.device
         self.k_cache, self.v_cache, self.cache_len = k_cache, v_cache, cache_len
         self.blk_len = blk_len
+        if blk_len is not None and accept_stat is None:
+            accept_stat = torch.zeros(k_cache.shape[1], dtype=torch.int32, device=dev)
+        self.accept_stat = accept_stat
         B = k_cache.shape[1]
         first_q = sets[0]["diff"][0][0]
         K = first_q.shape[2]
@@ -91,7 +96,7 @@ class DecodeCycles:
                                                softmax_scale, blk_len=blk_len))
             calls.append(PreparedGreedy(s["logits"], s["cand"], acc, None, corr, self.cons_ws, blk_len=blk_len))
             calls.append(PreparedCommit(k_cache, v_cache, kb, vb, cache_len, acc, corr, s["cand"], anchor,
-                                        toks, ntok, blk_len=blk_len, k_min=k_min))
+                                        toks, ntok, blk_len=blk_len, accept_stat=accept_stat, k_min=k_min))
             self._calls.append(calls)
             self._blocks.append((kb, vb))
             self.diff_out.append(d_out)

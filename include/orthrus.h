@@ -324,28 +324,35 @@ orthrus_status orthrus_cache_commit(const orthrus_commit_desc* d, uint16_t* k_ca
 
 /* orthrus_cache_commit with a block length per sequence (dynamic block
  * sizes, paper notes §7.4 and §9.6), which it also advances.
- *   blk_len  int32 [B] on the device: read as k_b = clamp(blk_len[b], 1, K),
- *            then rewritten IN PLACE with the next cycle's block length.
- *   k_min    floor of the block length, 1 <= k_min <= K (else
- *            ORTHRUS_ERR_BAD_SHAPE).
+ *   blk_len      int32 [B] on the device: read as k_b = clamp(blk_len[b], 1, K),
+ *                then rewritten IN PLACE with the next cycle's block length.
+ *   accept_stat  int32 [B] on the device, the caller's per-sequence state
+ *                (0 when a sequence starts: no evidence), updated IN PLACE.
+ *   k_min        floor of the block length, 1 <= k_min <= K (else
+ *                ORTHRUS_ERR_BAD_SHAPE).
  * The commit is orthrus_cache_commit with K = k_b for sequence b: with
  * r = a + [a < k_b], verify rows 0..r-1 go to cache rows t..t+r-1, the
  * correction is emitted when a < k_b, and a = k_b makes cand[b, k_b-1] the
  * next anchor; a commit is refused when t < 0, a outside [0, k_b] or
- * t + r > max_len.  cand and tokens keep their [B, K] layout.  The next
- * length, after a committed cycle, is
- *   min(2 k_b, K)              if a == k_b  (the whole block was accepted),
- *   max(ceil(k_b / 2), k_min)  if 2 (a + 1) <= k_b  (at most half was used),
- *   k_b                        otherwise,
- * clamped to [k_min, K]; a refused commit writes k_b back.  blk_len NULL:
- * ORTHRUS_ERR_NULL_PTR; other errors as orthrus_cache_commit. */
+ * t + r > max_len.  cand and tokens keep their [B, K] layout.
+ * The next length.  accept_stat packs A (bits 31..16) and N (bits 15..0), the
+ * accepted and the tested draft candidates in units of 1/16, decayed by 7/8
+ * per committed cycle: with t = a + [a < k_b] candidates tested,
+ *   N <- min(N - floor(N/8) + 16 t, 65535),  A <- min(A - floor(A/8) + 16 a, N)
+ * (an A above N is read as N).  P = floor(65536 A / N) estimates, in Q16, the
+ * probability that a candidate matches once the ones before it did; the next
+ * block length is the smallest power of two k with P^k <= 8192 (1/8; the
+ * powers by repeated squaring, x <- floor(x^2 / 65536)), or K when N = 0,
+ * clamped to [k_min, K].  A refused commit writes k_b back and leaves
+ * accept_stat alone.  blk_len or accept_stat NULL: ORTHRUS_ERR_NULL_PTR; other
+ * errors as orthrus_cache_commit. */
 orthrus_status orthrus_cache_commit_dyn(const orthrus_commit_desc* d, uint16_t* k_cache,
                                         uint16_t* v_cache, const uint16_t* k_blk,
                                         const uint16_t* v_blk, int32_t* cache_len,
                                         const int32_t* accept_len, const int32_t* correction,
                                         const int32_t* cand, int32_t* next_anchor,
                                         int32_t* tokens, int32_t* n_tokens, int32_t* blk_len,
-                                        int32_t k_min, void* stream);
+                                        int32_t* accept_stat, int32_t k_min, void* stream);
 
 /* Element type of logits for orthrus_forward_kl. */
 typedef enum {

@@ -217,7 +217,7 @@ def test_valid_call_without_gpu_reports_hip_error():
         "P, None))\n"
         "print(lib.orthrus_block_attn_dyn(ctypes.byref(d), 1, P, P, P, P, P, P, P, P, P, P, 1 << 30, None))\n"
         "print(lib.orthrus_cache_commit_dyn(ctypes.byref(c), 1 << 40, 2 << 40, 3 << 40, 4 << 40, P, P, P, P, P, "
-        "P, P, P, 2, None))\n"
+        "P, P, P, P, 2, None))\n"
     ) % ROOT
     env = dict(os.environ, HIP_VISIBLE_DEVICES="")
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, env=env)
@@ -287,11 +287,13 @@ def test_dynamic_block_entry_points_check_arguments_on_the_host():
         _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL
     c = _cdesc()
 
-    def commit(blk=P, k_min=1):
+    def commit(blk=P, stat=P, k_min=1):
         return lib.orthrus_cache_commit_dyn(ctypes.byref(c), 1 << 40, 2 << 40, 3 << 40, 4 << 40, P, P, P, P, P,
-                                            P, P, blk, k_min, None)
+                                            P, P, blk, stat, k_min, None)
 
     assert commit(blk=None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert commit(stat=None) == _lib.ORTHRUS_ERR_NULL_PTR
+    assert commit(stat=P + 1) == _lib.ORTHRUS_ERR_MISALIGNED
     assert commit(k_min=0) == _lib.ORTHRUS_ERR_BAD_SHAPE
     assert commit(k_min=33) == _lib.ORTHRUS_ERR_BAD_SHAPE
     assert commit(blk=P + 2) == _lib.ORTHRUS_ERR_MISALIGNED

@@ -153,15 +153,19 @@ def test_commit_and_block_length_rule():
     g = torch.Generator().manual_seed(9)
     cand = torch.randint(0, 151936, (B, K), generator=g, dtype=torch.int32)
     corr = torch.randint(0, 151936, (B,), generator=g, dtype=torch.int32)
-    ref = oracle.commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cand, kl, k_min=2)
+    # statistics: none yet, a long history of matches, A above N (read as N), saturated fields
+    stat = [0, (3000 << 16) | 3100, (200 << 16) | 400, (90 << 16) | 60, 0, 17, -1, (1000 << 16) | 65535]
+    ref = oracle.commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cand, kl, stat, k_min=2)
     dlen = torch.tensor(lens, dtype=torch.int32, device=DEV)
     dblk = torch.tensor(kl, dtype=torch.int32, device=DEV)
+    dstat = torch.tensor(stat, dtype=torch.int32, device=DEV)
     anchor, toks, ntok = dvb.orthrus_cache_commit_dyn(kc, vc, kb, vb, dlen, torch.tensor(acc, dtype=torch.int32,
                                                                                            device=DEV),
-                                                      corr.to(DEV), cand.to(DEV), dblk, k_min=2)
+                                                      corr.to(DEV), cand.to(DEV), dblk, dstat, k_min=2)
     torch.cuda.synchronize()
     assert dlen.cpu().tolist() == ref["cache_len"].tolist()
     assert dblk.cpu().tolist() == ref["blk_len"].tolist()
+    assert [x & 0xFFFFFFFF for x in dstat.cpu().tolist()] == [int(x) & 0xFFFFFFFF for x in ref["accept_stat"]]
     assert ntok.cpu().tolist() == ref["n_tokens"].tolist()
     assert anchor.cpu().tolist() == ref["next_anchor"].tolist()
     assert toks.cpu().tolist() == ref["tokens"].tolist()
@@ -213,6 +217,7 @@ def test_decode_cycles_with_adaptive_block_lengths():
                 assert_attn_close(got, ref, f"c{c}/l{layer}/{view}")
     assert dlen.cpu().tolist() == st["cache_len"].tolist()
     assert dblk.cpu().tolist() == st["blk_len"].tolist()
+    assert drv.accept_stat.cpu().tolist() == st["accept_stat"].tolist()
     assert torch.equal(dkc.cpu(), bits_to_bf16(st["k_cache"]))
     assert torch.equal(dvc.cpu(), bits_to_bf16(st["v_cache"]))
     print("block lengths per cycle:", [r["blk_len_in"].tolist() for r in recs], "->", st["blk_len"].tolist(),
@@ -240,6 +245,7 @@ def test_adaptive_cycles_graph_replay_matches_eager():
     torch.cuda.synchronize()
     for t, s in zip((gk, gv, gl, gb), state()):
         t.copy_(s)
+    graphed.accept_stat.zero_()
     graphed.capture()
     for rnd in range(2):
         eager.run(3, first_cycle=3 * rnd)
@@ -248,5 +254,6 @@ def test_adaptive_cycles_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert gl.cpu().tolist() == el.cpu().tolist(), rnd
         assert gb.cpu().tolist() == eb.cpu().tolist(), rnd
+        assert graphed.accept_stat.cpu().tolist() == eager.accept_stat.cpu().tolist(), rnd
         assert torch.equal(gk, ek) and torch.equal(gv, ev), rnd
     print(f"graph replay: lengths {el.cpu().tolist()}, block lengths {eb.cpu().tolist()}", flush=True)
