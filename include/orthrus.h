@@ -449,7 +449,8 @@ orthrus_status orthrus_train_attn_bwd(const orthrus_train_attn_desc* d, const ui
 /* ------------------------------------------------------------------------
  * Tree verification (paper notes §7.4-7.5 and §9.6: verify a tree of
  * candidate prefixes built from the K diffusion marginals, DDTree style; a
- * dynamic block size is the same machinery with unused nodes).  A draft tree
+ * tree with unused nodes also carries a shorter block, and the *_dyn entry
+ * points above give every sequence its own block length).  A draft tree
  * has K nodes: node 0 is the anchor, node i > 0 has parent[b*K + i] < i and a
  * token; parent -1 marks an unused node.  Verify row i is the AR distribution
  * after the path root..i, so the verify attention lets row i see the block
