@@ -257,3 +257,47 @@ def test_adaptive_cycles_graph_replay_matches_eager():
         assert graphed.accept_stat.cpu().tolist() == eager.accept_stat.cpu().tolist(), rnd
         assert torch.equal(gk, ek) and torch.equal(gv, ev), rnd
     print(f"graph replay: lengths {el.cpu().tolist()}, block lengths {eb.cpu().tolist()}", flush=True)
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    K = int(rng.choice([1, 3, 8, 16, 24, 32, 40, 64, 100, 128]))
+    B = int(rng.integers(1, 7))
+    lens = [int(v) for v in rng.integers(0, 3000, size=B)]
+    kl = [int(v) for v in rng.integers(1, K + 1, size=B)]
+    cap = int(max(max(lens), 64) + rng.integers(0, 200))
+    return B, Hkv * G, Hkv, D, K, lens, cap, kl
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(seed):
+    """Seeded random shapes: batch 1..6, KV heads 1..8, GQA group 1..8,
+    head_dim 64/128, K up to 128, cached lengths 0..3000 and block lengths
+    1..K; the view alternates with the seed."""
+    B, Hq, Hkv, D, K, lens, cap, kl = _random_case(seed)
+    x = _inputs(B, Hq, Hkv, D, K, lens, cap, seed=2000 + seed)
+    _check_attn(x, kl, "diff" if seed % 2 == 0 else "verify",
+                f"random B{B} Hq{Hq} Hkv{Hkv} D{D} K{K} L{lens} cap{cap}")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+@pytest.mark.parametrize("B,Hq,Hkv,D,K,lens,cap", [
+    (1, 32, 8, 128, 32, [32768], 32768),      # the benchmark shape
+    (3, 16, 8, 64, 20, [0, 900, 2500], 2560),  # balanced placement, a dead query block
+    (2, 32, 8, 128, 128, [700, 33], 1024),     # row groups
+])
+def test_full_block_lengths_give_the_fixed_length_bits(mode, B, Hq, Hkv, D, K, lens, cap):
+    """Every k_b = K: the per-sequence-length call is the fixed-K call, bit
+    for bit (out and lse)."""
+    x = _inputs(B, Hq, Hkv, D, K, lens, cap, seed=K + B)
+    blk = torch.full((B,), K, dtype=torch.int32, device=DEV)
+    args = (x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"], x["cache_len"])
+    o1, l1 = dvb.orthrus_block_attn(*args, MODES[mode])
+    o2, l2 = dvb.orthrus_block_attn_dyn(*args, blk, MODES[mode])
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+    print(f"full-length bits B{B} K{K} {mode}: identical", flush=True)
