@@ -476,6 +476,32 @@ def time_dynamic_k(w, caches, kc_all, vc_all, device, args, fixed_cycles):
               f"({adapt['us_per_cycle']:.0f} us/cycle, mean block {adapt['mean_block_len']})",
               file=sys.stderr, flush=True)
         del sets
+    # a larger capacity: K = 128 buffers whose live block is 32, and adaptive
+    # cycles at that capacity against fixed K = 128 cycles (8 input sets)
+    if w.block_k < 128:
+        w128 = w.replace(block_k=128)
+        blk128 = torch.full((w.batch,), 128, dtype=torch.int32, device=device)
+        st = Step(w128, caches, device, blk_len=blk128)
+        cap = {}
+        for k in (32, 128):
+            blk128.fill_(k)
+            mk, _ = time_steps(st, args.steps, args.warmup, False)
+            cap[k] = round(mk * 1e3, 2)
+        del st
+        sets = cycle_sets(w128, 8, args.accept_rate, device)
+        fixed = time_cycles(w128, kc_all, vc_all, device, 16, 8, args.accept_rate, sets=sets)
+        adapt = time_cycles(w128, kc_all, vc_all, device, 16, 8, args.accept_rate, sets=sets, k_min=args.dyn_k_min)
+        keep = ("us_per_cycle", "tokens_per_cycle", "tokens_per_s")
+        out["capacity_128"] = {
+            "step_us_vs_live_block_len": cap,
+            "cycles_at_match_rate": args.accept_rate,
+            "fixed_k128": {k: fixed[k] for k in keep},
+            "adaptive": {k: adapt[k] for k in keep + ("mean_block_len",)},
+            "adaptive_over_fixed_tokens_per_s": round(adapt["tokens_per_s"] / fixed["tokens_per_s"], 3)}
+        print(f"[bench] capacity 128: step {cap[32]:.0f} us at live 32, {cap[128]:.0f} us at 128; cycles at rate "
+              f"{args.accept_rate}: fixed K=128 {fixed['tokens_per_s']:.0f} tokens/s, adaptive "
+              f"{adapt['tokens_per_s']:.0f} tokens/s (mean block {adapt['mean_block_len']})", file=sys.stderr, flush=True)
+        del sets
     return out
 
 

@@ -84,6 +84,22 @@ __device__ __forceinline__ int live_k(const AttnArgs& a, int b) {
   return k < 1 ? 1 : (k > a.block_k ? a.block_k : k);
 }
 
+// Row groups of sequence b that hold a live row: ceil(G k_b / rows_per_wg).
+__device__ __forceinline__ int live_row_groups(const AttnArgs& a, const AttnPlan& p, int b) {
+  const int R = a.group * live_k(a, b);
+  return min(p.row_groups, (R + p.rows_per_wg - 1) / p.rows_per_wg);
+}
+
+// A block length that leaves row groups without a live row: the n = RG * S
+// work-groups of a (sequence, KV head) are dealt round robin over its lrg live
+// row groups -- work-group j takes split j / lrg of live row group j % lrg, its
+// partial in slot j of the head's n -- so the whole launch keeps streaming.
+// Live row group rg then has this many splits (at most kMaxSplits; work-groups
+// past that stay idle).
+__device__ __forceinline__ int dealt_splits(int n, int lrg, int rg) {
+  return min((n - 1 - rg) / lrg + 1, kMaxSplits);
+}
+
 __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int split, int S) {
   SplitRange r;
   const int L = seq_len(a, b);
@@ -94,9 +110,9 @@ __device__ __forceinline__ SplitRange split_range(const AttnArgs& a, int b, int 
   r.kstart = split * chunk;
   r.kend = min(r.kstart + chunk, L);
   r.ncache = r.kstart < r.kend ? (r.kend - r.kstart + kTileKeys - 1) / kTileKeys : 0;
-  // split 0 streams the block keys first: their tile is computed while the
-  // first cache tile is still on its way from HBM
-  r.nblk = split == 0 ? (a.block_k + kTileKeys - 1) / kTileKeys : 0;
+  // split 0 streams the (live) block keys first: their tile is computed while
+  // the first cache tile is still on its way from HBM
+  r.nblk = split == 0 ? (live_k(a, b) + kTileKeys - 1) / kTileKeys : 0;
   r.ntiles = r.nblk + r.ncache;
   r.blk0 = 0;
   return r;
@@ -124,9 +140,9 @@ __device__ __forceinline__ int wave_sum(int x) {
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-// Tiles of one segment of sequence b: block-key tiles, then cache tiles.
+// Tiles of one segment of sequence b: (live) block-key tiles, then cache tiles.
 __device__ __forceinline__ int seg_tiles(const AttnArgs& a, int b) {
-  return (a.block_k + kTileKeys - 1) / kTileKeys + (seq_len(a, b) + kTileKeys - 1) / kTileKeys;
+  return (live_k(a, b) + kTileKeys - 1) / kTileKeys + (seq_len(a, b) + kTileKeys - 1) / kTileKeys;
 }
 // The fixed cost of one piece (its q and first tiles' latency, the closing
 // combine and partial write: about 7.7 us against 1.2 us per tile, fitted
@@ -140,39 +156,44 @@ constexpr int kPieceCost = 6;
 constexpr int kRaggedSlots = kRaggedMaxSeqs / 64;
 
 struct RaggedTiles {
-  int st[kRaggedSlots];  // segment units of sequence lane + 64*k: kPieceCost + tiles (0 past the batch)
+  // units per KV head of sequence lane + 64*k (0 past the batch): its row
+  // groups with a live row (all of them unless the block is short), each a
+  // segment of kPieceCost + tiles units
+  int su[kRaggedSlots];
 };
 
-__device__ __forceinline__ RaggedTiles ragged_tiles(const AttnArgs& a) {
+__device__ __forceinline__ RaggedTiles ragged_tiles(const AttnArgs& a, const AttnPlan& p) {
   const int lane = threadIdx.x & 63;
   RaggedTiles r;
 #pragma unroll
-  for (int k = 0; k < kRaggedSlots; ++k)
-    r.st[k] = lane + 64 * k < a.batch ? kPieceCost + seg_tiles(a, lane + 64 * k) : 0;
+  for (int k = 0; k < kRaggedSlots; ++k) {
+    const int b = lane + 64 * k;
+    r.su[k] = b < a.batch ? live_row_groups(a, p, b) * (kPieceCost + seg_tiles(a, b)) : 0;
+  }
   return r;
 }
 
-__device__ __forceinline__ long long ragged_total(const RaggedTiles& rt) {
+// Units of the whole list: every sequence's live segments, for every KV head.
+__device__ __forceinline__ long long ragged_total(const AttnArgs& a, const RaggedTiles& rt) {
   int t = 0;
 #pragma unroll
-  for (int k = 0; k < kRaggedSlots; ++k) t += rt.st[k];
-  return (long long)wave_sum(t);
+  for (int k = 0; k < kRaggedSlots; ++k) t += rt.su[k];
+  return (long long)wave_sum(t) * a.n_kv_heads;
 }
 
 struct SeqAt {
   int b;           // the sequence
-  int stiles;      // its segment units kPieceCost + S_b
   long long base;  // index of its first unit (segment h = 0) in the list
 };
 
 // The sequence whose segments hold list unit T < W (a whole wave calls it).
-__device__ SeqAt seq_at(const AttnArgs& a, const RaggedTiles& rt, int H, long long T) {
+__device__ SeqAt seq_at(const AttnArgs& a, const RaggedTiles& rt, long long T) {
   const int lane = threadIdx.x & 63;
   long long base = 0;
 #pragma unroll
   for (int k = 0; k < kRaggedSlots; ++k) {
     const int bb = 64 * k + lane;
-    const long long sz = (long long)rt.st[k] * H;  // this lane's sequence: all H segments
+    const long long sz = (long long)rt.su[k] * a.n_kv_heads;  // this lane's sequence: its live segments
     long long incl = sz;                          // inclusive scan over the lanes
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -183,18 +204,18 @@ __device__ SeqAt seq_at(const AttnArgs& a, const RaggedTiles& rt, int H, long lo
     const unsigned long long m = __ballot(bb < a.batch && T >= base + excl && T < base + incl);
     if (m) {
       const int src = __builtin_ctzll(m);
-      return {64 * k + src, __shfl(rt.st[k], src), base + __shfl(excl, src)};
+      return {64 * k + src, base + __shfl(excl, src)};
     }
     base += __shfl(incl, 63);
   }
-  return {-1, 0, base};
+  return {-1, base};
 }
 
 // Key range of tiles [p0, p1) of a segment of sequence b.
 __device__ __forceinline__ SplitRange piece_range(const AttnArgs& a, int b, int p0, int p1) {
   SplitRange r;
   const int L = seq_len(a, b);
-  const int nb = (a.block_k + kTileKeys - 1) / kTileKeys;
+  const int nb = (live_k(a, b) + kTileKeys - 1) / kTileKeys;  // as in seg_tiles
   r.blk0 = min(p0, nb);
   r.nblk = min(p1, nb) - r.blk0;
   const int c0 = max(p0, nb) - nb, c1 = max(p1, nb) - nb;  // cache tiles [c0, c1)
@@ -256,19 +277,31 @@ __device__ __forceinline__ void merge_wave(const AttnArgs& a, const AttnPlan& p,
   const int hw = LPR == 32 ? (lane >> 5) : 0;  // which row of the wave
   const int myrow = row + hw;
   const int rrow = min(myrow, p.rows_per_wg - 1);
-  const int S = a.splits;
-  const size_t slot0 = (size_t)grp * S;
+  // partial s of the group sits in slot slot0 + s * stride
+  int S = a.splits, stride = 1;
+  size_t slot0 = (size_t)grp * S;
+  if (a.blk_len != nullptr && p.row_groups > 1) {
+    const int bg = grp / p.row_groups, rg = grp % p.row_groups;
+    const int lrg = __builtin_amdgcn_readfirstlane(live_row_groups(a, p, bg / a.n_kv_heads));
+    if (lrg < p.row_groups) {  // the streaming launch dealt the head's work-groups over lrg row groups
+      if (rg >= lrg) return;   // a row group with no live row: nothing to merge
+      const int n = p.row_groups * a.splits;
+      S = dealt_splits(n, lrg, rg);
+      stride = lrg;
+      slot0 = (size_t)bg * n + rg;
+    }
+  }
   uint32_t v[SMAX];
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {
-    const size_t idx = (slot0 + min(s, S - 1)) * p.rows_per_wg + rrow;
+    const size_t idx = (slot0 + (size_t)min(s, S - 1) * stride) * p.rows_per_wg + rrow;
     v[s] = *reinterpret_cast<const uint32_t*>(a.ws_acc + idx * D + 2 * j);
   }
   float m[NW], l[NW];
 #pragma unroll
   for (int c = 0; c < NW; ++c) {
     const int sp = min(c * LPR + j, S - 1);
-    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + ((slot0 + sp) * p.rows_per_wg + rrow) * 2);
+    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + ((slot0 + (size_t)sp * stride) * p.rows_per_wg + rrow) * 2);
     const bool real = c * LPR + j < S;
     m[c] = real ? ml.x : kNegInf;
     l[c] = real ? ml.y : 0.0f;
@@ -671,7 +704,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     const int H = a.n_kv_heads * plan.row_groups;
     long long T, T1;
     {
-      const long long W = (long long)H * ragged_total(ragged_tiles(a));
+      const long long W = ragged_total(a, ragged_tiles(a, plan));
       // with fewer units than work-groups, one unit each: no used
       // work-group's range is empty, so the slots of every group stay
       // consecutive
@@ -682,24 +715,29 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     }
     bool first = true;
     while (T < T1) {  // uniform: every wave walks the same pieces
-      const SeqAt sq = seq_at(a, ragged_tiles(a), H, T);
+      const SeqAt sq = seq_at(a, ragged_tiles(a, plan), T);
       if (sq.b < 0) break;  // not reached: T < W lies in some sequence
+      const int stiles = kPieceCost + seg_tiles(a, sq.b);  // units of each of its segments
+      const int lrg = live_row_groups(a, plan, sq.b);
       const long long off = T - sq.base;
-      const int h = (int)(off / sq.stiles);
-      const int u0 = (int)(off % sq.stiles);  // units [u0, u1) of the segment
-      const int u1 = (int)min((long long)sq.stiles, T1 - (sq.base + (long long)h * sq.stiles));
+      const int h = (int)(off / stiles);
+      const int u0 = (int)(off % stiles);  // units [u0, u1) of the segment
+      const int u1 = (int)min((long long)stiles, T1 - (sq.base + (long long)h * stiles));
       T += u1 - u0;
       const int p0 = max(u0 - kPieceCost, 0), p1 = max(u1 - kPieceCost, 0);  // its tiles
       if (p0 == p1) continue;  // only the segment's cost units: no piece here
-      const int seg = sq.b * H + h;
+      // live segment h: KV head h / lrg, row group h % lrg (all row groups
+      // are live unless the block is short)
+      const int g = h / lrg, rg = h % lrg;
+      const int seg = sq.b * H + g * plan.row_groups + rg;
       const size_t slot = (size_t)lin + seg;
       if (threadIdx.x == 0) {  // the group's first and last slots, for the merge
         if (p0 == 0) a.ws_tab[seg].x = (int)slot;
-        if (p1 == sq.stiles - kPieceCost) a.ws_tab[seg].y = (int)slot;
+        if (p1 == stiles - kPieceCost) a.ws_tab[seg].y = (int)slot;
       }
       if (!first) __syncthreads();  // this piece reuses the LDS of the last one
       first = false;
-      piece(sq.b * a.n_kv_heads + h / plan.row_groups, h % plan.row_groups, piece_range(a, sq.b, p0, p1), slot);
+      piece(sq.b * a.n_kv_heads + g, rg, piece_range(a, sq.b, p0, p1), slot);
     }
   } else {
     // one piece: dispatch order (b, g) groups interleaved, split 0 (the block
@@ -711,10 +749,22 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     // likewise longest first, ranked on the device
     if (a.rank_blocks && a.batch <= kRankMaxBlocks)
       bg = block_by_rank(a.cache_len, a.batch, a.max_len, bg / a.n_kv_heads) * a.n_kv_heads + bg % a.n_kv_heads;
-    const int rg = (lin / (int)gridDim.z) % (int)gridDim.y;
-    const int split = lin / ((int)gridDim.z * (int)gridDim.y);
-    piece(bg, rg, split_range(a, bg / a.n_kv_heads, split, a.splits),
-          (size_t)(bg * plan.row_groups + rg) * a.splits + split);
+    int rg = (lin / (int)gridDim.z) % (int)gridDim.y;
+    int split = lin / ((int)gridDim.z * (int)gridDim.y);
+    int S = a.splits;
+    size_t slot = (size_t)(bg * plan.row_groups + rg) * a.splits + split;
+    if (a.blk_len != nullptr && plan.row_groups > 1) {
+      const int lrg = live_row_groups(a, plan, bg / a.n_kv_heads);
+      if (lrg < plan.row_groups) {  // short block: deal the head's work-groups over its live row groups
+        const int n = plan.row_groups * a.splits, j = rg * a.splits + split;
+        rg = j % lrg;
+        split = j / lrg;
+        S = dealt_splits(n, lrg, rg);
+        if (split >= S) return;
+        slot = (size_t)bg * n + j;
+      }
+    }
+    piece(bg, rg, split_range(a, bg / a.n_kv_heads, split, S), slot);
   }
 }
 
@@ -755,6 +805,9 @@ __global__ __launch_bounds__(kMergeThreads) void attn_merge_ragged_kernel(AttnAr
   const int j = (int)threadIdx.x % LPR;
   const int grp = mrow / plan.rows_per_wg;
   const int row = mrow % plan.rows_per_wg;
+  // a row group with no live row had no segment, so its table entry is stale
+  if (a.blk_len != nullptr && grp % plan.row_groups >= live_row_groups(a, plan, grp / plan.row_groups / a.n_kv_heads))
+    return;
   const int2 sl = a.ws_tab[grp];  // first and last slot of the group's partials
   const int S = sl.y - sl.x + 1;
   float M = kNegInf, L = 0.0f, acc[8];
@@ -843,9 +896,12 @@ hipError_t launch_merge(const AttnArgs& a, const AttnPlan& p, hipStream_t stream
     hipLaunchKernelGGL((attn_merge_ragged_kernel<D>), grid, dim3(kMergeThreads), 0, stream, a, p, total);
     return hipGetLastError();
   }
-  if (a.splits <= 8) return launch_merge_s<D, 8>(a, p, stream);
-  if (a.splits <= 16) return launch_merge_s<D, 16>(a, p, stream);
-  if (a.splits <= 32) return launch_merge_s<D, 32>(a, p, stream);
+  // with a per-sequence block length a live row group can hold the splits of
+  // every row group of its head (dealt), up to kMaxSplits
+  const int smax = (a.blk_len != nullptr && p.row_groups > 1) ? min(a.splits * p.row_groups, kMaxSplits) : a.splits;
+  if (smax <= 8) return launch_merge_s<D, 8>(a, p, stream);
+  if (smax <= 16) return launch_merge_s<D, 16>(a, p, stream);
+  if (smax <= 32) return launch_merge_s<D, 32>(a, p, stream);
   return launch_merge_s<D, kMaxSplits>(a, p, stream);
 }
 
@@ -866,7 +922,10 @@ template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& p, int phases, hipStream_t stream) {
   if (phases == 1) return launch_stream_any<D>(a, p, 0, stream);
   if (phases == 2) return launch_merge<D>(a, p, stream);
-  if (a.splits == 1 && !a.ragged) return launch_stream_any<D>(a, p, 1, stream);
+  // one split writes the rows directly -- unless short blocks may deal several
+  // splits to one row group
+  if (a.splits == 1 && !a.ragged && !(a.blk_len != nullptr && p.row_groups > 1))
+    return launch_stream_any<D>(a, p, 1, stream);
   const hipError_t e = launch_stream_any<D>(a, p, 0, stream);
   if (e != hipSuccess) return e;
   return launch_merge<D>(a, p, stream);

@@ -77,11 +77,14 @@ def test_balanced_batch(mode):
 
 
 @pytest.mark.parametrize("mode", ["diff", "verify"])
-@pytest.mark.parametrize("lens,kl", [([700], [5]), ([700], [64]), ([700], [100]), ([700], [128]),
-                                     ([700, 0, 300], [5, 128, 64])])
+@pytest.mark.parametrize("lens,kl", [([700], [5]), ([700], [64]), ([700], [72]), ([700], [100]), ([700], [128]),
+                                     ([700, 0, 300], [5, 128, 64]), ([2500, 40], [20, 33])])
 def test_large_block_row_groups(mode, lens, kl):
-    """K = 128 with G = 4: 512 rows in 4 row groups of 128; with k_b = 5 three
-    of them hold no live row and stream nothing."""
+    """K = 128 with G = 4: 512 rows in 4 row groups of 128.  With k_b = 5 three
+    of them hold no live row, and the head's 32 work-groups are dealt to the
+    live one as 32 splits; k_b = 72 leaves 3 live row groups, dealt 11, 11
+    and 10 splits.  The batches take the balanced placement, where a short
+    block's dead row groups get no segment."""
     x = _inputs(len(lens), 32, 8, 128, 128, lens, 1024, seed=sum(kl))
     _check_attn(x, kl, mode, "K=128")
 
@@ -301,3 +304,17 @@ def test_full_block_lengths_give_the_fixed_length_bits(mode, B, Hq, Hkv, D, K, l
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
     print(f"full-length bits B{B} K{K} {mode}: identical", flush=True)
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_unsplit_batch_with_short_blocks(mode):
+    """40 sequences with K = 128 capacity and 8 KV heads: 1280 groups, one
+    work-group each, no split.  Short blocks deal each head's 4 work-groups to
+    its live row groups, so the call takes the merge instead of writing the
+    rows directly."""
+    rng = np.random.default_rng(77)
+    lens = [int(v) for v in rng.integers(0, 1500, size=40)]
+    kl = [int(v) for v in rng.integers(1, 129, size=40)]
+    x = _inputs(40, 32, 8, 128, 128, lens, 1536, seed=77)
+    assert dvb.orthrus_attn_num_splits(dvb.attn_desc(x["q"], x["k_cache"])) == 1
+    _check_attn(x, kl, mode, "unsplit K=128")
