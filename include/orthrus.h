@@ -24,6 +24,16 @@
  *     non-OK status nothing was enqueued.  No exception crosses the ABI.
  *   - Calls are reentrant and thread-safe (the library has no mutable state).
  *   - Device buffers must be 16-byte aligned (128-bit loads and stores).
+ *
+ * Environment (read by the block-attention calls on every call; for tuning
+ * and diagnosis only, results stay within the documented tolerances):
+ *   ORTHRUS_MAX_SPLITS=n   caps the cache splits per (sequence, KV head) at n
+ *                          (it can only lower them); it must not change
+ *                          between an orthrus_block_attn_partial call and the
+ *                          orthrus_block_attn_merge of its partials.
+ *   ORTHRUS_EVEN_SPLITS=1  gives batches of several sequences equal splits
+ *                          per group instead of the balanced placement.
+ *   ORTHRUS_DEBUG          prints each attention launch plan to stderr.
  */
 #ifndef ORTHRUS_H
 #define ORTHRUS_H
