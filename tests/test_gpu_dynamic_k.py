@@ -318,3 +318,43 @@ def test_unsplit_batch_with_short_blocks(mode):
     x = _inputs(40, 32, 8, 128, 128, lens, 1536, seed=77)
     assert dvb.orthrus_attn_num_splits(dvb.attn_desc(x["q"], x["k_cache"])) == 1
     _check_attn(x, kl, mode, "unsplit K=128")
+
+
+def test_adaptive_cycles_follow_a_change_of_match_rate():
+    """24 cycles of three sequences whose draft matches well for 12 cycles
+    (rate 0.95) and poorly after (rate 0.4): the block lengths grow to the
+    capacity, then shrink, on the device, and after every cycle the
+    integers, lengths, statistics and block lengths equal the oracle's, and
+    so does the final cache.  The attention outputs are checked by the
+    six-cycle test above, not here."""
+    w = Workload("dcyc_switch", 1, 3, 8, 2, 64, 300, 32, 512, 3.0, 26, max_len=300 + 24 * 32)
+    hi = cycle_inputs(w, 12, accept_rate=0.95, seed_offset=41)
+    lo = cycle_inputs(w, 12, accept_rate=0.4, seed_offset=43)
+    sets = hi + lo
+    shape = (w.layers, w.batch, w.n_kv_heads, w.capacity, w.head_dim)
+    kc = torch.randn(shape, generator=torch.Generator().manual_seed(45)).to(torch.bfloat16)
+    vc = torch.randn(shape, generator=torch.Generator().manual_seed(46)).to(torch.bfloat16)
+    lens, kl, k_min = [300, 17, 0], [4, 32, 8], 2
+    recs, st = oracle.decode_cycles_dyn(kc, vc, lens, kl, k_min, sets, keep_attention=False)
+    dkc, dvc = kc.to(DEV), vc.to(DEV)
+    dlen = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dblk = torch.tensor(kl, dtype=torch.int32, device=DEV)
+    drv = DecodeCycles(dkc, dvc, dlen, _to_dev(sets), blk_len=dblk, k_min=k_min)
+    ks = []
+    for c in range(len(sets)):
+        drv.issue(c)
+        torch.cuda.synchronize()
+        ks.append(dblk.cpu().tolist())
+        rec = recs[c]
+        assert ks[-1] == rec["blk_len"].tolist(), f"cycle {c}"
+        assert drv.accept_stat.cpu().tolist() == rec["accept_stat"].tolist(), f"cycle {c}"
+        assert dlen.cpu().tolist() == rec["cache_len"].tolist(), f"cycle {c}"
+        for name in ("accept_len", "correction", "next_anchor", "tokens", "n_tokens"):
+            got = getattr(drv, name)[c].cpu().numpy()
+            assert np.array_equal(got, rec[name]), f"cycle {c} {name}: {got} vs {rec[name]}"
+    assert torch.equal(dkc.cpu(), bits_to_bf16(st["k_cache"]))
+    assert torch.equal(dvc.cpu(), bits_to_bf16(st["v_cache"]))
+    # the lengths reached the capacity while the draft matched and came down
+    # after (the statistics forget by 7/8 per cycle)
+    assert ks[11] == [32, 32, 32] and all(ks[-1][b] < ks[11][b] for b in range(3))
+    print("block lengths:", ks, flush=True)
