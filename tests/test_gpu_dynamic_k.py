@@ -358,3 +358,41 @@ def test_adaptive_cycles_follow_a_change_of_match_rate():
     # after (the statistics forget by 7/8 per cycle)
     assert ks[11] == [32, 32, 32] and all(ks[-1][b] < ks[11][b] for b in range(3))
     print("block lengths:", ks, flush=True)
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_block_lengths_out_of_range_are_clamped(mode):
+    """blk_len 0, -5 and 200 with K = 32 read as 1, 1 and 32 (attention)."""
+    x = _inputs(3, 32, 8, 128, 32, [900, 0, 2048], 2048, seed=91)
+    B, Hq, K, D = x["q"].shape
+    raw = [0, -5, 200]
+    blk = torch.tensor(raw, dtype=torch.int32, device=DEV)
+    out = torch.full_like(x["q"], MARK_OUT)
+    lse = torch.full(x["q"].shape[:3], MARK_LSE, dtype=torch.float32, device=DEV)
+    dvb.orthrus_block_attn_dyn(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"], x["cache_len"], blk,
+                               MODES[mode], out=out, lse=lse)
+    torch.cuda.synchronize()
+    kl = [1, 1, 32]
+    ref, ref_lse = oracle.block_attention_dyn(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"],
+                                              x["cache_len"], raw, MODES[mode])
+    assert_attn_close(torch.cat([out[b, :, :k].reshape(-1, D) for b, k in enumerate(kl)]),
+                      np.concatenate([ref[b, :, :k].reshape(-1, D) for b, k in enumerate(kl)]), "clamped")
+    for b, k in enumerate(kl):
+        assert bool((out[b, :, k:] == MARK_OUT).all()) and bool((lse[b, :, k:] == MARK_LSE).all())
+
+
+def test_consensus_block_lengths_out_of_range_are_clamped():
+    w = Workload("gc", 1, 3, 32, 8, 128, 1, 32, 4096, 3.0, 53)
+    logits, cand, _ = greedy_inputs(w, first_mismatch=torch.tensor([32, 32, 32]))
+    raw = [0, -5, 200]
+    ref_a, ref_am, ref_c = oracle.greedy_consensus_dyn(logits, cand, raw)
+    a, am, c = dvb.orthrus_consensus_greedy_dyn(logits.to(DEV), cand.to(DEV),
+                                                torch.tensor(raw, dtype=torch.int32, device=DEV))
+    ws = sample_inputs(w.replace(block_k=32), draft_noise=0.3)
+    ref_sa, ref_sc = oracle.sample_consensus_dyn(*ws, raw)
+    sa, sc = dvb.orthrus_consensus_sample_dyn(*[t.to(DEV) for t in ws], torch.tensor(raw, dtype=torch.int32,
+                                                                                      device=DEV))
+    torch.cuda.synchronize()
+    assert a.cpu().tolist() == ref_a.tolist() == [1, 1, 32]
+    assert c.cpu().tolist() == ref_c.tolist() and np.array_equal(am.cpu().numpy(), ref_am)
+    assert sa.cpu().tolist() == ref_sa.tolist() and sc.cpu().tolist() == ref_sc.tolist()
