@@ -27,7 +27,7 @@ __all__ = [
     "attn_desc", "orthrus_attn_workspace_size", "orthrus_attn_num_splits", "orthrus_block_attn",
     "orthrus_block_attn_diff", "orthrus_block_attn_verify", "orthrus_consensus_workspace_size",
     "orthrus_consensus_greedy", "orthrus_consensus_sample", "orthrus_status_string",
-    "PreparedAttention", "PreparedGreedy", "library_path", "CommitDesc", "orthrus_cache_commit",
+    "PreparedAttention", "PreparedGreedy", "PreparedSample", "library_path", "CommitDesc", "orthrus_cache_commit",
     "PreparedCommit", "orthrus_kl_workspace_size", "orthrus_forward_kl", "PreparedForwardKL",
     "TrainAttnDesc", "orthrus_train_attn_fwd", "orthrus_train_attn_bwd", "orthrus_block_attn_masked",
     "orthrus_topk_logprobs", "orthrus_tree_build", "orthrus_tree_masks", "orthrus_consensus_tree_greedy",
@@ -246,6 +246,35 @@ class PreparedGreedy:
         st = self._fn(*self._args, stream_ptr)
         if st:
             _lib.check("orthrus_consensus_greedy", st)
+
+
+class PreparedSample:
+    """A T>0 consensus call with every pointer resolved once."""
+
+    def __init__(self, p_target, q_draft, cand, uniforms, accept_len, correction, workspace, blk_len=None):
+        B, K, V = p_target.shape
+        dev = p_target.device
+        _need(p_target, "p_target", torch.float32, (B, K, V))
+        _need(q_draft, "q_draft", torch.float32, (B, K, V), dev)
+        _need(cand, "cand", torch.int32, (B, K), dev)
+        _need(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+        nbytes = orthrus_consensus_workspace_size(B, K, V)
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")
+        self._keep = (p_target, q_draft, cand, uniforms, accept_len, correction, workspace, blk_len)
+        lib = _lib.load()
+        self._fn = lib.orthrus_consensus_sample
+        self._args = (B, K, V, p_target.data_ptr(), q_draft.data_ptr(), cand.data_ptr(), uniforms.data_ptr(),
+                      accept_len.data_ptr(), correction.data_ptr(), workspace.data_ptr(), workspace.numel())
+        if blk_len is not None:  # dynamic block sizes
+            _need(blk_len, "blk_len", torch.int32, (B,), dev)
+            self._fn = lib.orthrus_consensus_sample_dyn
+            self._args = self._args[:7] + (blk_len.data_ptr(),) + self._args[7:]
+
+    def __call__(self, stream_ptr: int) -> None:
+        st = self._fn(*self._args, stream_ptr)
+        if st:
+            _lib.check("orthrus_consensus_sample", st)
 
 
 def orthrus_consensus_greedy(logits, cand, accept_len=None, row_argmax=None, correction=None,

@@ -20,7 +20,7 @@ from __future__ import annotations
 import torch
 
 from . import (ORTHRUS_MASK_DIFF_BIDIR, ORTHRUS_MASK_EXPLICIT, ORTHRUS_MASK_VERIFY_CAUSAL, PreparedAttention,
-               PreparedCommit, PreparedGreedy, _need, attn_desc, orthrus_attn_workspace_size,
+               PreparedCommit, PreparedGreedy, PreparedSample, _need, attn_desc, orthrus_attn_workspace_size,
                orthrus_consensus_workspace_size)
 
 
@@ -32,7 +32,9 @@ class DecodeCycles:
     sets              list of input sets, each a dict with
         "diff", "verify": per-layer lists of (q [B,Hq,K,D], k_blk [B,Hkv,K,D],
                           v_blk [B,Hkv,K,D]) bf16 device tensors
-        "logits" fp32 [B,K,V] and "cand" int32 [B,K] device tensors
+        "logits" fp32 [B,K,V] and "cand" int32 [B,K] device tensors (greedy
+        consensus), or "p", "q" fp32 [B,K,V], "cand" int32 [B,K] and
+        "uniforms" fp32 [B,K+1] (T>0 consensus by rejection sampling)
     Cycle c uses set c % len(sets) and writes that set's outputs:
     ``diff_out[s][layer]``, ``verify_out[s][layer]`` (bf16 [B,Hq,K,D]),
     ``accept_len[s]``, ``correction[s]``, ``next_anchor[s]``, ``tokens[s]``,
@@ -61,7 +63,7 @@ class DecodeCycles:
         B = k_cache.shape[1]
         first_q = sets[0]["diff"][0][0]
         K = first_q.shape[2]
-        V = sets[0]["logits"].shape[2]
+        V = (sets[0]["p"] if "p" in sets[0] else sets[0]["logits"]).shape[2]
         desc = attn_desc(first_q, k_cache[0], softmax_scale)
         self.attn_ws = torch.empty(max(orthrus_attn_workspace_size(desc), 16), dtype=torch.uint8, device=dev)
         self.cons_ws = torch.empty(max(orthrus_consensus_workspace_size(B, K, V), 16), dtype=torch.uint8,
@@ -94,7 +96,11 @@ class DecodeCycles:
                 calls.append(PreparedAttention(ORTHRUS_MASK_VERIFY_CAUSAL, s["verify"][l][0], kb[l], vb[l],
                                                k_cache[l], v_cache[l], cache_len, v_out[l], None, self.attn_ws,
                                                softmax_scale, blk_len=blk_len))
-            calls.append(PreparedGreedy(s["logits"], s["cand"], acc, None, corr, self.cons_ws, blk_len=blk_len))
+            if "p" in s:
+                calls.append(PreparedSample(s["p"], s["q"], s["cand"], s["uniforms"], acc, corr, self.cons_ws,
+                                            blk_len=blk_len))
+            else:
+                calls.append(PreparedGreedy(s["logits"], s["cand"], acc, None, corr, self.cons_ws, blk_len=blk_len))
             calls.append(PreparedCommit(k_cache, v_cache, kb, vb, cache_len, acc, corr, s["cand"], anchor,
                                         toks, ntok, blk_len=blk_len, accept_stat=accept_stat, k_min=k_min))
             self._calls.append(calls)

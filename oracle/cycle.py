@@ -42,7 +42,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import MASK_DIFF_BIDIR, MASK_VERIFY_CAUSAL, block_attention
-from .consensus import greedy_consensus
+from .consensus import greedy_consensus, sample_consensus
 
 
 def _bits(x) -> np.ndarray:
@@ -139,7 +139,9 @@ def decode_cycles(k_cache, v_cache, cache_len, cycles, scale=None, keep_attentio
     cycles  list of dicts, one per cycle, with
         "diff", "verify": per-layer lists of (q, k_blk, v_blk) bf16
                           ([B,Hq,K,D], [B,Hkv,K,D], [B,Hkv,K,D])
-        "logits" fp32 [B,K,V], "cand" int [B,K]
+        "logits" fp32 [B,K,V], "cand" int [B,K]  (greedy consensus), or
+        "p", "q" fp32 [B,K,V], "cand" int [B,K], "uniforms" fp32 [B,K+1]
+        (T>0 consensus by exact rejection sampling, notes §4.3)
     There is no model between the calls: the block inputs and the verify logits
     of each cycle are given, and the cycle's state (cache rows, lengths) flows
     from one cycle to the next exactly as in decoding.
@@ -164,7 +166,10 @@ def decode_cycles(k_cache, v_cache, cache_len, cycles, scale=None, keep_attentio
                                         MASK_VERIFY_CAUSAL, scale)
                 rec["diff_out"].append(od)
                 rec["verify_out"].append(ov)
-        acc, _, corr = greedy_consensus(cyc["logits"], cyc["cand"])
+        if "p" in cyc:
+            acc, corr = sample_consensus(cyc["p"], cyc["q"], cyc["cand"], cyc["uniforms"])
+        else:
+            acc, _, corr = greedy_consensus(cyc["logits"], cyc["cand"])
         kb = np.stack([_bits(vv[1]) for vv in cyc["verify"]])
         vb = np.stack([_bits(vv[2]) for vv in cyc["verify"]])
         res = commit_block(kc, vc, kb, vb, lens, acc, corr, cyc["cand"])

@@ -40,7 +40,8 @@ Readings of points the pages leave open:
   integers so that every implementation takes the same decision: A and N are
   16-bit fields of one int32 (A high, N low) in units of 1/16 candidate; a
   committed cycle with a accepted of k (t = a + [a < k] tested) sets
-  A <- A - floor(A/8) + 16 a and N <- N - floor(N/8) + 16 t; p is
+  A <- A - floor(A/8) + 16 a and N <- N - floor(N/8) + 16 t (N saturating
+  at 65535, A at N); p is
   P = floor(65536 A / N) (A above N counts as N), P^k is formed by squaring
   with floor(x^2 / 65536), and 1/8 is 8192.  A refused commit (R17) changes
   neither the statistics nor k.
@@ -140,8 +141,8 @@ def update_accept_stat(stat: int, a: int, k: int) -> int:
     """The statistic after a committed cycle that accepted a of k (R30)."""
     A, N = stat_fields(stat)
     t = a + (1 if a < k else 0)
-    A = A - A // 8 + STAT_UNIT * a
-    N = N - N // 8 + STAT_UNIT * t
+    N = min(N - N // 8 + STAT_UNIT * t, 0xFFFF)   # both fields saturate (blocks past 511)
+    A = min(A - A // 8 + STAT_UNIT * a, N)
     return (A << 16) | N
 
 
@@ -231,7 +232,10 @@ def decode_cycles_dyn(k_cache, v_cache, cache_len, blk_len, k_min: int, cycles, 
                                             MASK_VERIFY_CAUSAL, scale)
                 rec["diff_out"].append(od)
                 rec["verify_out"].append(ov)
-        acc, _, corr = greedy_consensus_dyn(cyc["logits"], cyc["cand"], kl)
+        if "p" in cyc:  # T>0 consensus
+            acc, corr = sample_consensus_dyn(cyc["p"], cyc["q"], cyc["cand"], cyc["uniforms"], kl)
+        else:
+            acc, _, corr = greedy_consensus_dyn(cyc["logits"], cyc["cand"], kl)
         kb = np.stack([_bits(vv[1]) for vv in cyc["verify"]])
         vb = np.stack([_bits(vv[2]) for vv in cyc["verify"]])
         res = commit_block_dyn(kc, vc, kb, vb, lens, acc, corr, cyc["cand"], kl, stat, k_min)

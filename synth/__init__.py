@@ -322,6 +322,24 @@ def cycle_inputs(w: Workload, n_cycles: int, accept_rate: float = 0.912, device=
     return out
 
 
+def sample_cycle_inputs(w: Workload, n_cycles: int, draft_noise: Optional[float] = 0.3, device="cpu",
+                        seed_offset: int = 0, layers: Optional[int] = None):
+    """Inputs of ``n_cycles`` synthetic T>0 decode cycles: per cycle fresh
+    block inputs for every layer and both views (as ``cycle_inputs``) and the
+    target/draft probabilities, candidates and uniforms of ``sample_inputs``
+    (a draft close to the target with ``draft_noise``).  Returns dicts with
+    "diff", "verify", "p", "q", "cand" and "uniforms"."""
+    n_layers = w.layers if layers is None else layers
+    out = []
+    for c in range(n_cycles):
+        wc = w.replace(seed=w.seed * 1009 + 31 * c + seed_offset)
+        diff = [view_inputs(wc, layer, "diff", device) for layer in range(n_layers)]
+        verify = [view_inputs(wc, layer, "verify", device) for layer in range(n_layers)]
+        p, q, cand, u = sample_inputs(wc, device, draft_noise=draft_noise)
+        out.append({"diff": diff, "verify": verify, "p": p, "q": q, "cand": cand, "uniforms": u})
+    return out
+
+
 def kl_inputs(rows: int, vocab: int, sigma: float = 3.0, dtype=torch.float32, seed: int = 0,
               draft_noise: Optional[float] = None, device="cpu"):
     """Target (AR) and draft (diffusion) logits [rows, vocab] for the forward-KL

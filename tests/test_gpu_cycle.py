@@ -2,8 +2,8 @@
 
 The commit is byte and integer work, so every comparison with the oracle is
 bit-exact: cache contents, advanced lengths, emitted tokens, token counts and
-next anchors.  Whole cycles (both views' attention per layer, greedy
-consensus, commit, repeated with the state carried on the device) are checked
+next anchors.  Whole cycles (both views' attention per layer, greedy or
+T > 0 consensus, commit, repeated with the state carried on the device) are checked
 cycle by cycle: integers bit-exact, attention outputs within max-abs 2e-2 and
 relative L2 5e-3 of the fp64 oracle.  A captured HIP graph of a round of
 cycles must replay bit-identically to the same cycles issued eagerly.
@@ -16,7 +16,7 @@ import dual_view_block_amd as dvb
 import oracle
 from dual_view_block_amd.cycle import DecodeCycles
 from oracle.cycle import bits_to_bf16
-from synth import WORKLOADS, Workload, cycle_inputs
+from synth import WORKLOADS, Workload, cycle_inputs, sample_cycle_inputs
 from tests._parity import assert_attn_close
 
 pytestmark = pytest.mark.gpu
@@ -136,9 +136,14 @@ def test_commit_rejects_block_inside_cache():
 def _to_dev(sets):
     out = []
     for s in sets:
-        out.append({"diff": [tuple(t.to(DEV) for t in v) for v in s["diff"]],
-                    "verify": [tuple(t.to(DEV) for t in v) for v in s["verify"]],
-                    "logits": s["logits"].to(DEV), "cand": s["cand"].to(DEV), "j_star": s["j_star"]})
+        d = {"diff": [tuple(t.to(DEV) for t in v) for v in s["diff"]],
+             "verify": [tuple(t.to(DEV) for t in v) for v in s["verify"]]}
+        for k in ("logits", "cand", "p", "q", "uniforms"):
+            if k in s:
+                d[k] = s[k].to(DEV)
+        if "j_star" in s:
+            d["j_star"] = s["j_star"]
+        out.append(d)
     return out
 
 
@@ -213,3 +218,69 @@ def test_decode_cycles_graph_replay_matches_eager():
                 assert torch.equal(graphed.diff_out[s][layer], eager.diff_out[s][layer])
         assert torch.equal(gk, ek) and torch.equal(gv, ev), f"round {rnd}"
     print(f"graph replay: lengths {el.cpu().tolist()}", flush=True)
+
+
+def _check_cycles(w, drv, recs, state, dkc, dvc, dlen):
+    for c, rec in enumerate(recs):
+        for name in ("accept_len", "correction", "next_anchor", "tokens", "n_tokens"):
+            got = getattr(drv, name)[c].cpu().numpy()
+            assert np.array_equal(got, rec[name]), f"cycle {c} {name}: {got} vs {rec[name]}"
+        for layer in range(w.layers):
+            assert_attn_close(drv.diff_out[c][layer], rec["diff_out"][layer], f"c{c}/l{layer}/diff")
+            assert_attn_close(drv.verify_out[c][layer], rec["verify_out"][layer], f"c{c}/l{layer}/verify")
+    assert dlen.cpu().tolist() == state["cache_len"].tolist()
+    assert torch.equal(dkc.cpu(), bits_to_bf16(state["k_cache"]))
+    assert torch.equal(dvc.cpu(), bits_to_bf16(state["v_cache"]))
+
+
+@pytest.mark.parametrize("case", [
+    # (workload, initial lengths, draft noise, cycles)
+    (Workload("scyc_small", 2, 2, 4, 2, 64, 300, 4, 1000, 4.0, 31, max_len=300 + 6 * 4), [300, 77], 0.5, 6),
+    (Workload("scyc_gqa4", 2, 3, 8, 2, 128, 700, 32, 4096, 3.0, 32, max_len=700 + 4 * 32), [700, 0, 129], 0.3, 4),
+])
+def test_sample_decode_cycles_match_oracle(case):
+    """T > 0 cycles (rejection-sampling consensus over a near draft): every
+    cycle's accepted prefix, sampled correction, emitted tokens and anchors
+    bit-exact, attention rows within tolerance, final cache bit-exact."""
+    w, lens, noise, n_cycles = case
+    sets = sample_cycle_inputs(w, n_cycles, draft_noise=noise, seed_offset=3)
+    kc, vc = _cycle_setup(w, 1, lens, 0.5, seed=9)[1:3]
+    L = torch.tensor(lens, dtype=torch.int32)
+    recs, state = oracle.decode_cycles(kc, vc, L, sets)
+    dkc, dvc, dlen = kc.to(DEV), vc.to(DEV), L.to(DEV)
+    drv = DecodeCycles(dkc, dvc, dlen, _to_dev(sets))
+    drv.run(n_cycles)
+    torch.cuda.synchronize()
+    _check_cycles(w, drv, recs, state, dkc, dvc, dlen)
+    print(f"{w.name}: accept lengths {[r['accept_len'].tolist() for r in recs]}", flush=True)
+
+
+def test_sample_decode_cycles_graph_replay_matches_eager():
+    """A captured round of 2 T > 0 cycles replayed twice, with eager work and
+    synchronisations between the replays, equals 4 eager cycles bit for bit."""
+    w = Workload("scyc_graph", 2, 2, 8, 2, 128, 900, 32, 2048, 3.0, 33, max_len=900 + 4 * 32)
+    sets = _to_dev(sample_cycle_inputs(w, 2, draft_noise=0.3, seed_offset=5))
+    kc, vc = _cycle_setup(w, 1, [900, 50], 0.5, seed=13)[1:3]
+    L = torch.tensor([900, 50], dtype=torch.int32)
+    ek, ev, el = kc.to(DEV), vc.to(DEV), L.to(DEV)
+    eager = DecodeCycles(ek, ev, el, sets)
+    gk, gv, gl = kc.to(DEV), vc.to(DEV), L.to(DEV)
+    graphed = DecodeCycles(gk, gv, gl, sets)
+    graphed.run(1)
+    torch.cuda.synchronize()
+    gk.copy_(kc.to(DEV))
+    gv.copy_(vc.to(DEV))
+    gl.copy_(L.to(DEV))
+    graphed.capture()
+    for rnd in range(2):
+        eager.run(2, first_cycle=2 * rnd)
+        torch.cuda.synchronize()
+        graphed.replay()
+        torch.cuda.synchronize()
+        _ = gk.float().sum()
+        torch.cuda.synchronize()
+        assert torch.equal(gl, el), f"round {rnd}"
+        for a, b in zip(graphed.tokens + graphed.accept_len, eager.tokens + eager.accept_len):
+            assert torch.equal(a, b), f"round {rnd}"
+        assert torch.equal(gk, ek) and torch.equal(gv, ev), f"round {rnd}"
+    print(f"sample graph replay: lengths {el.cpu().tolist()}", flush=True)

@@ -178,9 +178,13 @@ def test_commit_and_block_length_rule():
 
 
 def _to_dev(sets):
-    return [{"diff": [tuple(t.to(DEV) for t in v) for v in s["diff"]],
-             "verify": [tuple(t.to(DEV) for t in v) for v in s["verify"]],
-             "logits": s["logits"].to(DEV), "cand": s["cand"].to(DEV)} for s in sets]
+    out = []
+    for s in sets:
+        d = {"diff": [tuple(t.to(DEV) for t in v) for v in s["diff"]],
+             "verify": [tuple(t.to(DEV) for t in v) for v in s["verify"]]}
+        d.update({k: s[k].to(DEV) for k in ("logits", "cand", "p", "q", "uniforms") if k in s})
+        out.append(d)
+    return out
 
 
 def _cycle_case(w, n, rate, seed):
@@ -396,3 +400,38 @@ def test_consensus_block_lengths_out_of_range_are_clamped():
     assert a.cpu().tolist() == ref_a.tolist() == [1, 1, 32]
     assert c.cpu().tolist() == ref_c.tolist() and np.array_equal(am.cpu().numpy(), ref_am)
     assert sa.cpu().tolist() == ref_sa.tolist() and sc.cpu().tolist() == ref_sc.tolist()
+
+
+def test_sample_decode_cycles_with_adaptive_block_lengths():
+    """T > 0 cycles with adaptive block lengths: three sequences starting at
+    block lengths 32, 3 and 12; the sampler reads only the live rows and
+    uniforms u_0..u_{k-1} and u_K; every cycle's integers, the statistics,
+    the block lengths and the final cache match the oracle's cycles."""
+    from synth import sample_cycle_inputs
+    w = Workload("dscyc", 2, 3, 8, 2, 128, 500, 32, 4096, 3.0, 26, max_len=500 + 6 * 32)
+    sets = sample_cycle_inputs(w, 6, draft_noise=0.4, seed_offset=7)
+    _, kc, vc = _cycle_case(w, 1, 0.5, 17)
+    lens, kl, k_min = [500, 0, 64], [32, 3, 12], 2
+    recs, st = oracle.decode_cycles_dyn(kc, vc, lens, kl, k_min, sets)
+    dkc, dvc = kc.to(DEV), vc.to(DEV)
+    dlen = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dblk = torch.tensor(kl, dtype=torch.int32, device=DEV)
+    drv = DecodeCycles(dkc, dvc, dlen, _to_dev(sets), blk_len=dblk, k_min=k_min)
+    drv.run(len(sets))
+    torch.cuda.synchronize()
+    D = w.head_dim
+    for c, rec in enumerate(recs):
+        for name in ("accept_len", "correction", "next_anchor", "tokens", "n_tokens"):
+            got = getattr(drv, name)[c].cpu().numpy()
+            assert np.array_equal(got, rec[name]), f"cycle {c} {name}: {got} vs {rec[name]}"
+        k_in = rec["blk_len_in"]
+        for layer in range(w.layers):
+            got = torch.cat([drv.verify_out[c][layer][b, :, :k_in[b]].reshape(-1, D) for b in range(w.batch)])
+            ref = np.concatenate([rec["verify_out"][layer][b, :, :k_in[b]].reshape(-1, D) for b in range(w.batch)])
+            assert_attn_close(got, ref, f"c{c}/l{layer}/verify")
+    assert dlen.cpu().tolist() == st["cache_len"].tolist()
+    assert dblk.cpu().tolist() == st["blk_len"].tolist()
+    assert drv.accept_stat.cpu().tolist() == st["accept_stat"].tolist()
+    assert torch.equal(dkc.cpu(), bits_to_bf16(st["k_cache"]))
+    assert torch.equal(dvc.cpu(), bits_to_bf16(st["v_cache"]))
+    print("T>0 block lengths per cycle:", [r["blk_len_in"].tolist() for r in recs], flush=True)

@@ -309,3 +309,93 @@ def test_quantile_first_mismatch_follow_the_law():
     assert abs(n.double().mean().item() - 10.8) < 0.1
     assert first_mismatch_quantiles(4, 8, 1.0, 0).tolist() == [8, 8, 8, 8]
     assert first_mismatch_quantiles(4, 8, 0.0, 0).tolist() == [0, 0, 0, 0]
+
+
+# ------------------------------------------------- T > 0 whole cycles ----
+def _one_hot_target_sets(sets, seed):
+    """The greedy cycle sets turned into T > 0 sets: the target puts all its
+    mass on each row's argmax of the logits, the draft is a full-support
+    softmax, and the uniforms lie on the 2**-24 grid in [0, 1)."""
+    g = torch.Generator().manual_seed(seed)
+    out = []
+    for s in sets:
+        B, K, V = s["logits"].shape
+        p = torch.zeros(B, K, V)
+        p.scatter_(2, s["logits"].argmax(-1, keepdim=True), 1.0)
+        q = torch.softmax(torch.randn(B, K, V, generator=g, dtype=torch.float64), -1).float()
+        u = (torch.randint(0, 1 << 24, (B, K + 1), generator=g).double() / (1 << 24)).float()
+        t = {k: v for k, v in s.items() if k != "logits"}
+        t.update(p=p, q=q, uniforms=u)
+        out.append(t)
+    return out
+
+
+def _cycle_state(w, seed):
+    shape = (w.layers, w.batch, w.n_kv_heads, w.capacity, w.head_dim)
+    kc = torch.randn(shape, generator=torch.Generator().manual_seed(seed + 1)).to(torch.bfloat16)
+    vc = torch.randn(shape, generator=torch.Generator().manual_seed(seed + 2)).to(torch.bfloat16)
+    return kc, vc
+
+
+def test_sample_cycles_with_a_one_hot_target_are_the_greedy_cycles():
+    """A target with all its mass on the argmax turns rejection sampling into
+    greedy consensus (notes §4.2-4.3): a candidate at the argmax has ratio
+    1/q > u and is kept, any other has p = 0 and is refused, and the residual
+    max(p - q, 0) is a point mass at the argmax.  The T > 0 cycles must then
+    retrace the greedy cycles, and the planted first mismatch."""
+    w = Workload("t0", 2, 3, 4, 2, 32, 60, 6, 40, 4.0, 11, max_len=60 + 5 * 6)
+    greedy = cycle_inputs(w, 5, accept_rate=0.7)
+    kc, vc = _cycle_state(w, 5)
+    lens = torch.tensor([60, 0, 17], dtype=torch.int32)
+    r1, s1 = decode_cycles(kc, vc, lens, greedy, keep_attention=False)
+    r2, s2 = decode_cycles(kc, vc, lens, _one_hot_target_sets(greedy, 3), keep_attention=False)
+    for c, (a, b) in enumerate(zip(r1, r2)):
+        assert b["accept_len"].tolist() == greedy[c]["j_star"].tolist()
+        for n in ("accept_len", "correction", "cache_len", "next_anchor", "tokens", "n_tokens"):
+            np.testing.assert_array_equal(a[n], b[n], err_msg=f"cycle {c} {n}")
+    np.testing.assert_array_equal(s1["k_cache"], s2["k_cache"])
+    np.testing.assert_array_equal(s1["v_cache"], s2["v_cache"])
+
+
+def test_sample_cycles_with_the_draft_equal_to_the_target_keep_every_candidate():
+    """q = p makes every ratio exactly 1 > u: each cycle keeps all K
+    candidates, emits no correction, and the cache grows by K per cycle with
+    the candidates as the emitted tokens."""
+    from synth import sample_cycle_inputs
+    w = Workload("t1", 1, 2, 4, 2, 32, 50, 5, 30, 3.0, 12, max_len=50 + 4 * 5)
+    sets = sample_cycle_inputs(w, 4, draft_noise=0.3)
+    for s in sets:
+        s["q"] = s["p"].clone()
+    kc, vc = _cycle_state(w, 6)
+    recs, st = decode_cycles(kc, vc, torch.tensor([50, 3], dtype=torch.int32), sets, keep_attention=False)
+    for c, rec in enumerate(recs):
+        assert rec["accept_len"].tolist() == [5, 5] and rec["correction"].tolist() == [-1, -1]
+        assert rec["cache_len"].tolist() == [50 + 5 * (c + 1), 3 + 5 * (c + 1)]
+        assert rec["tokens"][:, :5].tolist() == sets[c]["cand"].tolist()
+    assert st["cache_len"].tolist() == [70, 23]
+
+
+def test_sample_cycles_commit_what_the_sampler_decides():
+    """Cycles over a near draft: each cycle commits the accepted prefix plus
+    the sampled correction, and the lengths add up from cycle to cycle."""
+    from synth import sample_cycle_inputs
+    w = Workload("t2", 2, 3, 4, 2, 32, 40, 8, 60, 3.0, 13, max_len=40 + 6 * 8)
+    sets = sample_cycle_inputs(w, 6, draft_noise=0.5)
+    kc, vc = _cycle_state(w, 7)
+    recs, st = decode_cycles(kc, vc, torch.tensor([40, 1, 25], dtype=torch.int32), sets, keep_attention=False)
+    cur = np.array([40, 1, 25])
+    seen = set()
+    for c, rec in enumerate(recs):
+        acc, corr = oracle.sample_consensus(sets[c]["p"], sets[c]["q"], sets[c]["cand"], sets[c]["uniforms"])
+        np.testing.assert_array_equal(rec["accept_len"], acc)
+        np.testing.assert_array_equal(rec["correction"], corr)
+        n = acc + (acc < 8)
+        cur = cur + n
+        np.testing.assert_array_equal(rec["cache_len"], cur)
+        for b in range(3):
+            assert rec["tokens"][b, :acc[b]].tolist() == sets[c]["cand"][b, :acc[b]].tolist()
+            if acc[b] < 8:
+                assert rec["tokens"][b, acc[b]] == corr[b]
+        seen.update(acc.tolist())
+    assert len(seen) > 2, "the near draft should give a spread of accept lengths"
+    np.testing.assert_array_equal(st["cache_len"], cur)

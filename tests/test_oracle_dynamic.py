@@ -330,3 +330,43 @@ def test_cycle_block_lengths_follow_the_rule_and_the_lengths_add_up():
                 assert np.isnan(out[b, :, rec["blk_len_in"][b]:]).all()
                 assert np.isfinite(out[b, :, :rec["blk_len_in"][b]]).all()
     assert st["blk_len"].tolist() == k.tolist()
+
+
+def test_sample_cycles_with_a_one_hot_target_are_the_greedy_cycles():
+    """With block lengths adapting, T > 0 cycles whose target is a point mass
+    at the argmax retrace the greedy cycles: same accepted prefixes (the
+    planted mismatch cut at k_b), corrections, statistics and block lengths."""
+    w = Workload("dyns", 1, 3, 4, 2, 16, 30, 8, 40, 4.0, 7, max_len=30 + 6 * 8)
+    sets, kc, vc = _cycles(w, 6, 0.7, 4)
+    g = torch.Generator().manual_seed(8)
+    tsets = []
+    for s in sets:
+        B, K, V = s["logits"].shape
+        p = torch.zeros(B, K, V)
+        p.scatter_(2, s["logits"].argmax(-1, keepdim=True), 1.0)
+        q = torch.softmax(torch.randn(B, K, V, generator=g, dtype=torch.float64), -1).float()
+        u = (torch.randint(0, 1 << 24, (B, K + 1), generator=g).double() / (1 << 24)).float()
+        tsets.append({"diff": s["diff"], "verify": s["verify"], "cand": s["cand"], "p": p, "q": q, "uniforms": u})
+    r1, s1 = oracle.decode_cycles_dyn(kc, vc, [30, 0, 12], [8, 2, 5], 2, sets, keep_attention=False)
+    r2, s2 = oracle.decode_cycles_dyn(kc, vc, [30, 0, 12], [8, 2, 5], 2, tsets, keep_attention=False)
+    for c, (a, b) in enumerate(zip(r1, r2)):
+        for n in ("accept_len", "correction", "cache_len", "tokens", "n_tokens", "accept_stat", "blk_len"):
+            np.testing.assert_array_equal(a[n], b[n], err_msg=f"cycle {c} {n}")
+    np.testing.assert_array_equal(s1["k_cache"], s2["k_cache"])
+
+
+def test_sample_cycles_with_the_draft_equal_to_the_target_grow_the_block():
+    """q = p keeps every live candidate, so a = k_b each cycle; the estimate
+    of the match rate stays at 1 and the block length climbs to K."""
+    from synth import sample_cycle_inputs
+    w = Workload("dyns2", 1, 2, 4, 2, 16, 20, 16, 30, 3.0, 9, max_len=20 + 8 * 16)
+    sets = sample_cycle_inputs(w, 8, draft_noise=0.3)
+    for s in sets:
+        s["q"] = s["p"].clone()
+    kc = torch.randn((1, 2, 2, w.capacity, 16), generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    vc = torch.randn((1, 2, 2, w.capacity, 16), generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    recs, st = oracle.decode_cycles_dyn(kc, vc, [20, 4], [1, 3], 1, sets, keep_attention=False)
+    for rec in recs:
+        np.testing.assert_array_equal(rec["accept_len"], rec["blk_len_in"])
+        assert (rec["correction"] == -1).all()
+    assert st["blk_len"].tolist() == [16, 16]
