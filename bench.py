@@ -53,6 +53,13 @@ def _parse():
     ap.add_argument("--cycle-sets", type=int, default=32,
                     help="distinct input sets the cycles rotate through (one graph round); their "
                          "first-mismatch indices are the quantiles of the acceptance law")
+    ap.add_argument("--t0-cycles", type=int, default=64,
+                    help="synthetic T>0 decode cycles timed (0 to skip): as --cycles, with the rejection-"
+                         "sampling consensus over target and draft probabilities and given uniforms")
+    ap.add_argument("--t0-sets", type=int, default=8, help="input sets the T>0 cycles rotate through")
+    ap.add_argument("--t0-noise", type=float, default=0.2,
+                    help="draft logits = target logits + N(0, noise) for the T>0 cycles (0.2 gives a "
+                         "per-candidate acceptance of about 0.92 at sigma 3, V 151936)")
     ap.add_argument("--tree-cycles", type=int, default=32,
                     help="synthetic tree-verification cycles timed (0 to skip): per cycle the diffusion "
                          "attention of every layer, top-m marginals, a best-first draft tree, its masks, the "
@@ -365,9 +372,19 @@ def cycle_sets(w, n_sets: int, accept_rate: float, device):
     return sets
 
 
+def sample_cycle_sets(w, n_sets: int, noise: float, device):
+    """Input sets of synthetic T>0 decode cycles: target and draft
+    probabilities (draft logits = target logits + N(0, noise)), candidates
+    drawn from the draft and the uniforms of the accept tests."""
+    from synth import sample_cycle_inputs
+
+    return sample_cycle_inputs(w, n_sets, draft_noise=noise, device=device)
+
+
 def time_cycles(w, kc_all, vc_all, device, n_cycles: int, n_sets: int, accept_rate: float, sets=None,
                 k_min: int = 0):
-    """Synthetic decode cycles (both views of every layer, greedy consensus,
+    """Synthetic decode cycles (both views of every layer, greedy consensus --
+    or T>0 consensus when the input sets carry probabilities -- and the
     commit) issued through dual_view_block_amd.cycle.DecodeCycles: one round of
     `n_sets` cycles is captured into a HIP graph and replayed; lengths advance
     on the device.  With k_min > 0 the block length is adaptive: every
@@ -920,6 +937,7 @@ def main():
     # one layer-major cache for all layers, with room past L for the rows the
     # synthetic decode cycles commit (the step itself reads rows [0, L) only)
     w = w.replace(max_len=max(w.capacity, w.cache_len + (args.cycles + 2 * args.cycle_sets) * w.block_k,
+                              w.cache_len + (args.t0_cycles + args.t0_sets) * w.block_k,
                               w.cache_len + (args.tree_cycles + 8) * w.block_k))
     kc_all, vc_all = model_cache(w, device)
     caches = [(kc_all[layer], vc_all[layer]) for layer in range(w.layers)]
@@ -966,6 +984,16 @@ def main():
         cyc = time_cycles(w, kc_all, vc_all, device, args.cycles, args.cycle_sets, args.accept_rate)
         print(f"[bench] cycles: {cyc['us_per_cycle']:.1f} us/cycle, {cyc['tokens_per_cycle']:.2f} tokens/cycle, "
               f"commit {cyc['commit_us']:.2f} us", file=sys.stderr, flush=True)
+
+    t0c = None
+    if args.t0_cycles > 0:
+        t0_sets = sample_cycle_sets(w, args.t0_sets, args.t0_noise, device)
+        t0c = time_cycles(w, kc_all, vc_all, device, args.t0_cycles, args.t0_sets, None, sets=t0_sets)
+        t0c.pop("accept_rate", None)
+        t0c.update(consensus="sample", draft_noise=args.t0_noise)
+        del t0_sets
+        print(f"[bench] T>0 cycles: {t0c['us_per_cycle']:.1f} us/cycle, {t0c['tokens_per_cycle']:.2f} tokens/cycle, "
+              f"{t0c['tokens_per_s']:.0f} tokens/s", file=sys.stderr, flush=True)
 
     dyn = None
     if args.dyn_k:
@@ -1049,6 +1077,8 @@ def main():
     }
     if cyc is not None:
         line["decode_cycles"] = cyc
+    if t0c is not None:
+        line["decode_cycles_t0"] = t0c
     if dyn is not None:
         line["dynamic_k"] = dyn
     if fkl is not None:
