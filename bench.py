@@ -18,6 +18,8 @@ the logits) divided by the step time.
 from __future__ import annotations
 
 import argparse
+import contextlib
+import ctypes
 import json
 import os
 import statistics
@@ -31,6 +33,39 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "attn_stream_traffic.json")
 ATTN_SOURCE = os.path.join(ROOT, "dual_view_block_amd", "csrc", "attention.hip")
 STREAM_KERNEL = "attn_stream_kernel"
 COPY_KERNEL = "copyBuffer"  # the runtime's device-to-device copy kernel
+
+
+class _Markers:
+    """roctx ranges around the bench phases, so that a trace taken with
+    `rocprofv3 --marker-trace` shows where each phase's kernels fall.  The
+    marker library of the ROCm profiler SDK is loaded if present; without it
+    every range is a no-op."""
+
+    def __init__(self):
+        self.lib = None
+        for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+            for path in (name, os.path.join("/opt/rocm/lib", name)):
+                try:
+                    lib = ctypes.CDLL(path)
+                except OSError:
+                    continue
+                lib.roctxRangePushA.argtypes, lib.roctxRangePushA.restype = [ctypes.c_char_p], ctypes.c_int
+                lib.roctxRangePop.argtypes, lib.roctxRangePop.restype = [], ctypes.c_int
+                self.lib = lib
+                return
+
+    @contextlib.contextmanager
+    def range(self, name: str):
+        if self.lib is not None:
+            self.lib.roctxRangePushA(("bench:" + name).encode())
+        try:
+            yield
+        finally:
+            if self.lib is not None:
+                self.lib.roctxRangePop()
+
+
+MARKERS = _Markers()
 
 
 def _parse():
@@ -950,8 +985,10 @@ def main():
         return
     step = Step(w, caches, device)
     splits = step.splits
-    ms, wall_ms = time_steps(step, args.steps, args.warmup, args.graph)
-    kern = time_kernels(step)
+    with MARKERS.range("steps"):
+        ms, wall_ms = time_steps(step, args.steps, args.warmup, args.graph)
+    with MARKERS.range("kernel_timing"):
+        kern = time_kernels(step)
     # where this run's streaming-kernel dispatches fall, in launch order, for
     # reading a kernel trace of the same command (bench.py --summarize-trace)
     n_l = len(step.calls["diff"]) + len(step.calls["verify"])
@@ -974,21 +1011,24 @@ def main():
             continue
         wk = w.replace(block_k=K)
         sk = Step(wk, caches, device)
-        mk, _ = time_steps(sk, args.steps, args.warmup, args.graph)
+        with MARKERS.range(f"k_sweep_K{K}"):
+            mk, _ = time_steps(sk, args.steps, args.warmup, args.graph)
         sweep[K] = mk * 1e3
         del sk
         print(f"[bench] K={K}: step {mk * 1e3:.1f} us", file=sys.stderr, flush=True)
 
     cyc = None
     if args.cycles > 0:
-        cyc = time_cycles(w, kc_all, vc_all, device, args.cycles, args.cycle_sets, args.accept_rate)
+        with MARKERS.range("decode_cycles"):
+            cyc = time_cycles(w, kc_all, vc_all, device, args.cycles, args.cycle_sets, args.accept_rate)
         print(f"[bench] cycles: {cyc['us_per_cycle']:.1f} us/cycle, {cyc['tokens_per_cycle']:.2f} tokens/cycle, "
               f"commit {cyc['commit_us']:.2f} us", file=sys.stderr, flush=True)
 
     t0c = None
     if args.t0_cycles > 0:
         t0_sets = sample_cycle_sets(w, args.t0_sets, args.t0_noise, device)
-        t0c = time_cycles(w, kc_all, vc_all, device, args.t0_cycles, args.t0_sets, None, sets=t0_sets)
+        with MARKERS.range("decode_cycles_t0"):
+            t0c = time_cycles(w, kc_all, vc_all, device, args.t0_cycles, args.t0_sets, None, sets=t0_sets)
         t0c.pop("accept_rate", None)
         t0c.update(consensus="sample", draft_noise=args.t0_noise)
         del t0_sets
@@ -997,25 +1037,29 @@ def main():
 
     dyn = None
     if args.dyn_k:
-        dyn = time_dynamic_k(w, caches, kc_all, vc_all, device, args, cyc)
+        with MARKERS.range("dynamic_k"):
+            dyn = time_dynamic_k(w, caches, kc_all, vc_all, device, args, cyc)
 
     tcy = None
     if args.tree_cycles > 0:
-        tcy = time_tree_cycles(w, kc_all, vc_all, device, args.tree_cycles)
+        with MARKERS.range("tree_cycles"):
+            tcy = time_tree_cycles(w, kc_all, vc_all, device, args.tree_cycles)
         print(f"[bench] tree cycles: {tcy['us_per_cycle']:.1f} us/cycle; masked verify call "
               f"{tcy['masked_verify_call_us']:.1f} us, topk {tcy['topk_us']:.1f} us, build {tcy['tree_build_us']:.1f} "
               f"us, tree consensus {tcy['tree_consensus_us']:.1f} us", file=sys.stderr, flush=True)
 
     tra = None
     if args.train_attn:
-        tra = time_train_attn(w, device)
+        with MARKERS.range("train_attention"):
+            tra = time_train_attn(w, device)
         print(f"[bench] training attention L2048 x 256 blocks: forward {tra['forward']['us']:.1f} us "
               f"({tra['forward']['tflops']:.0f} TFLOP/s), backward {tra['backward']['us']:.1f} us "
               f"({tra['backward']['tflops']:.0f} TFLOP/s)", file=sys.stderr, flush=True)
 
     fkl = None
     if args.kl_rows > 0:
-        fkl = time_forward_kl(device, args.kl_rows, w.vocab)
+        with MARKERS.range("forward_kl"):
+            fkl = time_forward_kl(device, args.kl_rows, w.vocab)
         print(f"[bench] forward KL {fkl['rows']}x{fkl['vocab']} bf16: loss {fkl['loss']['us']:.1f} us "
               f"({fkl['loss']['achieved_gbs']:.0f} GB/s), loss+grad {fkl['loss_and_grad']['us']:.1f} us "
               f"({fkl['loss_and_grad']['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
@@ -1024,7 +1068,8 @@ def main():
     if args.configs:
         del step
         torch.cuda.empty_cache()
-        cfg = time_configs(device, args.steps, args.warmup)
+        with MARKERS.range("other_configs"):
+            cfg = time_configs(device, args.steps, args.warmup)
 
     step_bytes = 2 * w.layers * attn_bytes(w) + greedy_bytes(w)
     value = step_bytes / (ms * 1e-3) / 1e12
@@ -1090,7 +1135,8 @@ def main():
     if cfg is not None:
         line["other_configs"] = cfg
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, caches, device)
+        with MARKERS.range("cpu_baseline"):
+            line["cpu_baseline"] = cpu_baseline(w, caches, device)
     print(json.dumps(line), flush=True)
 
 
