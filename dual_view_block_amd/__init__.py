@@ -169,6 +169,10 @@ class PreparedAttention:
     def __init__(self, mode, q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace,
                  softmax_scale: float = 0.0, block_mask=None, blk_len=None):
         _check_attn(q, k_blk, v_blk, k_cache, v_cache, cache_len)
+        _need(out, "out", torch.bfloat16, tuple(q.shape), q.device)
+        if lse is not None:
+            _need(lse, "lse", torch.float32, tuple(q.shape[:3]), q.device)
+        _need(workspace, "workspace", torch.uint8, None, q.device)
         self.desc = attn_desc(q, k_cache, softmax_scale)
         self._keep = (q, k_blk, v_blk, k_cache, v_cache, cache_len, out, lse, workspace, block_mask, blk_len)
         nbytes = orthrus_attn_workspace_size(self.desc)
@@ -228,6 +232,11 @@ class PreparedGreedy:
         dev = logits.device
         _need(logits, "logits", torch.float32, (B, K, V))
         _need(cand, "cand", torch.int32, (B, K), dev)
+        _need(accept_len, "accept_len", torch.int32, (B,), dev)
+        _need(correction, "correction", torch.int32, (B,), dev)
+        if row_argmax is not None:
+            _need(row_argmax, "row_argmax", torch.int32, (B, K), dev)
+        _need(workspace, "workspace", torch.uint8, None, dev)
         nbytes = orthrus_consensus_workspace_size(B, K, V)
         if workspace.numel() < nbytes:
             raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")
@@ -258,6 +267,9 @@ class PreparedSample:
         _need(q_draft, "q_draft", torch.float32, (B, K, V), dev)
         _need(cand, "cand", torch.int32, (B, K), dev)
         _need(uniforms, "uniforms", torch.float32, (B, K + 1), dev)
+        _need(accept_len, "accept_len", torch.int32, (B,), dev)
+        _need(correction, "correction", torch.int32, (B,), dev)
+        _need(workspace, "workspace", torch.uint8, None, dev)
         nbytes = orthrus_consensus_workspace_size(B, K, V)
         if workspace.numel() < nbytes:
             raise ValueError(f"workspace has {workspace.numel()} bytes, needs {nbytes}")

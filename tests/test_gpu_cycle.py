@@ -284,3 +284,32 @@ def test_sample_decode_cycles_graph_replay_matches_eager():
             assert torch.equal(a, b), f"round {rnd}"
         assert torch.equal(gk, ek) and torch.equal(gv, ev), f"round {rnd}"
     print(f"sample graph replay: lengths {el.cpu().tolist()}", flush=True)
+
+
+def test_prepared_calls_reject_wrong_outputs():
+    """The prepared calls check their output and workspace tensors (dtype,
+    shape, device) before any launch: a short output would be written past
+    its end."""
+    B, K, V = 2, 4, 100
+    i32 = dict(dtype=torch.int32, device=DEV)
+    logits = torch.zeros((B, K, V), device=DEV)
+    cand = torch.zeros((B, K), **i32)
+    ws = torch.empty(max(dvb.orthrus_consensus_workspace_size(B, K, V), 16), dtype=torch.uint8, device=DEV)
+    good = dict(accept_len=torch.empty(B, **i32), correction=torch.empty(B, **i32))
+    dvb.PreparedGreedy(logits, cand, good["accept_len"], None, good["correction"], ws)
+    with pytest.raises(ValueError):
+        dvb.PreparedGreedy(logits, cand, torch.empty(B - 1, **i32), None, good["correction"], ws)
+    with pytest.raises(TypeError):
+        dvb.PreparedGreedy(logits, cand, good["accept_len"], None, torch.empty(B, dtype=torch.int64, device=DEV), ws)
+    u = torch.zeros((B, K + 1), device=DEV)
+    with pytest.raises(ValueError):
+        dvb.PreparedSample(logits, logits, cand, u, good["accept_len"], torch.empty(B + 1, **i32), ws)
+    w = Workload("chk", 1, B, 4, 2, 64, 100, K, V, 1.0, 3)
+    from synth import attention_inputs
+    x = attention_inputs(w, device=DEV)
+    desc = dvb.attn_desc(x["q"], x["k_cache"])
+    aws = torch.empty(max(dvb.orthrus_attn_workspace_size(desc), 16), dtype=torch.uint8, device=DEV)
+    with pytest.raises(ValueError):
+        dvb.PreparedAttention(dvb.ORTHRUS_MASK_VERIFY_CAUSAL, x["q"], x["k_blk"], x["v_blk"], x["k_cache"],
+                              x["v_cache"], x["cache_len"], torch.empty_like(x["q"])[:, :, :-1].contiguous(),
+                              None, aws)
