@@ -313,3 +313,32 @@ def test_prepared_calls_reject_wrong_outputs():
         dvb.PreparedAttention(dvb.ORTHRUS_MASK_VERIFY_CAUSAL, x["q"], x["k_blk"], x["v_blk"], x["k_cache"],
                               x["v_cache"], x["cache_len"], torch.empty_like(x["q"])[:, :, :-1].contiguous(),
                               None, aws)
+
+
+def test_sample_decode_cycles_ragged_batch_of_16():
+    """T > 0 cycles over 16 sequences of ragged length (0 to 3000 keys, the
+    balanced placement of the streaming kernel), a far draft (noise 1.0, so
+    that accept lengths spread over the whole range): every cycle's integers
+    and the final cache bit-exact against the oracle's cycles."""
+    lens = [int(v) for v in np.random.default_rng(41).integers(0, 3000, size=16)]
+    lens[3], lens[7] = 0, 1
+    w = Workload("scyc_b16", 2, 16, 8, 2, 64, 3000, 16, 512, 3.0, 34, max_len=3000 + 5 * 16)
+    sets = sample_cycle_inputs(w, 5, draft_noise=1.0, seed_offset=11)
+    kc, vc = _cycle_setup(w, 1, lens, 0.5, seed=17)[1:3]
+    L = torch.tensor(lens, dtype=torch.int32)
+    recs, state = oracle.decode_cycles(kc, vc, L, sets, keep_attention=False)
+    dkc, dvc, dlen = kc.to(DEV), vc.to(DEV), L.to(DEV)
+    drv = DecodeCycles(dkc, dvc, dlen, _to_dev(sets))
+    drv.run(len(sets))
+    torch.cuda.synchronize()
+    seen = set()
+    for c, rec in enumerate(recs):
+        for name in ("accept_len", "correction", "next_anchor", "tokens", "n_tokens"):
+            got = getattr(drv, name)[c].cpu().numpy()
+            assert np.array_equal(got, rec[name]), f"cycle {c} {name}: {got} vs {rec[name]}"
+        seen.update(rec["accept_len"].tolist())
+    assert len(seen) >= 4, seen
+    assert dlen.cpu().tolist() == state["cache_len"].tolist()
+    assert torch.equal(dkc.cpu(), bits_to_bf16(state["k_cache"]))
+    assert torch.equal(dvc.cpu(), bits_to_bf16(state["v_cache"]))
+    print(f"ragged T>0 cycles: accept lengths seen {sorted(seen)}", flush=True)
