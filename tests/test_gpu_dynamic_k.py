@@ -435,3 +435,42 @@ def test_sample_decode_cycles_with_adaptive_block_lengths():
     assert torch.equal(dkc.cpu(), bits_to_bf16(st["k_cache"]))
     assert torch.equal(dvc.cpu(), bits_to_bf16(st["v_cache"]))
     print("T>0 block lengths per cycle:", [r["blk_len_in"].tolist() for r in recs], flush=True)
+
+
+def test_adaptive_sample_cycles_graph_replay_matches_eager():
+    """T > 0 cycles with adaptive block lengths, captured as a round of 3 and
+    replayed twice with eager work and synchronisations between the replays:
+    lengths, block lengths, statistics and cache equal 6 eager cycles bit for
+    bit after each replay."""
+    from synth import sample_cycle_inputs
+    w = Workload("dscyc_g", 2, 2, 8, 2, 128, 600, 32, 2048, 3.0, 27, max_len=600 + 6 * 32)
+    sets = _to_dev(sample_cycle_inputs(w, 3, draft_noise=0.5, seed_offset=19))
+    _, kc, vc = _cycle_case(w, 1, 0.5, 21)
+    lens, kl = [600, 41], [32, 8]
+
+    def state():
+        return (kc.to(DEV), vc.to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                torch.tensor(kl, dtype=torch.int32, device=DEV))
+
+    ek, ev, el, eb = state()
+    eager = DecodeCycles(ek, ev, el, sets, blk_len=eb, k_min=2)
+    gk, gv, gl, gb = state()
+    graphed = DecodeCycles(gk, gv, gl, sets, blk_len=gb, k_min=2)
+    graphed.run(1)  # warm the calls once, then restore the state before capture
+    torch.cuda.synchronize()
+    for t, s in zip((gk, gv, gl, gb), state()):
+        t.copy_(s)
+    graphed.accept_stat.zero_()
+    graphed.capture()
+    for rnd in range(2):
+        eager.run(3, first_cycle=3 * rnd)
+        torch.cuda.synchronize()
+        graphed.replay()
+        torch.cuda.synchronize()
+        _ = gk.float().sum()
+        torch.cuda.synchronize()
+        assert gl.cpu().tolist() == el.cpu().tolist(), rnd
+        assert gb.cpu().tolist() == eb.cpu().tolist(), rnd
+        assert graphed.accept_stat.cpu().tolist() == eager.accept_stat.cpu().tolist(), rnd
+        assert torch.equal(gk, ek) and torch.equal(gv, ev), rnd
+    print(f"T>0 graph replay: lengths {el.cpu().tolist()}, block lengths {eb.cpu().tolist()}", flush=True)
