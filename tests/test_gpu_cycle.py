@@ -237,6 +237,9 @@ def _check_cycles(w, drv, recs, state, dkc, dvc, dlen):
     # (workload, initial lengths, draft noise, cycles)
     (Workload("scyc_small", 2, 2, 4, 2, 64, 300, 4, 1000, 4.0, 31, max_len=300 + 6 * 4), [300, 77], 0.5, 6),
     (Workload("scyc_gqa4", 2, 3, 8, 2, 128, 700, 32, 4096, 3.0, 32, max_len=700 + 4 * 32), [700, 0, 129], 0.3, 4),
+    # K 64 and 128: two and four row groups of 128 query rows per KV head
+    (Workload("scyc_k64", 2, 2, 8, 2, 128, 900, 64, 2048, 3.0, 35, max_len=900 + 3 * 64), [900, 333], 0.2, 3),
+    (Workload("scyc_k128", 1, 2, 8, 2, 64, 600, 128, 1024, 3.0, 36, max_len=600 + 3 * 128), [600, 5], 0.1, 3),
 ])
 def test_sample_decode_cycles_match_oracle(case):
     """T > 0 cycles (rejection-sampling consensus over a near draft): every
