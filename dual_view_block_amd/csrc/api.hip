@@ -44,6 +44,9 @@ orthrus_status check_desc(const orthrus_attn_desc* d) {
   if (!(isfinite(d->softmax_scale) && d->softmax_scale >= 0.0f)) return ORTHRUS_ERR_BAD_SHAPE;
   if (d->head_dim != 64 && d->head_dim != 128) return ORTHRUS_ERR_UNSUPPORTED;
   if (d->block_k > 128) return ORTHRUS_ERR_UNSUPPORTED;
+  // cache positions, split bounds and tile starts are int in the kernels: with
+  // at most 2^30 rows every such sum stays below 2^31
+  if (d->max_len > (1 << 30)) return ORTHRUS_ERR_UNSUPPORTED;
   // every element offset must fit comfortably in 63 bits and every grid dimension in range
   const long long rows = (long long)(d->n_q_heads / d->n_kv_heads) * d->block_k;
   if ((long long)d->batch * d->n_kv_heads > 65535LL || rows > (1LL << 20)) return ORTHRUS_ERR_BAD_SHAPE;
@@ -59,7 +62,7 @@ AttnPlan make_plan(const orthrus_attn_desc* d) {
   p.row_groups = (p.rows + p.rows_per_wg - 1) / p.rows_per_wg;
   const long long groups = (long long)d->batch * d->n_kv_heads * p.row_groups;
   long long s = kPlanCUs / groups;
-  const long long max_tiles = (d->max_len + kTileKeys - 1) / kTileKeys;
+  const long long max_tiles = ((long long)d->max_len + kTileKeys - 1) / kTileKeys;
   if (s > max_tiles) s = max_tiles;
   if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
@@ -165,9 +168,13 @@ orthrus_status run_attn(const orthrus_attn_desc* d, int mode, const uint16_t* q,
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_HIP;
 }
 
+// Vocabularies up to 2^30 entries: every int sum of a vocabulary index and a
+// chunk or stride length in the kernels and plans then stays below 2^31.
+constexpr int32_t kMaxVocab = 1 << 30;
+
 orthrus_status check_consensus_sizes(int32_t B, int32_t K, int32_t V) {
   if (B < 1 || K < 1 || V < 1) return ORTHRUS_ERR_BAD_SHAPE;
-  if (K > 128) return ORTHRUS_ERR_UNSUPPORTED;
+  if (K > 128 || V > kMaxVocab) return ORTHRUS_ERR_UNSUPPORTED;
   if ((long long)B * K > 65535LL) return ORTHRUS_ERR_BAD_SHAPE;
   return ORTHRUS_OK;
 }
@@ -181,7 +188,7 @@ ConsensusPlan make_consensus_plan(int32_t B, int32_t K, int32_t V) {
   if (gc > gmax) gc = gmax;
   if (gc < 1) gc = 1;
   p.greedy_chunks = (int)gc;
-  long long sc = (V + 4095) / 4096;
+  long long sc = ((long long)V + 4095) / 4096;
   if (sc > 256) sc = 256;
   if (sc < 1) sc = 1;
   p.sample_chunks = (int)sc;
@@ -196,15 +203,17 @@ orthrus_status check_commit_desc(const orthrus_commit_desc* d) {
   if (d->n_layers < 1 || d->batch < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->block_k < 1 ||
       d->max_len < 0)
     return ORTHRUS_ERR_BAD_SHAPE;
-  if (d->head_dim % 8 != 0 || d->head_dim > 1024 || d->block_k > 1024) return ORTHRUS_ERR_UNSUPPORTED;
-  if ((long long)d->n_layers * d->batch * d->n_kv_heads > 0x7fffffffLL) return ORTHRUS_ERR_BAD_SHAPE;
+  if (d->head_dim % 8 != 0 || d->head_dim > 1024 || d->block_k > 1024 || d->max_len > (1 << 30))
+    return ORTHRUS_ERR_UNSUPPORTED;
+  const long long lb = (long long)d->n_layers * d->batch;  // below 2^62: no overflow
+  if (lb > 0x7fffffffLL || lb * d->n_kv_heads > 0x7fffffffLL) return ORTHRUS_ERR_BAD_SHAPE;
   return ORTHRUS_OK;
 }
 
 orthrus_status check_kl_sizes(int32_t rows, int32_t vocab, int dtype) {
   if (dtype != ORTHRUS_DTYPE_F32 && dtype != ORTHRUS_DTYPE_BF16) return ORTHRUS_ERR_BAD_SHAPE;
   if (rows < 1 || vocab < 1) return ORTHRUS_ERR_BAD_SHAPE;
-  if (rows > 65535) return ORTHRUS_ERR_UNSUPPORTED;
+  if (rows > 65535 || vocab > kMaxVocab) return ORTHRUS_ERR_UNSUPPORTED;
   return ORTHRUS_OK;
 }
 
@@ -718,7 +727,7 @@ orthrus_status orthrus_cache_commit_path(const orthrus_commit_desc* d, uint16_t*
 }
 
 size_t orthrus_topk_workspace_size(int32_t rows, int32_t vocab, int32_t m) {
-  if (rows < 1 || vocab < 1 || m < 1 || m > 32 || m > vocab || rows > 65535) return 0;
+  if (rows < 1 || vocab < 1 || m < 1 || m > 32 || m > vocab || rows > 65535 || vocab > kMaxVocab) return 0;
   const size_t chunks = (size_t)topk_chunks(vocab);
   return round_up((size_t)rows * chunks * ((size_t)m * 8 + 8), kAlign);
 }
@@ -726,7 +735,7 @@ size_t orthrus_topk_workspace_size(int32_t rows, int32_t vocab, int32_t m) {
 orthrus_status orthrus_topk_logprobs(int32_t rows, int32_t vocab, int32_t m, const float* logits, float* logp,
                                      int32_t* idx, void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 1 || vocab < 1 || m < 1 || m > vocab) return ORTHRUS_ERR_BAD_SHAPE;
-  if (m > 32 || rows > 65535) return ORTHRUS_ERR_UNSUPPORTED;
+  if (m > 32 || rows > 65535 || vocab > kMaxVocab) return ORTHRUS_ERR_UNSUPPORTED;
   if (!logits || !logp || !idx || !workspace) return ORTHRUS_ERR_NULL_PTR;
   if (!aligned4(logits) || !aligned4(logp) || !aligned4(idx) || !aligned16(workspace))
     return ORTHRUS_ERR_MISALIGNED;

@@ -74,7 +74,8 @@ typedef struct {
   int32_t n_kv_heads;    /* Hkv >= 1; q head h reads KV head h / (Hq / Hkv) */
   int32_t head_dim;      /* D, 64 or 128 (other values: ORTHRUS_ERR_UNSUPPORTED) */
   int32_t block_k;       /* K, 1..128 block positions (anchor + K-1 masks) */
-  int32_t max_len;       /* cache capacity per sequence = row stride of the cache */
+  int32_t max_len;       /* cache capacity per sequence = row stride of the cache,
+                            0..2^30 (more: ORTHRUS_ERR_UNSUPPORTED) */
   float softmax_scale;   /* 0 -> 1/sqrt(D) */
 } orthrus_attn_desc;
 
@@ -222,7 +223,8 @@ size_t orthrus_consensus_workspace_size(int32_t batch, int32_t block_k, int32_t 
  *   correction int32 [B]       argmax of row a if a < K, else -1 (no bonus)
  * argmax: lowest index among equal maxima; NaN ranks above every number (first
  * NaN wins); -0 equals +0.  Results are bit-exact (comparisons only).
- * Sizes: 1 <= B, 1 <= K <= 128, 1 <= V < 2^31. */
+ * Sizes: 1 <= B, 1 <= K <= 128, B * K <= 65535, 1 <= V <= 2^30 (larger K or
+ * V: ORTHRUS_ERR_UNSUPPORTED; larger B * K: ORTHRUS_ERR_BAD_SHAPE). */
 orthrus_status orthrus_consensus_greedy(int32_t batch, int32_t block_k, int32_t vocab,
                                         const float* logits, const int32_t* cand,
                                         int32_t* accept_len, int32_t* row_argmax,
@@ -259,7 +261,8 @@ orthrus_status orthrus_consensus_greedy_dyn(int32_t batch, int32_t block_k, int3
  *                             S = sum w, m = floor(u_K * 2^24).
  * Integer arithmetic makes the result bit-exact and independent of reduction
  * order.  Rows must be probability vectors (each summing to at most 8);
- * a cand outside [0, V) counts as a rejection. */
+ * a cand outside [0, V) counts as a rejection.  Sizes as for
+ * orthrus_consensus_greedy. */
 orthrus_status orthrus_consensus_sample(int32_t batch, int32_t block_k, int32_t vocab,
                                         const float* p_target, const float* q_draft,
                                         const int32_t* cand, const float* uniforms,
@@ -291,7 +294,8 @@ typedef struct {
   int32_t n_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;    /* D, a multiple of 8, at most 1024 */
   int32_t block_k;     /* K, 1..1024 */
-  int32_t max_len;     /* cache capacity per sequence = row stride of the cache */
+  int32_t max_len;     /* cache capacity per sequence = row stride of the cache,
+                          0..2^30 (more: ORTHRUS_ERR_UNSUPPORTED) */
 } orthrus_commit_desc;
 
 /* Close one decode cycle on the device: write the verified rows of the AR
@@ -388,8 +392,8 @@ size_t orthrus_kl_workspace_size(int32_t rows, int32_t vocab, int32_t dtype);
  *              registers), owned by the caller; no initialisation needed.
  * Logits must be finite; no temperature is applied (the caller scales the
  * logits for one).  Sums run in fp32 in a fixed order, so results are
- * deterministic.  Rows are contiguous with stride V; rows up to 65535
- * (more: ORTHRUS_ERR_UNSUPPORTED).  grad may alias neither input. */
+ * deterministic.  Rows are contiguous with stride V; rows up to 65535 and
+ * V up to 2^30 (more: ORTHRUS_ERR_UNSUPPORTED).  grad may alias neither input. */
 orthrus_status orthrus_forward_kl(int32_t rows, int32_t vocab, int32_t dtype,
                                   const void* target_logits, const void* draft_logits, float* kl,
                                   void* grad, float grad_scale, void* workspace,
@@ -472,7 +476,7 @@ orthrus_status orthrus_train_attn_bwd(const orthrus_train_attn_desc* d, const ui
  * marginals a draft tree is built from): idx = the m largest logits (ties:
  * lower index first), logp = logit - ln sum_v exp(logit_v), descending.
  *   logits fp32 [rows, V];  logp fp32 [rows, m];  idx int32 [rows, m]
- * 1 <= m <= min(32, V); rows <= 65535.  Workspace: orthrus_topk_workspace_size
+ * 1 <= m <= min(32, V); rows <= 65535; V <= 2^30.  Workspace: orthrus_topk_workspace_size
  * (0 if the sizes are invalid). */
 size_t orthrus_topk_workspace_size(int32_t rows, int32_t vocab, int32_t m);
 orthrus_status orthrus_topk_logprobs(int32_t rows, int32_t vocab, int32_t m, const float* logits,

@@ -297,3 +297,102 @@ def test_dynamic_block_entry_points_check_arguments_on_the_host():
     assert commit(k_min=0) == _lib.ORTHRUS_ERR_BAD_SHAPE
     assert commit(k_min=33) == _lib.ORTHRUS_ERR_BAD_SHAPE
     assert commit(blk=P + 2) == _lib.ORTHRUS_ERR_MISALIGNED
+
+
+# ---------------------------------------------------- randomized host checks ----
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_I32 = st.one_of(st.integers(-3, 300), st.sampled_from([0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 4096,
+                                                         65535, 65536, 1 << 20, (1 << 31) - 1, -(1 << 31)]))
+
+
+@settings(max_examples=300, deadline=None)
+@given(batch=_I32, hq=_I32, hkv=_I32, d=st.sampled_from([0, 32, 64, 96, 128, 256, -64]), k=_I32,
+       max_len=_I32, scale=st.sampled_from([0.0, 0.088, 1.0, -1.0, float("nan"), float("inf")]),
+       mode=st.integers(-1, 3))
+def test_attention_descriptors_at_random_never_launch_without_a_gpu(batch, hq, hkv, d, k, max_len, scale, mode):
+    """Any descriptor: the size queries agree on which ones are accepted, an
+    accepted one gets a split count in [1, 64] and a workspace that holds its
+    split partials, and a call with valid-looking pointers and that workspace
+    ends in a documented status -- ORTHRUS_ERR_HIP for an accepted one, as
+    there is no GPU in this process -- without reaching a launch.  Under the
+    host sanitizers (tests/test_abi_hostsan.py) this also checks the planning
+    arithmetic for overflow and out-of-range reads."""
+    lib = _lib.load()
+    desc = _desc(batch=batch, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, block_k=k, max_len=max_len,
+                 softmax_scale=scale)
+    ws = lib.orthrus_attn_workspace_size(ctypes.byref(desc))
+    splits = lib.orthrus_attn_num_splits(ctypes.byref(desc))
+    assert (ws == 0) == (splits == -1), (ws, splits)
+    if ws:
+        assert 1 <= splits <= 64
+        rows = (hq // hkv) * k
+        per_wg = 32 if rows <= 32 else (64 if rows <= 64 else 128)
+        groups = batch * hkv * -(-rows // per_wg)
+        assert ws >= groups * splits * per_wg * (8 + 2 * d)
+    st_ = _attn_call(desc, mode, ws_bytes=max(ws, 16))
+    documented = {_lib.ORTHRUS_ERR_NULL_PTR, _lib.ORTHRUS_ERR_BAD_SHAPE, _lib.ORTHRUS_ERR_UNSUPPORTED,
+                  _lib.ORTHRUS_ERR_HIP, _lib.ORTHRUS_ERR_WORKSPACE_TOO_SMALL, _lib.ORTHRUS_ERR_MISALIGNED}
+    assert st_ in documented, st_
+    if ws and mode in (0, 1):
+        assert st_ == _lib.ORTHRUS_ERR_HIP
+
+
+@settings(max_examples=200, deadline=None)
+@given(batch=_I32, k=_I32, vocab=_I32)
+def test_consensus_sizes_at_random(batch, k, vocab):
+    """Consensus workspace sizes for any (B, K, V): zero exactly for the
+    shapes the header rules out (B < 1, K outside [1, 128], B K > 65535,
+    V outside [1, 2^30]), and a valid call without a GPU ends in
+    ORTHRUS_ERR_HIP before any launch.  Under the host sanitizers this found
+    an int overflow in the sampler's plan at V = 2^31 - 1."""
+    lib = _lib.load()
+    ws = lib.orthrus_consensus_workspace_size(batch, k, vocab)
+    ok = batch >= 1 and 1 <= k <= 128 and batch * k <= 65535 and 1 <= vocab <= 1 << 30
+    assert (ws > 0) == ok, (batch, k, vocab, ws)
+    if ok:
+        st_ = lib.orthrus_consensus_greedy(batch, k, vocab, 4096, 4096, 4096, None, 4096, 4096, ws, None)
+        assert st_ == _lib.ORTHRUS_ERR_HIP, st_
+
+
+@settings(max_examples=200, deadline=None)
+@given(rows=_I32, vocab=_I32, dtype=st.integers(-1, 3), m=_I32)
+def test_kl_and_topk_sizes_at_random(rows, vocab, dtype, m):
+    """Workspace queries of the forward KL and of the top-m marginals for any
+    sizes: zero exactly outside the documented ranges (rows in [1, 65535], V in
+    [1, 2^30], a known dtype; 1 <= m <= min(32, V))."""
+    lib = _lib.load()
+    kl_ok = 1 <= rows <= 65535 and 1 <= vocab <= 1 << 30 and dtype in (0, 1)
+    assert (lib.orthrus_kl_workspace_size(rows, vocab, dtype) > 0) == kl_ok
+    tk_ok = 1 <= rows <= 65535 and 1 <= vocab <= 1 << 30 and 1 <= m <= min(32, vocab)
+    assert (lib.orthrus_topk_workspace_size(rows, vocab, m) > 0) == tk_ok
+
+
+def test_extreme_sizes_are_refused_without_overflow():
+    """Sizes at the ends of int32 (regressions: the host planning summed a
+    length or a vocabulary with a tile or chunk size in int, and multiplied
+    three commit dimensions in 64 bits, both past their range; under the host
+    sanitizers (tests/test_abi_hostsan.py) an overflow fails this test)."""
+    lib = _lib.load()
+    big = (1 << 31) - 1
+    for max_len in (big, (1 << 30) + 1):
+        d = _desc(max_len=max_len)
+        assert lib.orthrus_attn_workspace_size(ctypes.byref(d)) == 0
+        assert lib.orthrus_attn_num_splits(ctypes.byref(d)) == -1
+        assert _attn_call(d) == _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_attn_workspace_size(ctypes.byref(_desc(max_len=1 << 30))) > 0
+    for v in (big, (1 << 30) + 1):
+        assert lib.orthrus_consensus_workspace_size(1, 32, v) == 0
+        assert lib.orthrus_kl_workspace_size(8, v, 1) == 0
+        assert lib.orthrus_topk_workspace_size(8, v, 4) == 0
+        assert lib.orthrus_consensus_greedy(1, 32, v, 4096, 4096, 4096, None, 4096, 4096, 1 << 40, None) == \
+            _lib.ORTHRUS_ERR_UNSUPPORTED
+    assert lib.orthrus_consensus_workspace_size(1, 32, 1 << 30) > 0
+    p = [1 << 20] * 12
+    for fields, expected in ((dict(n_layers=big, batch=big, n_kv_heads=big), _lib.ORTHRUS_ERR_BAD_SHAPE),
+                             (dict(n_layers=65536, batch=65536, n_kv_heads=1), _lib.ORTHRUS_ERR_BAD_SHAPE),
+                             (dict(max_len=big), _lib.ORTHRUS_ERR_UNSUPPORTED)):
+        base = dict(n_layers=36, batch=1, n_kv_heads=8, head_dim=128, block_k=32, max_len=36864)
+        base.update(fields)
+        cd = _lib.CommitDesc(**base)
+        assert lib.orthrus_cache_commit(ctypes.byref(cd), *p) == expected, fields
