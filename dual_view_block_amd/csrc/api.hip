@@ -57,7 +57,9 @@ AttnPlan make_plan(const orthrus_attn_desc* d) {
   AttnPlan p{};
   const int G = d->n_q_heads / d->n_kv_heads;
   p.rows = G * d->block_k;
-  p.qblocks = p.rows <= 32 ? 1 : (p.rows <= 64 ? 2 : 4);
+  // more than 128 rows: 256-row work-groups whose waves each take a query
+  // block over whole tiles, so the cache is streamed once per 256 rows
+  p.qblocks = p.rows <= 32 ? 1 : (p.rows <= 64 ? 2 : (p.rows <= 128 || env_int("ORTHRUS_ROWS128", 0) == 1 ? 4 : 8));
   p.rows_per_wg = 32 * p.qblocks;
   p.row_groups = (p.rows + p.rows_per_wg - 1) / p.rows_per_wg;
   const long long groups = (long long)d->batch * d->n_kv_heads * p.row_groups;

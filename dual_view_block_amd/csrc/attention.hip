@@ -10,7 +10,8 @@
 // Work layout.  grid = (S splits, row groups, B * Hkv); one work-group of 8
 // waves (512 threads, two waves per SIMD) per CU.  A work-group owns one
 // contiguous chunk of the (b, g) cache rows and up to 128 query rows (4
-// blocks of 32); split 0 also takes the K block keys as one extra masked
+// blocks of 32), or 256 (8 blocks, one per wave over whole tiles) when a KV
+// head has more than 128; split 0 also takes the K block keys as one extra masked
 // tile, before its cache tiles, so that the block is computed while the first
 // cache tile is on its way from HBM.  Work-groups are numbered so that the
 // (b, g) groups interleave and the block-carrying splits are dispatched
@@ -373,7 +374,12 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   constexpr int OPITCH = ROWB + 16;
   static_assert(CPT >= 1 && HMB >= 1, "tile and head_dim fit the work-group");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[REGION0 + 128 * OPITCH];
+  // NQB 8 (256 rows): every wave takes its own query block over the whole
+  // tile, both key halves one after the other, so no two waves share a row
+  // and the key halves need no combine at the end
+  constexpr bool WT = NQB == 8;
+  constexpr int STG_ROWS = NQB > 4 ? 32 * NQB : 128;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[REGION0 + STG_ROWS * OPITCH];
   __shared__ float2 xstat[8][32];
 
   const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
@@ -384,8 +390,8 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = w >> 1;  // query block
-  const int kh = w & 1;   // key half of every tile
+  const int qb = WT ? w : w >> 1;  // query block
+  const int kh = WT ? 0 : w & 1;   // key half of every tile (both halves with WT)
   const int half = lane >> 5;
   // block_k rows per q head in memory; kb of them live (the rows are packed
   // h * kb + i), R live rows per (sequence, KV head)
@@ -482,8 +488,8 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   // krow sits at byte 16 * (chunk ^ f(krow)) of the row, i.e. at (32*ds) ^
   // kswz with kswz = 16 * (half ^ f(krow)) < ROWB.
   const uint32_t kbase = (uint32_t)(kh * HALFB + krow * ROWB) + 16u * (uint32_t)swz_k<DCH>(krow, half);
-  auto load_k = [&](int stage, bf16x8 (&kf)[NDS]) __attribute__((always_inline)) {
-    const uint32_t base = (uint32_t)(stage * STAGEB) + kbase;
+  auto load_k = [&](int stage, int khx, bf16x8 (&kf)[NDS]) __attribute__((always_inline)) {
+    const uint32_t base = (uint32_t)(stage * STAGEB + (khx - kh) * HALFB) + kbase;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) kf[ds] = *reinterpret_cast<const bf16x8*>(smem + (base ^ (32u * ds)));
   };
@@ -502,11 +508,11 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     const int d0 = 32 * mb + 16 * (grp16 & 1) + 4 * qq;
     vbase[mb] = (uint32_t)(TILEB + kh * HALFB + key0 * ROWB + swz_v<DCH>(key0, d0 >> 3) * 16 + (d0 & 7) * 2);
   }
-  auto load_v = [&](int stage, bf16x8 (&vf)[2][NMB]) __attribute__((always_inline)) {
+  auto load_v = [&](int stage, int khx, bf16x8 (&vf)[2][NMB]) __attribute__((always_inline)) {
     uint32_t vb[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) {
-      vb[mb] = (uint32_t)(stage * STAGEB) + vbase[mb];
+      vb[mb] = (uint32_t)(stage * STAGEB + (khx - kh) * HALFB) + vbase[mb];
       asm("" : "+v"(vb[mb]));
     }
 #pragma unroll
@@ -521,14 +527,14 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
       }
   };
   // register r holds key 32*kh + 8*(r/4) + 4*half + r%4 of the tile
-  auto mask_scores = [&](f32x16& s, int nvalid, bool block_tile, int key0) __attribute__((always_inline)) {
+  auto mask_scores = [&](f32x16& s, int khx, int nvalid, bool block_tile, int key0) __attribute__((always_inline)) {
     int lim = nvalid;
     if (block_tile && a.causal) lim = min(lim, qrow_i + 1 - key0);
-    int rel = lim - 4 * half - 32 * kh;
+    int rel = lim - 4 * half - 32 * khx;
     asm volatile("" : "+v"(rel));
     if (EXPL && block_tile) {
       const int mrow = min(qrow, R - 1) % kb;
-      const uint32_t em = (uint32_t)(a.blk_mask[(size_t)b * K + mrow] >> (4 * half + 32 * kh));
+      const uint32_t em = (uint32_t)(a.blk_mask[(size_t)b * K + mrow] >> (4 * half + 32 * khx));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = 8 * (r >> 2) + (r & 3);
@@ -568,12 +574,17 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) qf[ds] = active ? qp[2 * ds + half] : bf16x8{};
   }
-  // One tile of this wave's half: S^T, mask, softmax, O^T += V^T P^T.
+  // One tile of this wave's half (both halves in turn with WT): S^T, mask,
+  // softmax, O^T += V^T P^T.
   auto compute = [&](int st, int t) __attribute__((always_inline)) {
     const int nval = tile_valid(t);
-    if (!active || nval <= 32 * kh) return;  // no real key in this half
+    if (!active) return;
+#pragma unroll
+    for (int hk = 0; hk < (WT ? 2 : 1); ++hk) {
+    const int khx = WT ? hk : kh;
+    if (nval <= 32 * khx) break;  // no real key in this half (or past it)
     bf16x8 kf[NDS];
-    load_k(st, kf);
+    load_k(st, khx, kf);
     // all K fragment reads in flight before the first MFMA (left alone, the
     // scheduler keeps two or three and each MFMA waits on its own read)
     __builtin_amdgcn_sched_barrier(0);
@@ -583,10 +594,10 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) s = mfma32(kf[ds], qf[ds], s);
     bf16x8 vf[2][NMB];
-    load_v(st, vf);
+    load_v(st, khx, vf);
     if (t < sr.nblk || t - sr.nblk >= nfull) {
       const bool blk = t < sr.nblk;
-      mask_scores(s, nval, blk, (sr.blk0 + t) * kTileKeys);
+      mask_scores(s, khx, nval, blk, (sr.blk0 + t) * kTileKeys);
     }
     update_ref(s);
     float lsum = 0.0f;
@@ -606,6 +617,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) oacc[mb] = mfma32(vf[tt][mb], pb[tt], oacc[mb]);
+    }
   };
 
   // ---- pipeline: at the top of iteration t, tile t sits in LDS stage t & 1
@@ -637,7 +649,7 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   const float l_row = l_run + __shfl_xor(l_run, 32);
   float* xch = reinterpret_cast<float*>(smem);
   // every wave is past its last tile (the loop ends on a barrier): the ring is free
-  if (active) {
+  if (!WT && active) {
 #pragma unroll
     for (int j = 0; j < HMB; ++j)
 #pragma unroll
@@ -646,7 +658,23 @@ __global__ __launch_bounds__(kStreamThreads) void attn_stream_kernel(AttnArgs a,
   }
   __syncthreads();
   float m_out = kNegInf, l_out = 0.0f;
-  if (active) {
+  if (WT && active) {  // this wave saw every key of its rows: normalise and stage them
+    m_out = mref;
+    l_out = l_row;
+    const float inv = l_out > 0.0f ? 1.0f / l_out : 0.0f;
+    uint8_t* orow = smem + REGION0 + wrow * OPITCH;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        ushort4 o;
+        o.x = to_bf16_bits(oacc[mb][4 * q4 + 0] * inv);
+        o.y = to_bf16_bits(oacc[mb][4 * q4 + 1] * inv);
+        o.z = to_bf16_bits(oacc[mb][4 * q4 + 2] * inv);
+        o.w = to_bf16_bits(oacc[mb][4 * q4 + 3] * inv);
+        *reinterpret_cast<ushort4*>(orow + 2 * (32 * mb + 8 * q4 + 4 * half)) = o;
+      }
+  } else if (active) {
     const int pw = w ^ 1;
     const float2 po = xstat[pw][lane & 31];
     m_out = fmaxf(mref, po.x);
@@ -910,7 +938,8 @@ hipError_t launch_stream_any(const AttnArgs& a, const AttnPlan& p, int direct, h
   switch (p.qblocks) {
     case 1: return launch_stream<D, 1>(a, p, direct, stream);
     case 2: return launch_stream<D, 2>(a, p, direct, stream);
-    default: return launch_stream<D, 4>(a, p, direct, stream);
+    case 4: return launch_stream<D, 4>(a, p, direct, stream);
+    default: return launch_stream<D, 8>(a, p, direct, stream);
   }
 }
 

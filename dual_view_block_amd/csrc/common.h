@@ -24,7 +24,7 @@ constexpr int kRaggedMaxSeqs = 256;
 
 struct AttnPlan {
   int rows;          // R = G * K query rows per (sequence, KV head)
-  int qblocks;       // 32-row query blocks per work-group: 1, 2 or 4
+  int qblocks;       // 32-row query blocks per work-group: 1, 2, 4 or 8
   int rows_per_wg;   // 32 * qblocks
   int row_groups;    // ceil(R / rows_per_wg)
   int splits;        // most splits per (sequence, KV head, row group) the workspace holds

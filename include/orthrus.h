@@ -31,6 +31,11 @@
  *                          (it can only lower them); it must not change
  *                          between an orthrus_block_attn_partial call and the
  *                          orthrus_block_attn_merge of its partials.
+ *   ORTHRUS_ROWS128=1      caps a work-group at 128 query rows (more rows per
+ *                          KV head then take several row groups, each
+ *                          streaming the cache); it changes the workspace
+ *                          size, so it must be set alike for the size query
+ *                          and the calls.
  *   ORTHRUS_EVEN_SPLITS=1  gives batches of several sequences equal splits
  *                          per group instead of the balanced placement.
  *   ORTHRUS_DEBUG          prints each attention launch plan to stderr.

@@ -99,6 +99,32 @@ def test_large_blocks_32k(mode, K):
 
 
 @pytest.mark.parametrize("mode", ["diff", "verify"])
+def test_large_blocks_32k_rows128(mode, monkeypatch):
+    """K = 64 at L=32768 with work-groups capped at 128 rows (two row groups,
+    each streaming the cache): the tuning switch keeps that path exact too."""
+    monkeypatch.setenv("ORTHRUS_ROWS128", "1")
+    w = WORKLOADS["qwen3_8b_32k"].replace(block_k=64)
+    _check(_inputs(w), mode, "32k/K64/rows128")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
+@pytest.mark.parametrize("shape", [
+    # (B, Hq, Hkv, D, L, max_len, K): 256-row work-groups, partly live
+    (1, 32, 8, 128, 3000, 3008, 40),   # R = 160: five of eight query blocks live
+    (2, 16, 2, 64, 1500, 1600, 33),    # GQA 8, D = 64: R = 264 -> two row groups, the second 8 rows
+    (1, 32, 8, 128, 0, 64, 100),       # empty cache: two block tiles only
+    (3, 8, 2, 128, 257, 300, 128),     # R = 512, ragged lengths
+])
+def test_wide_row_groups(mode, shape):
+    B, Hq, Hkv, D, L, max_len, K = shape
+    w = Workload("wide", 1, B, Hq, Hkv, D, L, K, 10, 1.0, 123, max_len=max_len)
+    x = _inputs(w)
+    if B > 1 and L > 1:
+        x["cache_len"] = torch.tensor([L - 5 * b for b in range(B)], dtype=torch.int32, device=DEV)
+    _check(x, mode, f"wide{shape}")
+
+
+@pytest.mark.parametrize("mode", ["diff", "verify"])
 def test_ragged_batch_of_16(mode):
     """16 sequences, L_b ~ U{1024..16384}, capacity 16384, Qwen3-8B heads."""
     w = WORKLOADS["ragged_b16"]
