@@ -41,7 +41,7 @@ EXPORTS = (
     "orthrus_consensus_sample_dyn", "orthrus_cache_commit_dyn",
 )
 # bytes of the device scratch behind orthrus_block_attn_noalloc
-ORTHRUS_NOALLOC_SCRATCH_BYTES = 16 << 20
+ORTHRUS_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class AttnDesc(ctypes.Structure):

@@ -176,9 +176,10 @@ orthrus_status orthrus_block_attn_dyn(const orthrus_attn_desc* d, int32_t mode,
                                       const int32_t* blk_len, uint16_t* out, float* lse,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of the device scratch behind orthrus_block_attn_noalloc (16 MiB per
- * device, held from library load until the process ends). */
-#define ORTHRUS_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+/* Bytes of the device scratch behind orthrus_block_attn_noalloc (32 MiB per
+ * device, held from library load until the process ends): enough for one
+ * sequence of 8 KV heads at any block up to K = 128 (GQA 4). */
+#define ORTHRUS_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* orthrus_block_attn without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,

@@ -12,6 +12,9 @@ import pytest
 import dual_view_block_amd as dvb
 from dual_view_block_amd import _lib
 
+# calls that pass the host checks carry made-up device pointers: never where a GPU could run them
+pytestmark = pytest.mark.nogpu
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "orthrus.h")
 
@@ -236,7 +239,7 @@ def test_product_path_never_touches_the_oracle():
 
 def test_noalloc_entry_point_rejects_before_any_hip_call():
     """orthrus_block_attn_noalloc: a descriptor whose workspace exceeds the
-    16 MiB scratch is refused with ORTHRUS_ERR_UNSUPPORTED, and bad pointers,
+    32 MiB scratch is refused with ORTHRUS_ERR_UNSUPPORTED, and bad pointers,
     alignment and modes are refused as in orthrus_block_attn -- all on the host."""
     lib = _lib.load()
 

@@ -6,7 +6,11 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 from dual_view_block_amd import build as B
+
+pytestmark = pytest.mark.nogpu  # it runs tests/test_abi.py, whose calls carry made-up device pointers
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 

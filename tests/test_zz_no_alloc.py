@@ -46,6 +46,21 @@ def test_noalloc_matches_the_workspace_entry_point_twice():
         print(f"noalloc call {n} ({w.name}): bit-identical; max_abs={e[0]:.2e} rel_l2={e[1]:.2e}", flush=True)
 
 
+def test_noalloc_wide_row_groups():
+    """K = 64 at Qwen3-8B heads (256-row work-groups, 32 splits: 17.3 MB of
+    partials) fits the scratch and matches the workspace entry point bit for bit."""
+    w = WORKLOADS["qwen3_8b_8k"].replace(block_k=64)
+    x = attention_inputs(w, device=DEV)
+    assert dvb.orthrus_attn_workspace_size(dvb.attn_desc(x["q"], x["k_cache"])) > 16 << 20
+    ref_out, ref_lse, out, lse = _both(x, dvb.ORTHRUS_MASK_VERIFY_CAUSAL)
+    assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+    r, rl = oracle.block_attention(x["q"], x["k_blk"], x["v_blk"], x["k_cache"], x["v_cache"], x["cache_len"],
+                                   oracle.MASK_VERIFY_CAUSAL)
+    e = assert_attn_close(out, r, "noalloc K64")
+    assert_lse_close(lse, rl, "noalloc K64")
+    print(f"noalloc K64: bit-identical; max_abs={e[0]:.2e} rel_l2={e[1]:.2e}", flush=True)
+
+
 def test_noalloc_refuses_a_workspace_past_the_scratch():
     w = WORKLOADS["qwen3_8b_8k"].replace(batch=256, cache_len=64)
     x = attention_inputs(w, device=DEV)
